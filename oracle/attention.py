@@ -1,0 +1,165 @@
+"""Fused ring + current attention in fp64 (test infrastructure).
+
+Source: vLLM tpu-inference pull request "PCP: in-kernel ring cache phase,
+fused with the current phase".
+  * Summary: ring cache rounds and the causal current phase run in one launch
+    sharing one online softmax; no separate current launch, no LSE merge.
+  * Design: per query block the key walk first visits the ring region (cache
+    shards, no causal mask, bounded by each shard's valid length), then the
+    current-KV blocks with the causal mask; current KV is handed over in
+    token order.
+  * Testing: ring must agree with the gather-the-cache strategy.
+
+Agreement with the gather strategy means the fused launch computes exactly
+(up to rounding) plain softmax attention of chunk row ``i`` -- global
+position ``cache_len + i`` -- over the whole cache followed by current tokens
+``0..i``.  ``attention_rows`` is that definition.  ``ring_online`` takes the
+method's steps (ring rounds, then current blocks, one running (m, l, acc)).
+``two_pass_merge`` is the log-sum-exp merge of the removed two-launch variant
+(Summary section), kept only as an identity to check the others against.
+
+Conventions (readings where the pages are silent): GQA heads are contiguous
+groups, query head ``h`` uses KV head ``h // (NQ // NKV)``; ``lse`` is the
+natural-log log-sum-exp of the scaled scores, laid out ``[NQ, rows]``.
+"""
+import math
+import numpy as np
+
+
+def bf16_bits_to_f64(bits):
+    """bf16 bit patterns (uint16 / int16 array) -> exact float64 values."""
+    b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def _head_major(x):
+    """[T, NKV, HD] -> contiguous float64 [NKV, T, HD]."""
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64).transpose(1, 0, 2))
+
+
+def attention_rows(q, k_tok, v_tok, k_cur, v_cur, rows, scale,
+                   cache=True, current=True):
+    """Softmax attention of the chosen chunk rows, plain definition.
+
+    q      [C, NQ, HD]   chunk queries (any float dtype; bf16 values are exact)
+    k_tok  [L, NKV, HD]  cached keys in token order (L = cache_len)
+    v_tok  [L, NKV, HD]
+    k_cur  [C, NKV, HD]  current keys in token order, row j at position L + j
+    v_cur  [C, NKV, HD]
+    rows   iterable of chunk row indices to evaluate (real rows only)
+
+    Row ``i`` sees cache tokens ``0..L-1`` (if ``cache``) and current tokens
+    ``0..i`` (if ``current``).  Keys outside that set are excluded by slicing,
+    never multiplied by zero, so NaN or Inf stored there cannot reach the
+    result.  Returns ``out [len(rows), NQ, HD]`` and ``lse [NQ, len(rows)]``
+    in float64; a row with no visible key gets out = 0 and lse = -inf.
+    """
+    rows = list(rows)
+    C, NQ, HD = q.shape
+    L = k_tok.shape[0]
+    NKV = k_cur.shape[1]
+    G = NQ // NKV
+    K = _head_major(np.concatenate([np.asarray(k_tok, np.float64),
+                                    np.asarray(k_cur, np.float64)], axis=0))
+    V = _head_major(np.concatenate([np.asarray(v_tok, np.float64),
+                                    np.asarray(v_cur, np.float64)], axis=0))
+    out = np.zeros((len(rows), NQ, HD))
+    lse = np.full((NQ, len(rows)), -np.inf)
+    for r, i in enumerate(rows):
+        lo = 0 if cache else L
+        hi = L + i + 1 if current else L
+        if hi <= lo:
+            continue
+        qi = np.asarray(q[i], dtype=np.float64)            # [NQ, HD]
+        for g in range(NKV):
+            hs = slice(g * G, (g + 1) * G)
+            s = scale * (qi[hs] @ K[g, lo:hi].T)             # [G, n]
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            l = e.sum(axis=1, keepdims=True)
+            out[r, hs] = (e @ V[g, lo:hi]) / l
+            lse[hs, r] = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+def ring_attention(q, k_cache, v_cache, k_cur, v_cur, cache_len, P,
+                   interleave, rows, scale):
+    """The fused launch's result from a striped cache: de-stripe the shards
+    with the cache map, then ``attention_rows``."""
+    from .stripe import destripe
+    k_tok = destripe(np.asarray(k_cache), cache_len, P, interleave)
+    v_tok = destripe(np.asarray(v_cache), cache_len, P, interleave)
+    return attention_rows(q, k_tok, v_tok, k_cur, v_cur, rows, scale)
+
+
+def ring_online(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, interleave,
+                rows, scale, ring_start=0, block=64):
+    """The method's own walk, in fp64, one chunk row at a time.
+
+    Per row: running max ``m`` = -inf, normaliser ``l`` = 0, accumulator
+    ``acc`` = 0.  Ring region: for round k = 0..P-1 visit shard
+    ``(ring_start - k) mod P`` and its valid slots in blocks of ``block``
+    (no causal mask: every cached token precedes the chunk).  Current
+    region: current tokens in blocks of ``block``, keeping only tokens at or
+    before the row (causal).  Each block updates the shared state with
+    ``m' = max(m, max s)``, ``acc = e^(m-m') acc + sum e^(s-m') v``,
+    ``l = e^(m-m') l + sum e^(s-m')``.  Finally ``out = acc / l`` and
+    ``lse = m + ln l``.  Same return layout as ``attention_rows``.
+    """
+    from .stripe import shard_lengths
+    rows = list(rows)
+    C, NQ, HD = q.shape
+    NKV = k_cur.shape[1]
+    G = NQ // NKV
+    lens = shard_lengths(cache_len, P, interleave)
+    kc = np.asarray(k_cache, np.float64)
+    vc = np.asarray(v_cache, np.float64)
+    kcur = np.asarray(k_cur, np.float64)
+    vcur = np.asarray(v_cur, np.float64)
+    out = np.zeros((len(rows), NQ, HD))
+    lse = np.full((NQ, len(rows)), -np.inf)
+    for r, i in enumerate(rows):
+        qi = np.asarray(q[i], np.float64)
+        for g in range(NKV):
+            hs = slice(g * G, (g + 1) * G)
+            m = np.full(G, -np.inf)
+            l = np.zeros(G)
+            acc = np.zeros((G, HD))
+
+            def visit(kb, vb):
+                nonlocal m, l, acc
+                if kb.shape[0] == 0:
+                    return
+                s = scale * (qi[hs] @ kb.T)
+                m_new = np.maximum(m, s.max(axis=1))
+                alpha = np.exp(m - m_new)
+                p = np.exp(s - m_new[:, None])
+                l = alpha * l + p.sum(axis=1)
+                acc = alpha[:, None] * acc + p @ vb
+                m = m_new
+
+            for k in range(P):                      # ring rounds
+                s_id = (ring_start - k) % P
+                for b0 in range(0, lens[s_id], block):
+                    b1 = min(b0 + block, lens[s_id])
+                    visit(kc[s_id, b0:b1, g], vc[s_id, b0:b1, g])
+            for c0 in range(0, i + 1, block):        # current region, causal
+                c1 = min(c0 + block, i + 1)
+                visit(kcur[c0:c1, g], vcur[c0:c1, g])
+            out[r, hs] = acc / l[:, None]
+            lse[hs, r] = m + np.log(l)
+    return out, lse
+
+
+def two_pass_merge(o1, lse1, o2, lse2):
+    """Log-sum-exp merge of two partial attentions over disjoint key sets
+    (the step of the removed two-launch variant).  ``o*`` are
+    ``[rows, NQ, HD]``, ``lse*`` are ``[NQ, rows]``."""
+    lse = np.logaddexp(lse1, lse2)
+    w1 = np.where(np.isneginf(lse1), 0.0, np.exp(lse1 - lse)).T[:, :, None]
+    w2 = np.where(np.isneginf(lse2), 0.0, np.exp(lse2 - lse)).T[:, :, None]
+    return w1 * o1 + w2 * o2, lse
+
+
+def default_scale(head_dim):
+    return 1.0 / math.sqrt(head_dim)
