@@ -32,13 +32,8 @@ def bf16_bits_to_f64(bits):
     return b.view(np.float32).astype(np.float64)
 
 
-def _head_major(x):
-    """[T, NKV, HD] -> contiguous float64 [NKV, T, HD]."""
-    return np.ascontiguousarray(np.asarray(x, dtype=np.float64).transpose(1, 0, 2))
-
-
 def attention_rows(q, k_tok, v_tok, k_cur, v_cur, rows, scale,
-                   cache=True, current=True):
+                   cache=True, current=True, row_block=64):
     """Softmax attention of the chosen chunk rows, plain definition.
 
     q      [C, NQ, HD]   chunk queries (any float dtype; bf16 values are exact)
@@ -49,36 +44,53 @@ def attention_rows(q, k_tok, v_tok, k_cur, v_cur, rows, scale,
     rows   iterable of chunk row indices to evaluate (real rows only)
 
     Row ``i`` sees cache tokens ``0..L-1`` (if ``cache``) and current tokens
-    ``0..i`` (if ``current``).  Keys outside that set are excluded by slicing,
-    never multiplied by zero, so NaN or Inf stored there cannot reach the
-    result.  Returns ``out [len(rows), NQ, HD]`` and ``lse [NQ, len(rows)]``
-    in float64; a row with no visible key gets out = 0 and lse = -inf.
+    ``0..i`` (if ``current``); its scores are ``scale * q . k`` in fp64, and
+    ``out = sum_j e^(s_j - m) v_j / l``, ``l = sum_j e^(s_j - m)``,
+    ``lse = m + ln l`` with ``m`` the row's max score.  The sum over j is
+    taken in two parts: the cache part, identical for every row, as one
+    matrix product over a block of rows, and the current part row by row.
+    Current keys after row ``i`` are excluded by slicing, never multiplied
+    by zero, so NaN or Inf stored there cannot reach the result.  Returns
+    ``out [len(rows), NQ, HD]`` and ``lse [NQ, len(rows)]`` in float64; a
+    row with no visible key gets out = 0 and lse = -inf.
     """
     rows = list(rows)
     C, NQ, HD = q.shape
-    L = k_tok.shape[0]
+    L = k_tok.shape[0] if cache else 0
     NKV = k_cur.shape[1]
     G = NQ // NKV
-    K = _head_major(np.concatenate([np.asarray(k_tok, np.float64),
-                                    np.asarray(k_cur, np.float64)], axis=0))
-    V = _head_major(np.concatenate([np.asarray(v_tok, np.float64),
-                                    np.asarray(v_cur, np.float64)], axis=0))
     out = np.zeros((len(rows), NQ, HD))
     lse = np.full((NQ, len(rows)), -np.inf)
-    for r, i in enumerate(rows):
-        lo = 0 if cache else L
-        hi = L + i + 1 if current else L
-        if hi <= lo:
-            continue
-        qi = np.asarray(q[i], dtype=np.float64)            # [NQ, HD]
-        for g in range(NKV):
-            hs = slice(g * G, (g + 1) * G)
-            s = scale * (qi[hs] @ K[g, lo:hi].T)             # [G, n]
-            m = s.max(axis=1, keepdims=True)
-            e = np.exp(s - m)
-            l = e.sum(axis=1, keepdims=True)
-            out[r, hs] = (e @ V[g, lo:hi]) / l
-            lse[hs, r] = (m + np.log(l))[:, 0]
+    for g in range(NKV):
+        hs = slice(g * G, (g + 1) * G)
+        Kc = np.ascontiguousarray(np.asarray(k_tok[:L, g], np.float64))       # [L, HD]
+        Vc = np.ascontiguousarray(np.asarray(v_tok[:L, g], np.float64))
+        Kn = np.asarray(k_cur[:, g], np.float64)                               # [C, HD]
+        Vn = np.asarray(v_cur[:, g], np.float64)
+        for r0 in range(0, len(rows), row_block):
+            blk = rows[r0:r0 + row_block]
+            nb = len(blk)
+            Qb = np.stack([np.asarray(q[i, hs], np.float64) for i in blk])      # [nb, G, HD]
+            Sc = scale * (Qb.reshape(nb * G, HD) @ Kc.T).reshape(nb, G, L)     # cache scores
+            Sn = [scale * (Qb[b] @ Kn[:(i + 1 if current else 0)].T)          # current scores
+                  for b, i in enumerate(blk)]                                  # [G, i+1] each
+            # row max over both parts (-inf when a row sees nothing)
+            m = np.full((nb, G), -np.inf)
+            for b in range(nb):
+                if L > 0:
+                    m[b] = np.maximum(m[b], Sc[b].max(axis=1))
+                if Sn[b].shape[1] > 0:
+                    m[b] = np.maximum(m[b], Sn[b].max(axis=1))
+            m_safe = np.where(np.isneginf(m), 0.0, m)
+            Ec = np.exp(Sc - m_safe[:, :, None])                                # [nb, G, L]
+            Oc = (Ec.reshape(nb * G, L) @ Vc).reshape(nb, G, HD)
+            for b, i in enumerate(blk):
+                En = np.exp(Sn[b] - m_safe[b][:, None])                          # [G, i+1]
+                l = Ec[b].sum(axis=1) + En.sum(axis=1)
+                if not (l > 0).all():
+                    continue
+                out[r0 + b, hs] = (Oc[b] + En @ Vn[:En.shape[1]]) / l[:, None]
+                lse[hs, r0 + b] = m[b] + np.log(l)
     return out, lse
 
 

@@ -39,23 +39,20 @@ def shard_lengths(cache_len, P, interleave):
 
 def stripe(tokens, P, interleave, shard_cap, fill=np.nan):
     """Token-order ``[L, ...]`` -> striped ``[P, shard_cap, ...]``; slots that
-    hold no token are set to ``fill``."""
+    hold no token are set to ``fill``.  (``stripe_position`` is applied to
+    all positions at once as integer array arithmetic.)"""
     L = tokens.shape[0]
     out = np.full((P, shard_cap) + tokens.shape[1:], fill, dtype=tokens.dtype)
-    for p in range(L):
-        s, j = stripe_position(p, P, interleave)
-        out[s, j] = tokens[p]
+    s, j = stripe_position(np.arange(L, dtype=np.int64), P, interleave)
+    out[s, j] = tokens
     return out
 
 
 def destripe(cache, cache_len, P, interleave):
     """Striped ``[P, shard_cap, ...]`` -> token order ``[cache_len, ...]``.
     Only slots below each shard's length are read."""
-    out = np.empty((cache_len,) + cache.shape[2:], dtype=cache.dtype)
-    for p in range(cache_len):
-        s, j = stripe_position(p, P, interleave)
-        out[p] = cache[s, j]
-    return out
+    s, j = stripe_position(np.arange(cache_len, dtype=np.int64), P, interleave)
+    return cache[s, j]
 
 
 def kv_cache_write_ref(k_cache, v_cache, k_cur, v_cur, n_tokens, cache_len,

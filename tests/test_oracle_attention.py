@@ -232,11 +232,13 @@ def test_bf16_bits_decode():
 # --- mutation checks: a plausible mistake in the oracle must fail a pin ---
 
 MUTATIONS = [
-    ("hi = L + i + 1 if current else L", "hi = L + i + 2 if current else L"),   # causal off by one
+    ("Kn[:(i + 1 if current else 0)]", "Kn[:(i + 2 if current else 0)]"),        # causal off by one
     ("hs = slice(g * G, (g + 1) * G)", "hs = slice(g, NQ, NKV)"),               # interleaved GQA map
-    ("lo = 0 if cache else L", "lo = L if cache else L"),                       # cache dropped
-    ("s = scale * (qi[hs] @ K[g, lo:hi].T)", "s = -scale * (qi[hs] @ K[g, lo:hi].T)"),  # sign
-    ("lse[hs, r] = (m + np.log(l))[:, 0]", "lse[hs, r] = np.log(l)[:, 0]"),     # max dropped from lse
+    ("Oc = (Ec.reshape", "Oc = 0 * (Ec.reshape"),                               # cache values dropped
+    ("Sc = scale * (Qb", "Sc = -scale * (Qb"),                                  # sign of cache scores
+    ("lse[hs, r0 + b] = m[b] + np.log(l)", "lse[hs, r0 + b] = np.log(l)"),      # max dropped from lse
+    ("En @ Vn[:En.shape[1]]", "En @ Vn[1:En.shape[1] + 1]"),                    # value rows shifted
+    ("Kc = np.ascontiguousarray(np.asarray(k_tok[:L, g]", "Kc = np.ascontiguousarray(np.asarray(k_tok[:L, 0]"),  # kv head ignored
 ]
 
 
@@ -253,12 +255,16 @@ def _mutant(old, new):
 @pytest.mark.parametrize("old,new", MUTATIONS)
 def test_mutations_are_caught(old, new):
     mod = _mutant(old, new)
-    caught = not check_worked(mod)
-    case = rand_case(12, 5, 6, 4, 2, 3)
-    ref = brute_force(case["q"], case["k_tok"], case["v_tok"], case["k_cur"], case["v_cur"], 0.5)
-    out, lse = mod.attention_rows(case["q"], case["k_tok"], case["v_tok"], case["k_cur"],
-                                  case["v_cur"], range(5), 0.5)
-    for (i, h), (o, l) in ref.items():
-        if np.abs(out[i, h] - np.array(o)).max() > 1e-9 or abs(lse[h, i] - l) > 1e-9:
-            caught = True
+    try:  # a mutant that crashes is caught too
+        caught = not check_worked(mod)
+        case = rand_case(12, 5, 6, 4, 2, 3)
+        ref = brute_force(case["q"], case["k_tok"], case["v_tok"], case["k_cur"], case["v_cur"],
+                          0.5)
+        out, lse = mod.attention_rows(case["q"], case["k_tok"], case["v_tok"], case["k_cur"],
+                                      case["v_cur"], range(4), 0.5)
+        for (i, h), (o, l) in ref.items():
+            if i < 4 and (np.abs(out[i, h] - np.array(o)).max() > 1e-9 or abs(lse[h, i] - l) > 1e-9):
+                caught = True
+    except (ValueError, IndexError):
+        caught = True
     assert caught
