@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused ring + current attention step on one MI355X.
+
+A step is the whole hot path over one 4k-token chunk at 32k context:
+the strided KV-cache write of the chunk's 4096 current tokens into the P=8
+striped shards, then the single fused launch that visits the 28672 cached
+tokens (8 shard visits) and the causal current chunk (NQ=32, NKV=2, HD=256,
+bf16 in, fp32 accumulation, bf16 out + fp32 LSE).  Inputs are seeded N(0,1)
+bf16 draws (no dataset or trained weights are involved on this path) and are
+resident in HBM before timing; the cache is striped by the library's own
+strided write, as earlier chunks would have left it.
+
+Prints ONE JSON line.  ``value`` is TFLOP/s of algorithmic work
+4*HD*NQ*sum_rows(cache_len + i + 1) per step time; ``roofline`` relates the
+fused kernel's own duration (HIP events on its launch stream) to the bf16
+dense MFMA peak; ``cpu_baseline`` times the fp64 oracle on a bounded sample
+of rows of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "fused ring attention TFLOP/s + % bf16 MFMA peak; ms/chunk at 32k ctx"
+
+
+def alg_flops(w):
+    """QK^T + PV flops over visible (row, key) pairs of the real rows."""
+    rows = w.real_rows
+    pairs = rows * w.cache_len + rows * (rows + 1) // 2
+    return 4 * w.hd * w.nq * pairs
+
+
+def alg_bytes(w, with_write):
+    """Q + visible K/V once + out + LSE (+ the write's read and write)."""
+    row = w.nkv * w.hd * 2
+    b = w.real_rows * w.nq * w.hd * 2 * 2 + w.real_rows * w.nq * 4
+    b += 2 * (w.cache_len + w.real_rows) * row
+    if with_write:
+        b += 2 * 2 * w.real_rows * row
+    return b
+
+
+def setup(w, device):
+    import torch
+    import context_causal_attention_ring_amd as ra
+    import workloads
+    t = workloads.generate(w)
+    C = w.q_rows
+    d = dict(q=t["q"].to(device), k_cur=t["k_cur"].to(device), v_cur=t["v_cur"].to(device))
+    shape = (w.P, w.shard_cap, w.nkv, w.hd)
+    d["k_cache"] = torch.full(shape, float("nan"), device=device, dtype=torch.bfloat16)
+    d["v_cache"] = torch.full(shape, float("nan"), device=device, dtype=torch.bfloat16)
+    layout = ra.StripeLayout(w.interleave, 0)
+    dims = ra.make_dims(d["q"], d["k_cur"], w.shard_cap, real_rows=w.real_rows,
+                        head_rows=w.head_rows, scale=w.scale)
+    if w.cache_len:
+        k_tok = t["k_cache_tok"].to(device)
+        v_tok = t["v_cache_tok"].to(device)
+        ra.kv_cache_write(k_tok, v_tok, w.cache_len, d["k_cache"], d["v_cache"], 0, w.P, layout,
+                          dims)
+        torch.cuda.synchronize()
+        del k_tok, v_tok
+    d["out"] = torch.empty(C, w.nq, w.hd, device=device, dtype=torch.bfloat16)
+    d["lse"] = torch.empty(w.nq, C, device=device, dtype=torch.float32)
+    return t, d, layout, dims
+
+
+def cpu_baseline(w, t, budget_s=12.0):
+    """Time the fp64 oracle (as it stands) on a bounded sample of rows."""
+    import numpy as np
+    import oracle
+    try:
+        import threadpoolctl
+        threads = max(i["num_threads"] for i in threadpoolctl.threadpool_info()
+                      if i.get("user_api") == "blas")
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    args = [t[k].float().numpy() for k in ("q", "k_cache_tok", "v_cache_tok", "k_cur", "v_cur")]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(w.real_rows).tolist()
+    done, flops, elapsed, blk = 0, 0, 0.0, 8
+    while done < len(order) and elapsed < budget_s:
+        rows = order[done:done + blk]
+        t0 = time.perf_counter()
+        oracle.attention_rows(*args, rows, w.scale)
+        elapsed += time.perf_counter() - t0
+        flops += sum(4 * w.hd * w.nq * (w.cache_len + i + 1) for i in rows)
+        done += len(rows)
+        blk = min(64, blk * 2)
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 oracle on {done} random real rows of the {w.name} chunk "
+                      f"(all {w.nq} heads, {w.cache_len} cached + causal keys), "
+                      f"{elapsed:.1f} s; TFLOP/s of the same algorithmic count"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="32k", help="workload name (default: 32k)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per fused launch")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build computes one rank's share of the ring "
+              f"on a single MI355X; --gpus {args.gpus} is not supported.", file=sys.stderr)
+        return 2
+
+    import torch
+    import context_causal_attention_ring_amd as ra
+    import workloads
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+        return 0
+
+    w = workloads.CONFIGS[args.config]
+    with_write = True
+    t, d, layout, dims = setup(w, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        ra.kv_cache_write(d["k_cur"], d["v_cur"], w.real_rows, d["k_cache"], d["v_cache"],
+                          w.cache_len, w.P, layout, dims)
+        if ev is not None:
+            ev[0].record(stream)
+        ra.ring_attn_prefill(d["q"], d["k_cache"], d["v_cache"], d["k_cur"], d["v_cur"],
+                             w.cache_len, w.P, layout, d["out"], d["lse"], dims)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    total_s = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_ms_avg = sum(kern_ms) / len(kern_ms)
+    ms_per_step = total_s * 1e3 / args.steps
+
+    # Cold-cache view: evict the Infinity Cache with a 512 MiB write before each step.
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(min(args.steps, 10)):
+        scratch.fill_(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        b.synchronize()
+        cold.append(a.elapsed_time(b))
+    del scratch
+
+    F = alg_flops(w)
+    value = F / (ms_per_step * 1e-3) / 1e12
+    achieved = F / (kern_ms_avg * 1e-3) / 1e12
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+    props = torch.cuda.get_device_properties(dev)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: fused ring+current prefill of one {w.q_rows}-row "
+                               f"chunk (head {w.head_rows} + tail {w.tail_rows}) over "
+                               f"{w.cache_len} cached tokens in P={w.P} striped shards, "
+                               f"NQ={w.nq} NKV={w.nkv} HD={w.hd}, plus the strided "
+                               f"kv_cache_write of the chunk",
+                   "cache_len": w.cache_len, "P": w.P, "q_rows": w.q_rows,
+                   "real_rows": w.real_rows, "nq": w.nq, "nkv": w.nkv, "hd": w.hd,
+                   "flop_per_step": F},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "ms_per_chunk": round(ms_per_step, 4),
+        "ms_per_step_cold_median": round(sorted(cold)[len(cold) // 2], 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "ring_attn_fused_kernel<256>",
+                     "kernel_ms_avg": round(kern_ms_avg, 4)},
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, t)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

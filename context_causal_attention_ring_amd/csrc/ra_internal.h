@@ -1,0 +1,51 @@
+// Internal declarations shared by the host entry points and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+// Arguments of the fused ring + current attention kernel.  All sizes are
+// validated by the host before launch; 32-bit byte offsets are proven to fit.
+struct FusedParams {
+  const uint16_t* q;        // bf16 [C, NQ, HD]
+  const uint16_t* k_cache;  // bf16 [P, shard_cap, NKV, HD]
+  const uint16_t* v_cache;
+  const uint16_t* k_cur;    // bf16 [C, NKV, HD], token order
+  const uint16_t* v_cur;
+  void* out;                // [C, NQ, HD] bf16 | fp32
+  float* lse;               // [NQ, C] or nullptr
+  int64_t shard_cap;        // slots per shard
+  int64_t full;             // cache_len / (P * I)
+  int64_t rem;              // cache_len % (P * I)
+  int32_t P, interleave, ring_start;
+  int32_t nb;               // ring tiles per shard visit (max shard length / BKV, rounded up)
+  int32_t nq, nkv, group;   // group = NQ / NKV
+  int32_t q_rows, real_rows;
+  int32_t row_tiles;        // workgroups per KV head
+  int32_t grid_real;        // row_tiles * NKV
+  int32_t out_f32;
+  float scale_log2e;        // softmax scale * log2(e)
+};
+
+struct WriteParams {
+  const uint16_t* k_cur;
+  const uint16_t* v_cur;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int64_t cache_len;
+  int64_t shard_cap;
+  int32_t n_tokens, P, interleave;
+  int32_t row_chunks;       // 16-byte chunks per token row (NKV * HD / 8)
+};
+
+// Tile geometry of the fused kernel for a head dimension.
+constexpr int kWaves = 4;           // waves per workgroup
+constexpr int kRowsPerWave = 32;    // (token, head) rows per wave
+constexpr int kRowsPerWG = kWaves * kRowsPerWave;
+constexpr int kBKV = 64;            // keys per KV tile
+
+hipError_t launch_fused(const FusedParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_kv_cache_write(const WriteParams& p, hipStream_t stream);
+
+}  // namespace ra

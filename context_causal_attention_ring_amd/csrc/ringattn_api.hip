@@ -1,0 +1,250 @@
+// C entry points of libringattn: argument validation, stripe geometry and
+// kernel dispatch.  Everything here runs on the host; the only HIP calls
+// are the asynchronous launches, made after every check has passed.
+//
+// Stripe geometry follows the vLLM tpu-inference pull request "PCP: in-kernel
+// ring cache phase, fused with the current phase", Design section (striped
+// cache shards visited as ring rounds, the cache bound of a partial last
+// block applied at run time).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/ringattn.h"
+#include "ra_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a + na) and [b, b + nb) overlap (byte ranges; empty ranges never do).
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (!a || !b || na <= 0 || nb <= 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+// Length of shard s when positions [0, cache_len) are cached (closed form of
+// the round-robin deal in units of `interleave` tokens).
+int64_t shard_len(int64_t cache_len, int32_t P, int32_t interleave, int32_t s) {
+  const int64_t round = (int64_t)P * interleave;
+  const int64_t full = cache_len / round, rem = cache_len % round;
+  int64_t extra = rem - (int64_t)s * interleave;
+  extra = extra < 0 ? 0 : (extra > interleave ? interleave : extra);
+  return full * interleave + extra;
+}
+
+int check_layout(int32_t P, ra_stripe_layout_t s, int64_t cache_len) {
+  if (P < 1) return fail(RA_ERR_INVALID_ARG, "P must be >= 1; got %d", P);
+  if (s.interleave < 1)
+    return fail(RA_ERR_INVALID_ARG, "stripe_layout.interleave must be >= 1; got %d", s.interleave);
+  if (s.ring_start < 0 || s.ring_start >= P)
+    return fail(RA_ERR_INVALID_ARG, "stripe_layout.ring_start must be in [0, P=%d); got %d", P,
+                s.ring_start);
+  if (cache_len < 0) return fail(RA_ERR_INVALID_ARG, "cache_len must be >= 0; got %lld",
+                                 (long long)cache_len);
+  return RA_OK;
+}
+
+int check_heads(const ra_dims_t* d) {
+  if (!d) return fail(RA_ERR_INVALID_ARG, "dims must not be NULL");
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1)
+    return fail(RA_ERR_INVALID_ARG, "num_q_heads (%d) and num_kv_heads (%d) must be >= 1",
+                d->num_q_heads, d->num_kv_heads);
+  if (d->num_q_heads % d->num_kv_heads != 0)
+    return fail(RA_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                d->num_q_heads, d->num_kv_heads);
+  if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256)
+    return fail(RA_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256; got %d", d->head_dim);
+  if (d->shard_cap < 1)
+    return fail(RA_ERR_INVALID_ARG, "shard_cap must be >= 1; got %lld", (long long)d->shard_cap);
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ra_last_error(void) { return g_last_error.c_str(); }
+
+const char* ra_version(void) { return "libringattn 0.1 (gfx950)"; }
+
+int ra_shard_len(int64_t cache_len, int32_t P, ra_stripe_layout_t stripe_layout, int32_t shard,
+                 int64_t* len) {
+  if (int rc = check_layout(P, stripe_layout, cache_len)) return rc;
+  if (shard < 0 || shard >= P)
+    return fail(RA_ERR_INVALID_ARG, "shard must be in [0, P=%d); got %d", P, shard);
+  if (!len) return fail(RA_ERR_INVALID_ARG, "len must not be NULL");
+  *len = shard_len(cache_len, P, stripe_layout.interleave, shard);
+  return RA_OK;
+}
+
+int ring_attn_prefill(const void* q, const void* k_cache, const void* v_cache, const void* k_cur,
+                      const void* v_cur, int64_t cache_len, int32_t P,
+                      ra_stripe_layout_t stripe_layout, void* out, float* lse,
+                      const ra_dims_t* dims, void* stream) {
+  if (int rc = check_heads(dims)) return rc;
+  if (int rc = check_layout(P, stripe_layout, cache_len)) return rc;
+  const ra_dims_t& d = *dims;
+  const int32_t C = d.q_rows;
+  if (C < 0) return fail(RA_ERR_INVALID_ARG, "q_rows must be >= 0; got %d", C);
+  if (d.head_rows < 0 || d.head_rows > C)
+    return fail(RA_ERR_INVALID_ARG, "head_rows must be in [0, q_rows=%d]; got %d", C, d.head_rows);
+  if (d.real_rows < 0 || d.real_rows > C)
+    return fail(RA_ERR_INVALID_ARG, "real_rows must be in [0, q_rows=%d]; got %d", C, d.real_rows);
+  if (d.out_dtype != RA_DTYPE_BF16 && d.out_dtype != RA_DTYPE_FP32)
+    return fail(RA_ERR_INVALID_ARG, "out_dtype must be RA_DTYPE_BF16 or RA_DTYPE_FP32; got %d",
+                d.out_dtype);
+  if (!std::isfinite(d.scale))
+    return fail(RA_ERR_INVALID_ARG, "scale must be finite (0 selects 1/sqrt(head_dim))");
+  const int32_t NQ = d.num_q_heads, NKV = d.num_kv_heads, HD = d.head_dim;
+  const int32_t group = NQ / NKV;
+
+  // Shards: the first shard is the longest.
+  const int64_t max_len = shard_len(cache_len, P, stripe_layout.interleave, 0);
+  if (max_len > d.shard_cap)
+    return fail(RA_ERR_INVALID_ARG,
+                "cache_len %lld needs %lld slots in shard 0 but shard_cap is %lld",
+                (long long)cache_len, (long long)max_len, (long long)d.shard_cap);
+
+  if (d.real_rows == 0) return RA_OK;  // nothing real to compute
+
+  if (!q || !k_cur || !v_cur || !out)
+    return fail(RA_ERR_INVALID_ARG, "q, k_cur, v_cur and out must not be NULL");
+  if (cache_len > 0 && (!k_cache || !v_cache))
+    return fail(RA_ERR_INVALID_ARG, "k_cache and v_cache must not be NULL when cache_len > 0");
+  const void* ptrs[] = {q, k_cache, v_cache, k_cur, v_cur, out, lse};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr))
+      return fail(RA_ERR_INVALID_ARG, "every tensor pointer must be 16-byte aligned");
+
+  // 32-bit buffer offsets: a shard visit reads at most max_len + BKV rows,
+  // the current region at most q_rows + BKV rows.
+  const int64_t rowstride = (int64_t)NKV * HD * 2;
+  const int64_t lim31 = (int64_t)1 << 31;
+  if ((max_len + ra::kBKV) * rowstride >= lim31)
+    return fail(RA_ERR_UNSUPPORTED, "a shard of %lld tokens x %lld bytes exceeds 2 GiB",
+                (long long)max_len, (long long)rowstride);
+  if (((int64_t)C + ra::kBKV) * rowstride >= lim31)
+    return fail(RA_ERR_UNSUPPORTED, "the current chunk (%d tokens x %lld bytes) exceeds 2 GiB", C,
+                (long long)rowstride);
+  const int64_t rows_total = (int64_t)d.real_rows * group;
+  if (rows_total + ra::kRowsPerWG >= lim31 / 2)
+    return fail(RA_ERR_UNSUPPORTED, "real_rows * (NQ/NKV) = %lld is too large",
+                (long long)rows_total);
+
+  // Outputs must not alias inputs.
+  const int64_t q_bytes = (int64_t)C * NQ * HD * 2;
+  const int64_t cur_bytes = (int64_t)C * NKV * HD * 2;
+  const int64_t cache_bytes = (int64_t)P * d.shard_cap * NKV * HD * 2;
+  const int64_t out_bytes = (int64_t)C * NQ * HD * (d.out_dtype == RA_DTYPE_FP32 ? 4 : 2);
+  const int64_t lse_bytes = (int64_t)NQ * C * 4;
+  struct R { const void* p; int64_t n; };
+  const R ins[] = {{q, q_bytes}, {k_cache, cache_len > 0 ? cache_bytes : 0},
+                   {v_cache, cache_len > 0 ? cache_bytes : 0}, {k_cur, cur_bytes},
+                   {v_cur, cur_bytes}};
+  for (const R& r : ins) {
+    if (overlaps(out, out_bytes, r.p, r.n))
+      return fail(RA_ERR_INVALID_ARG, "out overlaps an input tensor");
+    if (overlaps(lse, lse_bytes, r.p, r.n))
+      return fail(RA_ERR_INVALID_ARG, "lse overlaps an input tensor");
+  }
+  if (overlaps(out, out_bytes, lse, lse_bytes))
+    return fail(RA_ERR_INVALID_ARG, "out and lse overlap");
+
+  ra::FusedParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_cache = static_cast<const uint16_t*>(k_cache);
+  p.v_cache = static_cast<const uint16_t*>(v_cache);
+  p.k_cur = static_cast<const uint16_t*>(k_cur);
+  p.v_cur = static_cast<const uint16_t*>(v_cur);
+  p.out = out;
+  p.lse = lse;
+  p.shard_cap = d.shard_cap;
+  const int64_t round = (int64_t)P * stripe_layout.interleave;
+  p.full = cache_len / round;
+  p.rem = cache_len % round;
+  p.P = P;
+  p.interleave = stripe_layout.interleave;
+  p.ring_start = stripe_layout.ring_start;
+  p.nb = (int32_t)((max_len + ra::kBKV - 1) / ra::kBKV);
+  p.nq = NQ;
+  p.nkv = NKV;
+  p.group = group;
+  p.q_rows = C;
+  p.real_rows = d.real_rows;
+  p.row_tiles = (int32_t)((rows_total + ra::kRowsPerWG - 1) / ra::kRowsPerWG);
+  p.grid_real = p.row_tiles * NKV;
+  p.out_f32 = d.out_dtype == RA_DTYPE_FP32;
+  const float scale = d.scale == 0.f ? 1.f / std::sqrt((float)HD) : d.scale;
+  p.scale_log2e = scale * 1.4426950408889634f;
+  if ((int64_t)p.nb * P >= lim31)
+    return fail(RA_ERR_UNSUPPORTED, "too many ring tiles");
+
+  hipError_t e = ra::launch_fused(p, HD, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(RA_ERR_HIP, "fused attention launch failed: %s", hipGetErrorString(e));
+  return RA_OK;
+}
+
+int kv_cache_write(const void* k_cur, const void* v_cur, int32_t n_tokens, void* k_cache,
+                   void* v_cache, int64_t cache_len, int32_t P, ra_stripe_layout_t stripe_layout,
+                   const ra_dims_t* dims, void* stream) {
+  if (int rc = check_heads(dims)) return rc;
+  if (int rc = check_layout(P, stripe_layout, cache_len)) return rc;
+  if (n_tokens < 0) return fail(RA_ERR_INVALID_ARG, "n_tokens must be >= 0; got %d", n_tokens);
+  const ra_dims_t& d = *dims;
+  const int64_t end = cache_len + n_tokens;
+  const int64_t need = shard_len(end, P, stripe_layout.interleave, 0);
+  if (need > d.shard_cap)
+    return fail(RA_ERR_INVALID_ARG,
+                "writing positions [%lld, %lld) needs %lld slots in shard 0 but shard_cap is %lld",
+                (long long)cache_len, (long long)end, (long long)need, (long long)d.shard_cap);
+  if (n_tokens == 0) return RA_OK;
+  if (!k_cur || !v_cur || !k_cache || !v_cache)
+    return fail(RA_ERR_INVALID_ARG, "k_cur, v_cur, k_cache and v_cache must not be NULL");
+  const void* ptrs[] = {k_cur, v_cur, k_cache, v_cache};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr))
+      return fail(RA_ERR_INVALID_ARG, "every tensor pointer must be 16-byte aligned");
+  const int64_t row_bytes = (int64_t)d.num_kv_heads * d.head_dim * 2;
+  const int64_t cur_bytes = row_bytes * n_tokens;
+  const int64_t cache_bytes = row_bytes * P * d.shard_cap;
+  if (overlaps(k_cache, cache_bytes, v_cache, cache_bytes))
+    return fail(RA_ERR_INVALID_ARG, "k_cache and v_cache overlap");
+  const void* curs[] = {k_cur, v_cur};
+  for (const void* c : curs)
+    if (overlaps(k_cache, cache_bytes, c, cur_bytes) || overlaps(v_cache, cache_bytes, c, cur_bytes))
+      return fail(RA_ERR_INVALID_ARG, "a cache tensor overlaps k_cur or v_cur");
+
+  ra::WriteParams p{};
+  p.k_cur = static_cast<const uint16_t*>(k_cur);
+  p.v_cur = static_cast<const uint16_t*>(v_cur);
+  p.k_cache = static_cast<uint16_t*>(k_cache);
+  p.v_cache = static_cast<uint16_t*>(v_cache);
+  p.cache_len = cache_len;
+  p.shard_cap = d.shard_cap;
+  p.n_tokens = n_tokens;
+  p.P = P;
+  p.interleave = stripe_layout.interleave;
+  p.row_chunks = (int32_t)(row_bytes / 16);
+  hipError_t e = ra::launch_kv_cache_write(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(RA_ERR_HIP, "kv_cache_write launch failed: %s", hipGetErrorString(e));
+  return RA_OK;
+}
+
+}  // extern "C"

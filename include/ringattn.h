@@ -1,0 +1,147 @@
+/*
+ * libringattn -- fused ring + current causal attention for chunked prefill,
+ * and the strided KV-cache write that fills its striped cache (MI355X, gfx950).
+ *
+ * Source of the method: vLLM tpu-inference pull request "PCP: in-kernel ring
+ * cache phase, fused with the current phase".
+ *   - Summary: the ring cache rounds and the causal current phase run in ONE
+ *     launch sharing one online softmax; no second launch, no LSE merge.
+ *   - Design: per query block the key walk visits the ring region (the P
+ *     striped cache shards) and then the current-KV blocks (causal); region
+ *     behaviour is selected by value; current KV is passed in token order.
+ *   - Testing: ring agrees with attention over the gathered cache; the
+ *     strided KV-cache write is bit-exact.
+ * On one GPU the ring hops between ranks become sequential shard visits
+ * inside the kernel; a call computes one rank's share at its real shape.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor arguments are DEVICE pointers owned by the caller, dense
+ *     row-major, 16-byte aligned.  bf16 is IEEE bfloat16 (1-8-7).
+ *   - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is
+ *     the default stream).  They do not synchronise the host, allocate, or
+ *     copy host to device, and keep no pointer after returning; buffers must
+ *     stay alive until the stream has run the work.
+ *   - Every argument is validated on the host before any HIP call.  On error
+ *     nothing is launched, a non-zero ra_status_t is returned and
+ *     ra_last_error() describes it.  Launch failures return RA_ERR_HIP.
+ *
+ * Striped cache ("striped shard", Design section).  Cached token positions
+ * are dealt to shards 0..P-1 in turn, in units of `interleave` consecutive
+ * tokens (interleave = 1: token round-robin).  Position p lives in
+ *     shard = (p / I) mod P,   slot = ((p / I) / P) * I + p mod I.
+ * A cache holding positions [0, cache_len) gives shard s the length
+ *     full*I + clamp(rem - s*I, 0, I),  full = cache_len / (P*I),
+ *                                        rem  = cache_len mod (P*I).
+ * Cache tensors are laid out [P, shard_cap, NKV, HD]; slots at or beyond a
+ * shard's length are never read (they may hold anything, NaN included).
+ */
+#ifndef RINGATTN_H
+#define RINGATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RA_OK = 0,
+  RA_ERR_INVALID_ARG = 1, /* argument out of its documented domain */
+  RA_ERR_UNSUPPORTED = 2, /* valid, but outside what this build implements */
+  RA_ERR_HIP = 3          /* the HIP runtime refused the launch */
+} ra_status_t;
+
+typedef enum { RA_DTYPE_BF16 = 0, RA_DTYPE_FP32 = 1 } ra_dtype_t;
+
+/* Stripe layout of the cache.  ring_start is the first shard visited; the
+ * visit order is ring_start, ring_start-1, ... (mod P), the order in which a
+ * rank sees its neighbours' shards arrive.  The result does not depend on it
+ * beyond floating-point rounding order. */
+typedef struct {
+  int32_t interleave; /* tokens per stripe unit, >= 1 */
+  int32_t ring_start; /* in [0, P) */
+} ra_stripe_layout_t;
+
+/* Shapes.  The chunk has q_rows = C rows: a head sequence of head_rows rows
+ * followed by a tail sequence (Design section: the launch keeps the two
+ * sequences, both padded to full length, and the caller discards pad rows).
+ * Chunk row i is the token at global position cache_len + i.  Rows
+ * [0, real_rows) are real; rows [real_rows, q_rows) are pads: their current
+ * K/V are never read as keys and their out/lse entries are not written. */
+typedef struct {
+  int32_t num_q_heads;  /* NQ >= 1 */
+  int32_t num_kv_heads; /* NKV >= 1, NQ % NKV == 0; query head h reads KV
+                           head h / (NQ / NKV) */
+  int32_t head_dim;     /* HD in {64, 128, 256} */
+  int32_t q_rows;       /* C >= 0 */
+  int32_t head_rows;    /* 0 <= head_rows <= q_rows (scheduling metadata) */
+  int32_t real_rows;    /* 0 <= real_rows <= q_rows */
+  int64_t shard_cap;    /* slots allocated per shard, >= 1 */
+  float scale;          /* softmax scale; 0 selects 1/sqrt(HD) */
+  int32_t out_dtype;    /* ra_dtype_t of `out` */
+} ra_dims_t;
+
+/*
+ * ring_attn_prefill -- one launch: all P shard visits, then the causal
+ * current chunk, through one online softmax (Summary and Design sections).
+ *
+ *   q        bf16 [C, NQ, HD]             chunk queries
+ *   k_cache  bf16 [P, shard_cap, NKV, HD] striped cache keys (read only)
+ *   v_cache  bf16 [P, shard_cap, NKV, HD] striped cache values (read only)
+ *   k_cur    bf16 [C, NKV, HD]  current keys, TOKEN order: row i is
+ *                               position cache_len + i
+ *   v_cur    bf16 [C, NKV, HD]  current values, token order
+ *   cache_len  number of cached positions, >= 0 (0: no ring region)
+ *   P          number of shards, >= 1
+ *   out      [C, NQ, HD] bf16 or fp32 (dims->out_dtype); real rows get
+ *            softmax(scale * q k^T) v over cache positions [0, cache_len)
+ *            and current rows 0..i
+ *   lse      fp32 [NQ, C] natural-log log-sum-exp of the scaled scores of
+ *            each real row, or NULL to skip
+ *
+ * k_cache/v_cache may be NULL only when cache_len == 0.  out and lse must
+ * not overlap any input.  Each shard's valid bytes must stay below 2^31.
+ * Returns RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED or RA_ERR_HIP.
+ */
+int ring_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
+                      const void* k_cur, const void* v_cur, int64_t cache_len,
+                      int32_t P, ra_stripe_layout_t stripe_layout, void* out,
+                      float* lse, const ra_dims_t* dims, void* stream);
+
+/*
+ * kv_cache_write -- strided write of the chunk's current K/V into the
+ * striped cache (Design section: striped shards; Testing section: the write
+ * is bit-exact).  Current token t < n_tokens (global position
+ * cache_len + t) is copied bit for bit to its (shard, slot) in k_cache and
+ * v_cache.  No other slot is touched.  It only writes slots that
+ * ring_attn_prefill with the same cache_len never reads, so the two calls
+ * commute.
+ *
+ *   k_cur, v_cur      bf16 [>= n_tokens, NKV, HD], token order
+ *   n_tokens          real tokens to write, >= 0 (pads are not written)
+ *   k_cache, v_cache  bf16 [P, shard_cap, NKV, HD]
+ *   dims              uses num_kv_heads, head_dim, shard_cap only
+ *
+ * Every written slot must be < shard_cap (else RA_ERR_INVALID_ARG).
+ */
+int kv_cache_write(const void* k_cur, const void* v_cur, int32_t n_tokens,
+                   void* k_cache, void* v_cache, int64_t cache_len, int32_t P,
+                   ra_stripe_layout_t stripe_layout, const ra_dims_t* dims,
+                   void* stream);
+
+/* Host-only: length of shard `shard` when positions [0, cache_len) are
+ * cached, by the closed form above.  Writes *len; no GPU involved. */
+int ra_shard_len(int64_t cache_len, int32_t P, ra_stripe_layout_t stripe_layout,
+                 int32_t shard, int64_t* len);
+
+/* Thread-local text for the last non-OK status returned on this thread. */
+const char* ra_last_error(void);
+
+/* Library version string. */
+const char* ra_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RINGATTN_H */

@@ -1,0 +1,127 @@
+"""The C ABI library loads, exports every entry point its header declares,
+and rejects bad arguments on the host before any HIP call.
+
+Every validation case below is invalid in at least one argument, so nothing
+is ever launched and the fake device addresses are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import context_causal_attention_ring_amd as ra
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000000  # aligned fake device address; never dereferenced
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "ringattn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M))
+
+
+def test_header_declares_the_binding_names():
+    assert header_functions() == set(ra.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ra.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert ra.ra_version().startswith("libringattn")
+
+
+@pytest.mark.parametrize("P,I", [(1, 1), (2, 1), (3, 2), (8, 1), (8, 16), (5, 3)])
+def test_shard_len_matches_oracle(P, I):
+    for L in (0, 1, 2, 7, 511, 512, 126973, 1044480):
+        exp = oracle.shard_lengths(L, P, I)
+        got = [ra.ra_shard_len(L, P, ra.StripeLayout(I, 0), s) for s in range(P)]
+        assert got == exp
+
+
+def dims(**kw):
+    base = dict(num_q_heads=4, num_kv_heads=1, head_dim=64, q_rows=128, head_rows=64,
+                real_rows=128, shard_cap=320, scale=0.0, out_dtype=0)
+    base.update(kw)
+    return ra.Dims(**base)
+
+
+def call_prefill(d, cache_len=512, P=2, layout=(1, 0), ptrs=None, out=FAKE + 0x8000000,
+                 lse=None):
+    q, kc, vc, kcur, vcur = ptrs or (FAKE, FAKE + 0x1000000, FAKE + 0x2000000,
+                                     FAKE + 0x3000000, FAKE + 0x4000000)
+    return ra.lib().ring_attn_prefill(q, kc, vc, kcur, vcur, cache_len, P,
+                                      ra.StripeLayout(*layout), out, lse, ctypes.byref(d), None)
+
+
+BAD_PREFILL = [
+    (dict(d=dims(num_q_heads=6, num_kv_heads=4)), 1, "multiple"),
+    (dict(d=dims(head_dim=96)), 2, "head_dim"),
+    (dict(d=dims(num_kv_heads=0)), 1, ">= 1"),
+    (dict(d=dims(), P=0), 1, "P must"),
+    (dict(d=dims(), layout=(0, 0)), 1, "interleave"),
+    (dict(d=dims(), layout=(1, 2)), 1, "ring_start"),
+    (dict(d=dims(), cache_len=-1), 1, "cache_len"),
+    (dict(d=dims(shard_cap=255)), 1, "shard_cap"),
+    (dict(d=dims(real_rows=129)), 1, "real_rows"),
+    (dict(d=dims(head_rows=-1)), 1, "head_rows"),
+    (dict(d=dims(q_rows=-5, real_rows=0, head_rows=0)), 1, "q_rows"),
+    (dict(d=dims(out_dtype=7)), 1, "out_dtype"),
+    (dict(d=dims(scale=float("inf"))), 1, "scale"),
+    (dict(d=dims(), out=None), 1, "NULL"),
+    (dict(d=dims(), ptrs=(FAKE + 8, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000,
+                          FAKE + 0x4000000)), 1, "aligned"),
+    (dict(d=dims(), ptrs=(FAKE, 0, 0, FAKE + 0x3000000, FAKE + 0x4000000)), 1, "k_cache"),
+    (dict(d=dims(), out=FAKE + 0x10), 1, "overlaps"),
+    (dict(d=dims(), lse=FAKE + 0x3000000), 1, "overlaps"),
+    (dict(d=dims(num_kv_heads=1, head_dim=256, shard_cap=1 << 23), cache_len=1 << 24), 2, "2 GiB"),
+]
+
+
+@pytest.mark.parametrize("kw,code,msg", BAD_PREFILL)
+def test_prefill_rejects_bad_arguments(kw, code, msg):
+    rc = call_prefill(**kw)
+    assert rc == code
+    assert msg in ra.lib().ra_last_error().decode()
+
+
+def test_prefill_no_real_rows_is_a_no_op():
+    # nothing real to compute: returns OK without touching the (fake) buffers
+    assert call_prefill(dims(real_rows=0)) == 0
+
+
+def call_write(d, n=128, cache_len=512, P=2, layout=(1, 0), ptrs=None):
+    kcur, vcur, kc, vc = ptrs or (FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000)
+    return ra.lib().kv_cache_write(kcur, vcur, n, kc, vc, cache_len, P, ra.StripeLayout(*layout),
+                                   ctypes.byref(d), None)
+
+
+BAD_WRITE = [
+    (dict(d=dims(shard_cap=319)), 1, "shard_cap"),
+    (dict(d=dims(), n=-1), 1, "n_tokens"),
+    (dict(d=dims(), P=0), 1, "P must"),
+    (dict(d=dims(head_dim=48)), 2, "head_dim"),
+    (dict(d=dims(), ptrs=(FAKE, FAKE + 0x1000000, FAKE + 0x2000008, FAKE + 0x3000000)), 1, "aligned"),
+    (dict(d=dims(), ptrs=(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x2000000)), 1, "overlap"),
+    (dict(d=dims(), ptrs=(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, 0)), 1, "NULL"),
+]
+
+
+@pytest.mark.parametrize("kw,code,msg", BAD_WRITE)
+def test_write_rejects_bad_arguments(kw, code, msg):
+    assert call_write(**kw) == code
+    assert msg in ra.lib().ra_last_error().decode()
+
+
+def test_write_zero_tokens_is_a_no_op():
+    assert call_write(dims(), n=0) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(ra, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(ra, "_lib", None)
+    with pytest.raises(ImportError):
+        ra.lib()

@@ -1,0 +1,241 @@
+"""GPU parity: libringattn (through its C ABI) against the fp64 oracle.
+
+Bars (written in each test): bf16 output max|d| <= 1e-2, fp32 output
+<= 1e-3, LSE <= 1e-4 (absolute), strided KV-cache write bit-exact.  Pad rows
+are not written by the library: their sentinel must survive.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import context_causal_attention_ring_amd as ra
+import oracle
+import workloads
+from helpers import Case, NAN_BF16, bits, f64, from_bits, sample_rows, striped_cache
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16, TOL_F32, TOL_LSE = 1e-2, 1e-3, 1e-4
+SENTINEL = -12288.0  # exact in bf16 and fp32
+
+
+REPORT = []
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    ra.lib()
+    yield
+    path = os.environ.get("RINGATTN_PARITY_REPORT")
+    if path:
+        with open(path, "w") as f:
+            json.dump(REPORT, f, indent=1)
+
+
+def run(case, out_fp32=False, ring_start=0, fill_out=SENTINEL):
+    """Launch the fused kernel on a Case; out/lse pre-filled with a sentinel."""
+    w, d = case.w, case.d
+    C, NQ, HD = w.q_rows, w.nq, w.hd
+    out = torch.full((C, NQ, HD), fill_out, device="cuda",
+                     dtype=torch.float32 if out_fp32 else torch.bfloat16)
+    lse = torch.full((NQ, C), fill_out, device="cuda", dtype=torch.float32)
+    dims = ra.make_dims(d["q"], d["k_cur"], w.shard_cap, real_rows=w.real_rows,
+                        head_rows=w.head_rows, scale=w.scale, out_fp32=out_fp32)
+    print(f"[gpu] ring_attn_prefill {w.name} C={C} L={w.cache_len} P={w.P} I={w.interleave} "
+          f"NQ={NQ} NKV={w.nkv} HD={HD} real={w.real_rows} start={ring_start}", flush=True)
+    ra.ring_attn_prefill(d["q"], d["k_cache"], d["v_cache"], d["k_cur"], d["v_cur"], w.cache_len,
+                         w.P, ra.StripeLayout(w.interleave, ring_start), out, lse, dims)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def compare(case, out, lse, rows, tol):
+    o_ref, l_ref = case.oracle_rows(rows)
+    o = out.double().numpy()[rows]
+    l = lse.double().numpy()[:, rows]
+    d_out = np.abs(o - o_ref).max()
+    d_lse = np.abs(l - l_ref).max()
+    print(f"    rows={len(rows)} max|d out|={d_out:.3e} max|d lse|={d_lse:.3e}", flush=True)
+    REPORT.append(dict(case=case.w.name, rows=len(rows), tol=tol, max_d_out=float(d_out),
+                       max_d_lse=float(d_lse)))
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    assert d_out <= tol, d_out
+    assert d_lse <= TOL_LSE, d_lse
+    return d_out
+
+
+def check_pads_untouched(case, out, lse):
+    r = case.w.real_rows
+    assert (out[r:].float() == SENTINEL).all()
+    assert (lse[:, r:] == SENTINEL).all()
+
+
+# ---------------------------------------------------------------- write
+
+WRITE_CASES = [
+    # (name, nkv, hd, cache_len, P, interleave, n_tokens, extra_cap)
+    ("tiny", 1, 64, 512, 2, 1, 128, 0),
+    ("32k", 2, 256, 28672, 8, 1, 4096, 0),
+    ("interleave16", 2, 128, 1000, 3, 16, 300, 5),
+    ("short-cache", 1, 64, 3, 8, 1, 70, 2),
+    ("empty-cache", 2, 64, 0, 4, 2, 33, 0),
+    ("128k-real", 2, 256, 126973, 8, 1, 3548, 0),
+]
+
+
+@pytest.mark.parametrize("name,nkv,hd,L,P,I,n,extra", WRITE_CASES)
+def test_kv_cache_write_bit_exact(name, nkv, hd, L, P, I, n, extra):
+    cap = max(oracle.shard_lengths(L + n, P, I)) + extra
+    rng = np.random.default_rng(L + n)
+    k_cache0 = rng.integers(0, 2 ** 16, size=(P, cap, nkv, hd), dtype=np.uint16)
+    v_cache0 = rng.integers(0, 2 ** 16, size=(P, cap, nkv, hd), dtype=np.uint16)
+    k_cur = rng.integers(0, 2 ** 16, size=(n + 5, nkv, hd), dtype=np.uint16)  # + pad rows
+    v_cur = rng.integers(0, 2 ** 16, size=(n + 5, nkv, hd), dtype=np.uint16)
+    kc_ref, vc_ref = oracle.kv_cache_write_ref(k_cache0, v_cache0, k_cur, v_cur, n, L, P, I)
+    kc, vc = from_bits(k_cache0).cuda(), from_bits(v_cache0).cuda()
+    dims = ra.Dims(num_q_heads=nkv, num_kv_heads=nkv, head_dim=hd, q_rows=n + 5, head_rows=0,
+                   real_rows=n, shard_cap=cap, scale=0.0, out_dtype=0)
+    print(f"[gpu] kv_cache_write {name} L={L} P={P} I={I} n={n}", flush=True)
+    ra.kv_cache_write(from_bits(k_cur).cuda(), from_bits(v_cur).cuda(), n, kc, vc, L, P,
+                      ra.StripeLayout(I, 0), dims)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(kc.cpu()), kc_ref)
+    assert np.array_equal(bits(vc.cpu()), vc_ref)
+
+
+# ---------------------------------------------------------------- fused attention, full parity
+
+def small(name, **kw):
+    base = dict(seed=7, nq=8, nkv=2, hd=128, cache_len=1000, P=3, head_rows=150, tail_rows=150,
+                real_rows=300)
+    base.update(kw)
+    w = workloads.custom(name, **base)
+    cap = max(oracle.shard_lengths(w.cache_len + w.real_rows, w.P, w.interleave) + [1])
+    return workloads.with_fields(w, shard_cap=cap)
+
+
+FULL_CASES = [
+    workloads.CONFIGS["tiny"],
+    small("hd128-P3-ragged", real_rows=277),
+    small("hd256-gqa16-P8", nq=32, nkv=2, hd=256, cache_len=700, P=8, head_rows=96,
+          tail_rows=96, real_rows=192),
+    small("hd64-P1", hd=64, P=1, cache_len=333),
+    small("P2-interleave16", P=2, interleave=16, cache_len=517),
+    small("P4-cache-lt-P", P=4, cache_len=3, nq=4, nkv=1),
+    small("empty-cache", cache_len=0, P=2),
+    small("all-pad-tail", real_rows=150),
+    small("odd-group3", nq=6, nkv=2, hd=64, cache_len=200, P=5, real_rows=61, head_rows=40,
+          tail_rows=40),
+    small("mha", nq=2, nkv=2, hd=256, cache_len=129, P=2, real_rows=65, head_rows=33,
+          tail_rows=33),
+]
+
+
+@pytest.mark.parametrize("w", FULL_CASES, ids=lambda w: w.name)
+def test_parity_full(w):
+    case = Case(w).to_device()
+    out, lse = run(case)
+    compare(case, out, lse, list(range(w.real_rows)), TOL_BF16)
+    check_pads_untouched(case, out, lse)
+
+
+@pytest.mark.parametrize("w", [FULL_CASES[0], FULL_CASES[1], FULL_CASES[2]], ids=lambda w: w.name)
+def test_parity_fp32_output(w):
+    case = Case(w).to_device()
+    out, lse = run(case, out_fp32=True)
+    compare(case, out, lse, list(range(w.real_rows)), TOL_F32)
+
+
+def test_ring_start_invariance_and_determinism():
+    w = FULL_CASES[2]
+    case = Case(w).to_device()
+    a, la = run(case)
+    b, lb = run(case)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
+    c, lc = run(case, ring_start=w.P - 1)
+    rows = list(range(w.real_rows))
+    assert (a[rows].float() - c[rows].float()).abs().max().item() <= TOL_BF16
+    assert (la[:, rows] - lc[:, rows]).abs().max().item() <= TOL_LSE
+
+
+def test_unused_slots_and_future_nan_do_not_leak():
+    """NaN vs zero in unused shard slots and in pad rows: real rows bitwise equal."""
+    w = FULL_CASES[1]
+    a_case = Case(w, fill=NAN_BF16).to_device()
+    b_case = Case(w, fill=0).to_device()
+    for k in ("q", "k_cur", "v_cur"):  # pads: NaN in a, zero in b
+        b_case.d[k][w.real_rows:] = 0
+    a, la = run(a_case)
+    b, lb = run(b_case)
+    r = w.real_rows
+    assert torch.equal(a[:r].view(torch.int16), b[:r].view(torch.int16))
+    assert torch.equal(la[:, :r], lb[:, :r])
+
+
+def test_negative_control():
+    """A perturbed cache must be far outside the parity tolerance."""
+    w = FULL_CASES[2]
+    case = Case(w).to_device()
+    out, lse = run(case)
+    rows = list(range(w.real_rows))
+    d_ok = compare(case, out, lse, rows, TOL_BF16)
+    bad = Case(workloads.with_fields(w, seed=w.seed + 100))
+    t = case.t
+    o_bad, _ = oracle.attention_rows(f64(t["q"]), f64(bad.t["k_cache_tok"]),
+                                     f64(bad.t["v_cache_tok"]), f64(t["k_cur"]), f64(t["v_cur"]),
+                                     rows, w.scale)
+    d_bad = np.abs(out.double().numpy()[rows] - o_bad).max()
+    print(f"    negative control: parity {d_ok:.3e} vs perturbed cache {d_bad:.3e}", flush=True)
+    assert d_bad >= 10 * max(d_ok, 1e-4)
+
+
+def test_two_region_merge_agreement():
+    """The fused result equals the oracle's two-pass (cache-only + current-only) merge."""
+    w = FULL_CASES[1]
+    case = Case(w).to_device()
+    out, lse = run(case, out_fp32=True)
+    t = case.t
+    rows = list(range(w.real_rows))
+    args = (f64(t["q"]), f64(t["k_cache_tok"]), f64(t["v_cache_tok"]), f64(t["k_cur"]),
+            f64(t["v_cur"]), rows, w.scale)
+    o1, l1 = oracle.attention_rows(*args, current=False)
+    o2, l2 = oracle.attention_rows(*args, cache=False)
+    om, lm = oracle.two_pass_merge(o1, l1, o2, l2)
+    assert np.abs(out.double().numpy()[rows] - om).max() <= TOL_F32
+    assert np.abs(lse.double().numpy()[:, rows] - lm).max() <= TOL_LSE
+
+
+# ---------------------------------------------------------------- full-size configs, sampled rows
+
+@pytest.mark.parametrize("name,n_random", [("8k", 40), ("32k", 40), ("128k", 32), ("1m", 4)])
+def test_parity_full_size_sampled(name, n_random):
+    w = workloads.CONFIGS[name]
+    case = Case(w).to_device()
+    out, lse = run(case)
+    rows = sample_rows(w, n_random, seed=w.seed)
+    compare(case, out, lse, rows, TOL_BF16)
+    check_pads_untouched(case, out, lse)
+
+
+def test_32k_write_then_prefill():
+    """The 32k step as timed: strided write of the chunk, then the fused
+    prefill on the same stream; the write must not disturb the prefill."""
+    w = workloads.CONFIGS["32k"]
+    case = Case(w).to_device()
+    d = case.d
+    dims = ra.make_dims(d["q"], d["k_cur"], w.shard_cap, real_rows=w.real_rows,
+                        head_rows=w.head_rows, scale=w.scale)
+    print("[gpu] 32k kv_cache_write + ring_attn_prefill", flush=True)
+    ra.kv_cache_write(d["k_cur"], d["v_cur"], w.real_rows, d["k_cache"], d["v_cache"],
+                      w.cache_len, w.P, ra.StripeLayout(1, 0), dims)
+    out, lse = run(case)
+    kc_ref, vc_ref = oracle.kv_cache_write_ref(bits(case.kc), bits(case.vc), bits(case.t["k_cur"]),
+                                               bits(case.t["v_cur"]), w.real_rows, w.cache_len,
+                                               w.P, 1)
+    assert np.array_equal(bits(d["k_cache"].cpu()), kc_ref)
+    assert np.array_equal(bits(d["v_cache"].cpu()), vc_ref)
+    compare(case, out, lse, sample_rows(w, 16, seed=5), TOL_BF16)
