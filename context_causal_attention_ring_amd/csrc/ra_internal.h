@@ -41,7 +41,7 @@ struct WriteParams {
 
 // Tile geometry of the fused kernel for a head dimension.
 constexpr int kWaves = 4;           // waves per workgroup
-constexpr int kRowsPerWave = 32;    // (token, head) rows per wave
+constexpr int kRowsPerWave = 32;    // (token, head) rows per wave (one 32-row MFMA block)
 constexpr int kRowsPerWG = kWaves * kRowsPerWave;
 constexpr int kBKV = 64;            // keys per KV tile
 

@@ -9,25 +9,36 @@
 // separate code paths.
 //
 // Mapping onto CDNA4:
-//  * A workgroup owns 128 (token, query-head) rows of ONE KV head: the GQA
+//  * A workgroup owns 256 (token, query-head) rows of ONE KV head: the GQA
 //    group's query heads are packed into the rows, so every K/V tile is
-//    fetched once per group.  Each of the 4 waves owns 32 rows and keeps its
-//    Q rows in registers for the whole walk.
+//    fetched once per group.  Each of the 4 waves (one per SIMD) owns 64
+//    rows as two 32-row blocks and keeps their Q in registers for the whole
+//    walk; every K or V operand read from LDS feeds two MFMAs.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: each lane then holds 16 keys of ONE row, so
 //    the row max / sum are in-lane plus one exchange with lane^32, and the
 //    probabilities are already laid out as the B operand of O^T = V^T P^T
 //    (the key order inside a 16-key step is permuted identically on both
-//    operands, which leaves the contraction unchanged).
-//  * K/V tiles are staged in LDS, double buffered (the two "bkv slots"),
-//    row-major with a 16-byte-chunk XOR swizzle.  V^T operands are read with
-//    ds_read_b64_tr_b16, which transposes 4x16 blocks in flight.
-//  * Fetches go through buffer descriptors whose size is the valid length of
-//    the visited region: rows past a shard's length (or past the real chunk
-//    rows) come back as zeros without touching memory -- the zero-size fetch
-//    of the inactive region, chosen by value.  The mask is one bound per
-//    lane, key < lim, with lim = shard length in the ring region and
-//    token + 1 (causal) in the current region.
+//    operands, which leaves the contraction unchanged).  The fp32
+//    accumulator (64 rows x HD) lives in the AGPRs.
+//  * K/V tiles of 32 keys go HBM -> LDS by buffer_load ... lds (no register
+//    staging), three LDS slots deep: while tile v's scores are computed,
+//    tile v+1 is in flight and tile v-1's values are still being consumed.
+//    Rows are stored with a 16-byte-chunk XOR swizzle chosen per operand so
+//    that K reads (32 rows, one chunk) and transposed V reads
+//    (ds_read_b64_tr_b16, 4 rows x 4 chunks) are both bank-conflict free.
+//  * Fetches go through buffer descriptors whose size is the valid length
+//    of the visited region: rows past a shard's length (or past the real
+//    chunk rows) come back as zeros without touching memory -- the
+//    zero-size fetch of the inactive region, chosen by value.  The mask is
+//    one bound per row, key < lim, with lim = shard length in the ring
+//    region and token + 1 (causal) in the current region; tiles that no
+//    bound cuts skip the compare entirely.
+//  * Online softmax in log2 units with a lazy running max: the
+//    accumulator is rescaled only when some row's max grows by more than
+//    kTau (a wave vote), so the common tile costs max, fma, exp2, add and
+//    a bf16 pack per score.  The softmax of tile v is issued between the
+//    P.V MFMAs of tile v-1, which do not depend on it.
 //  * Workgroup ids are remapped so that the workgroups resident on one XCD
 //    share a KV head and walk the same tiles, keeping the re-streamed K/V in
 //    that XCD's L2.
@@ -37,29 +48,32 @@ namespace ra {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
+// Lazy-rescale threshold (log2 units): probabilities stay <= 2^kTau.  With
+// fp32 output the running max is exact (threshold 0), so the dominant
+// probability of each row is exactly 1 and carries no bf16 rounding.
+template <bool F32OUT>
+constexpr float kTau = F32OUT ? 0.0f : 8.0f;
 
-// XOR pattern for the 16-byte chunk index of LDS tile row `row`.  For a
-// 512-byte row it makes both access patterns conflict-free: 16 consecutive
-// rows at one chunk (K operand reads) and 4 consecutive rows x 4 chunks
-// (transposed V reads).
-__device__ __forceinline__ int swz(int row, int cpr) {
+// Chunk swizzles (16-byte chunks within a tile row).  K rows are read 32 at
+// a time at one chunk: 16 consecutive rows must land in 16 distinct bank
+// groups.  V rows are read by the transposing loads as 4 rows x 4 chunks:
+// 4*(row & 3) spreads them, and rows r and r + 8 (the two reads of one
+// operand) share a pattern so their addresses differ by a constant.
+__device__ __forceinline__ int swz_k(int row, int cpr) {
   return (4 * (row & 3) + ((row >> 2) & 3)) & (cpr - 1);
 }
-
-// Element offset of (row, col) in an LDS tile stored [rows][D], swizzled.
-template <int D>
-__device__ __forceinline__ int lds_off(int row, int col) {
-  return row * D + (((col >> 3) ^ swz(row, D / 8)) << 3) + (col & 7);
-}
+__device__ __forceinline__ int swz_v(int row, int cpr) { return (4 * (row & 3)) & (cpr - 1); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // Raw buffer (stride 0): loads at byte offsets >= `bytes` return zero.
@@ -67,23 +81,70 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
-template <int D>
-__global__ __launch_bounds__(kWaves * 64) void ring_attn_fused_kernel(FusedParams p) {
-  constexpr int NT = kWaves * 64;
+// 16 bytes per lane from a buffer into LDS at dst + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* dst, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const uint16_t* base, uint32_t byte_off) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+
+__device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* base, uint32_t byte_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(reinterpret_cast<const char*>(base) + byte_off));
+}
+
+// acc *= alpha on a 16-wide accumulator kept in AGPRs: read, multiply and
+// write back in place, so the accumulator never needs a VGPR home.  The
+// caller waits out the MFMA result hazard (see rescale_agprs).
+__device__ __forceinline__ void scale_agprs(f32x16& a, float alpha) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only parses device code
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float x = a[i];
+    float t;
+    asm volatile(
+        "v_accvgpr_read_b32 %1, %0\n\t"
+        "v_mul_f32 %1, %1, %2\n\t"
+        "v_accvgpr_write_b32 %0, %1"
+        : "+a"(x), "=&v"(t)
+        : "v"(alpha));
+    a[i] = x;
+  }
+#endif
+}
+
+__device__ __forceinline__ float wave_max_pair(float x) {
+  // max with the lane 32 apart (the other half of the same row's keys)
+  return __builtin_elementwise_maximum(x, __shfl_xor(x, 32));
+}
+
+struct True { static constexpr bool value = true; };
+struct False { static constexpr bool value = false; };
+
+template <int D, bool F32OUT>
+__global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedParams p) {
   constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
-  constexpr int NKB = kBKV / 32;          // 32-key blocks per tile
   constexpr int NDB = D / 32;             // 32-wide d blocks of the output
   constexpr int NKS = D / 16;             // k-steps of the QK^T contraction
+  constexpr int NKX = NKS < 8 ? NKS : 8;  // distinct K read patterns
+  constexpr int NKB = kBKV / 32;          // 32-key blocks per tile
+  constexpr int NPS = kBKV / 16;          // 16-key steps of P.V per tile
   constexpr int TILE = kBKV * D;          // elements of one K or V tile
-  constexpr int LOADS = kBKV * CPR / NT;  // 16-byte chunks per thread per tile
-  static_assert((kBKV * CPR) % NT == 0, "tile must split evenly over threads");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * TILE];  // [slot][K, V]
+  constexpr int DPW = kBKV * CPR / (64 * kWaves);  // DMA instructions per wave per tile
+  static_assert(DPW >= 1 && DPW * 64 * kWaves == kBKV * CPR, "tile must split over the waves");
+  // LDS: two K slots then two V slots.
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * TILE];
+  uint16_t* const kslot0 = lds;
+  uint16_t* const vslot0 = lds + 2 * TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int h = lane >> 5;   // lane half: keys / d interleave of the MFMA layouts
-  const int lr = lane & 31;  // row within the wave
+  const int lr = lane & 31;  // this lane's row within the wave
 
   // XCD-aware workgroup order (grid is a multiple of 8).
   const int nwg = gridDim.x;
@@ -99,38 +160,47 @@ __global__ __launch_bounds__(kWaves * 64) void ring_attn_fused_kernel(FusedParam
   const int head = g * p.group + (row - token * p.group);
   const bool row_ok = token < p.real_rows;
 
-  // Q^T operand: lane holds d = 16 s + 8 h + [0, 8) of its row.
+  // Q^T operand: lane holds d = 16 s + 8 h + [0, 8) of its row.  Loaded
+  // through a descriptor bounded at the real rows, so rows past them read 0.
   bf16x8 qreg[NKS];
   {
-    const uint16_t* qp = p.q + ((int64_t)token * p.nq + head) * D + 8 * h;
+    const __amdgpu_buffer_rsrc_t qr =
+        make_rsrc(p.q, (uint32_t)p.real_rows * (uint32_t)p.nq * D * 2);
+    const uint32_t qoff = ((uint32_t)token * p.nq + head) * D * 2 + 16 * h;
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      i16x8 x = row_ok ? *reinterpret_cast<const i16x8*>(qp + 16 * s) : i16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      qreg[s] = __builtin_bit_cast(bf16x8, x);
-    }
+    for (int s = 0; s < NKS; ++s)
+      qreg[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff + 32 * s, 0, 0));
   }
 
   // Tile schedule: ring region = P shard visits of nb tiles, then the
   // current tiles up to this workgroup's last real token.
   const int wg_last = min(p.real_rows - 1, (row0 + kRowsPerWG - 1) / p.group);
+  const int wg_first = row0 / p.group;
   const int n_ring = p.P * p.nb;
-  const int n_cur = (wg_last + kBKV) / kBKV;
+  const int n_cur = wg_last / kBKV + 1;
   const int T = n_ring + n_cur;
   const uint32_t rowstride = (uint32_t)p.nkv * D * 2;  // bytes between tokens
   const uint32_t cur_bytes = (uint32_t)p.real_rows * rowstride;
 
-  // Per-tile source, chosen by value: descriptor, first byte offset and the
-  // key bound (relative to the tile) of the ring or the current region.
+  // Per-tile source, chosen by value.
   struct Src {
     __amdgpu_buffer_rsrc_t kr, vr;
-    uint32_t off;
-    int lim_uniform;  // ring: valid keys left in the shard
+    uint32_t off;     // byte offset of the tile's first row
+    int lim_ring;     // ring: valid keys of the shard left from this tile
+    int key0;         // current: chunk position of the tile's first key
     bool in_ring;
-    int tile_key0;    // current: first key position of the tile
   };
   auto source = [&](int v) {
     Src s;
     s.in_ring = v < n_ring;
+    if (v >= T) {  // past the walk: a zero-size fetch (fills the slot with zeros)
+      s.kr = s.vr = make_rsrc(p.k_cur, 0);
+      s.off = 0;
+      s.lim_ring = 0;
+      s.key0 = 0;
+      s.in_ring = false;
+      return s;
+    }
     if (s.in_ring) {
       const int k = v / p.nb;
       const int b = v - k * p.nb;
@@ -144,141 +214,238 @@ __global__ __launch_bounds__(kWaves * 64) void ring_attn_fused_kernel(FusedParam
       s.kr = make_rsrc(p.k_cache + base, bytes);
       s.vr = make_rsrc(p.v_cache + base, bytes);
       s.off = (uint32_t)b * kBKV * rowstride;
-      s.lim_uniform = (int)(len - (int64_t)b * kBKV);
-      s.tile_key0 = 0;
+      s.lim_ring = (int)(len - (int64_t)b * kBKV);
+      s.key0 = 0;
     } else {
       const int c = v - n_ring;
       s.kr = make_rsrc(p.k_cur + g * D, cur_bytes);
       s.vr = make_rsrc(p.v_cur + g * D, cur_bytes);
       s.off = (uint32_t)c * kBKV * rowstride;
-      s.lim_uniform = 0;
-      s.tile_key0 = c * kBKV;
+      s.lim_ring = 0;
+      s.key0 = c * kBKV;
     }
     return s;
   };
 
-  i32x4 kst[LOADS], vst[LOADS];
-  auto load_tile = [&](int v) {
-    const Src s = source(v);
+  // DMA: wave-instruction i of this wave fills physical chunks
+  // [(wave*DPW + i)*64, +64) of a tile, lane L the chunk at +L; the lane
+  // fetches the logical chunk that the swizzle stores there.
+  uint32_t dma_k[DPW], dma_v[DPW];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int q = tid + i * NT;
-      const int j = q / CPR, c = q % CPR;
-      const uint32_t off = s.off + (uint32_t)j * rowstride + c * 16;
-      kst[i] = __builtin_amdgcn_raw_buffer_load_b128(s.kr, off, 0, 0);
-      vst[i] = __builtin_amdgcn_raw_buffer_load_b128(s.vr, off, 0, 0);
-    }
-  };
-  auto store_tile = [&](int slot) {
-    uint16_t* kl = lds + slot * 2 * TILE;
-    uint16_t* vl = kl + TILE;
+  for (int i = 0; i < DPW; ++i) {
+    const int pch = (wave * DPW + i) * 64 + lane;
+    const int r = pch / CPR, pc = pch % CPR;
+    dma_k[i] = (uint32_t)r * rowstride + (uint32_t)((pc ^ swz_k(r, CPR)) * 16);
+    dma_v[i] = (uint32_t)r * rowstride + (uint32_t)((pc ^ swz_v(r, CPR)) * 16);
+  }
+  auto issue_k = [&](const Src& s, uint16_t* dst) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int q = tid + i * NT;
-      const int j = q / CPR, c = q % CPR;
-      const int o = j * D + ((c ^ swz(j, CPR)) << 3);
-      *reinterpret_cast<i32x4*>(kl + o) = kst[i];
-      *reinterpret_cast<i32x4*>(vl + o) = vst[i];
-    }
+    for (int i = 0; i < DPW; ++i)
+      dma16(s.kr, dst + (wave * DPW + i) * 512, dma_k[i], s.off);
   };
+  auto issue_v = [&](const Src& s, uint16_t* dst) {
+#pragma unroll
+    for (int i = 0; i < DPW; ++i)
+      dma16(s.vr, dst + (wave * DPW + i) * 512, dma_v[i], s.off);
+  };
+
+  // K operand reads: lane reads row 32 kb + lr, chunk 2s + h.  (2s + h) ^ swz
+  // = 2s ^ x with x = h ^ swz < 16, so steps s and s + 8 differ by 256 bytes
+  // and key blocks by 32 rows.
+  uint32_t kx[NKX];
+  {
+    const int x = h ^ swz_k(lr, CPR);
+#pragma unroll
+    for (int j = 0; j < NKX; ++j) kx[j] = (uint32_t)(lr * D * 2 + (((2 * j) ^ x) << 4));
+  }
+  // Transposed V reads.  Lane (block b4 = lane/16, i16 = lane%16) supplies
+  // row 4h + i16/4 (+8 for the second half of the 8 keys, +16 per k-step)
+  // and columns 32 db + 16 (b4 & 1) + 4 (i16 & 3); it receives d =
+  // 32 db + 16 (b4 & 1) + i16 for 4 consecutive keys.
+  constexpr int NVX = NDB < 4 ? NDB : 4;
+  uint32_t vx[NVX];
+  {
+    const int b4 = lane >> 4, i16 = lane & 15;
+    const int r = 4 * h + (i16 >> 2);
+    const int sw = swz_v(r, CPR);
+    const int cin = 2 * (b4 & 1) + ((i16 & 3) >> 1);  // chunk within the 32-col block
+#pragma unroll
+    for (int db = 0; db < NVX; ++db)
+      vx[db] = (uint32_t)(r * D * 2 + (((4 * db + cin) ^ sw) << 4) + 8 * (i16 & 1));
+  }
 
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-  float m_run = kNegInf;  // running max, log2 units
-  float l_run = 0.f;      // running sum over this lane's half of the keys
+  float mlog = kNegInf;  // running max used for the exponent, log2 units
+  float lsum = 0.f;      // this lane's share of the row sum
+  float lsum_q = 0.f;    // the same over bf16-rounded probabilities (fp32 output)
+  const float c2 = p.scale_log2e;
 
-  if (T > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  // Lane geometry of the transposed V reads (4 x 16 blocks per 16 lanes).
-  const int b4 = lane >> 4, i16 = lane & 15;
-  const int vcol = 16 * (b4 & 1) + 4 * (i16 & 3);
-  const int vrow = 4 * h + (i16 >> 2);
-
-  for (int v = 0; v < T; ++v) {
-    if (v + 1 < T) load_tile(v + 1);
-    const uint16_t* kl = lds + (v & 1) * 2 * TILE;
-    const uint16_t* vl = kl + TILE;
-    const Src src = source(v);
-    const int lim = src.in_ring ? src.lim_uniform : token + 1 - src.tile_key0;
-
-    // S^T = K Q^T for the tile's 32-key blocks.
-    f32x16 S[NKB];
+  // S^T = K Q^T for one tile.  The two key blocks' chains are interleaved
+  // and each K operand is read from LDS two k-steps before its MFMA.
+  auto qk = [&](const uint16_t* kt, f32x16 (&S)[NKB]) {
+    auto kop = [&](int s, int kb) {
+      return lds_read_b128(kt, kx[s & 7] + (s >> 3) * 256 + kb * 32 * D * 2);
+    };
+    bf16x8 ka[3][NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       S[kb] = f32x16{};
-      const int krow = kb * 32 + lr;
+      ka[0][kb] = kop(0, kb);
+      if (NKS > 1) ka[1][kb] = kop(1, kb);
+    }
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            kl + krow * D + (((2 * s + h) ^ swz(krow, CPR)) << 3));
-        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], S[kb], 0, 0, 0);
+    for (int s = 0; s < NKS; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        if (s + 2 < NKS) ka[(s + 2) % 3][kb] = kop(s + 2, kb);
+        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s % 3][kb], qreg[s], S[kb], 0, 0, 0);
       }
     }
+  };
 
-    // Online softmax, shared by both regions.  Register i of block kb holds
-    // key kb*32 + (i/4)*8 + 4h + i%4 of this lane's row.
-    float mx = kNegInf;
+  // O^T += V^T P^T for one tile.
+  auto pv = [&](const uint16_t* vt, const bf16x8 (&pb)[NPS]) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb * 32 + (i >> 2) * 8 + 4 * h + (i & 3);
-        float t = S[kb][i] * p.scale_log2e;
-        t = key < lim ? t : kNegInf;
-        S[kb][i] = t;
-        mx = fmaxf(mx, t);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float ls = 0.f;
-    bf16x8 pb[2 * NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(S[kb][i] - m_use);
-        ls += e;
-        pb[2 * kb + (i >> 3)][i & 7] = (__bf16)e;
-      }
-    }
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-
-    // O^T += V^T P^T, 16 keys per step.
-#pragma unroll
-    for (int ks = 0; ks < kBKV / 16; ++ks) {
+    for (int ks = 0; ks < NPS; ++ks) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int r = 16 * ks + vrow;
-        const int col = db * 32 + vcol;
-        const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vl + lds_off<D>(r, col)));
-        const i16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vl + lds_off<D>(r + 8, col)));
+        const uint32_t o = vx[db & 3] + (db >> 2) * 256 + ks * 16 * D * 2;
+        const i16x4 x1 = lds_read_tr(vt, o);
+        const i16x4 x2 = lds_read_tr(vt, o + 8 * D * 2);
         const i16x8 x = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), pb[ks],
                                                           acc[db], 0, 0, 0);
       }
     }
+  };
 
-    if (v + 1 < T) store_tile((v + 1) & 1);
+  // Region by value: keys with index >= lim in the tile are masked.
+  auto mask = [&](f32x16 (&S)[NKB], int lim) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb * 32 + (i >> 2) * 8 + 4 * h + (i & 3);
+        S[kb][i] = key < lim ? S[kb][i] : kNegInf;
+      }
+  };
+
+  // Online softmax of one tile: probabilities into pb, returns the factor
+  // the accumulator must be scaled by (1 unless some row of the wave raised
+  // its running max by more than kTau, which `any` reports).
+  auto softmax = [&](f32x16 (&S)[NKB], bf16x8 (&pb)[NPS], bool& any) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2)
+        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(S[kb][i], S[kb][i + 1]));
+    mx = wave_max_pair(mx) * c2;  // scale > 0, so max commutes with the scaling
+    const bool need = mx > mlog + kTau<F32OUT>;
+    any = __builtin_amdgcn_ballot_w64(need) != 0;
+    const float m_new = any ? __builtin_elementwise_maximum(mlog, mx) : mlog;
+    const float alpha = (m_new == mlog) ? 1.f : __builtin_amdgcn_exp2f(mlog - m_new);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    // lsum is the exact fp32 row sum (for the LSE and, with bf16 output,
+    // the normalisation).  For fp32 output the normalisation instead uses
+    // lsum_q, the sum of the bf16-rounded probabilities that feed the P.V
+    // MFMA (v_dot2 against (1, 1)): numerator and denominator then weight
+    // every key identically, which keeps the rounding of dominant keys out
+    // of the result.
+    float ls = 0.f, lq = 0.f;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i], c2, -m_use));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i + 1], c2, -m_use));
+        ls += e0 + e1;
+        const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+        if (F32OUT) lq = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lq, false);
+        pb[2 * kb + (i >> 3)][i & 7] = pr[0];
+        pb[2 * kb + (i >> 3)][(i & 7) + 1] = pr[1];
+      }
+    lsum = lsum * alpha + ls;
+    if (F32OUT) lsum_q = lsum_q * alpha + lq;
+    mlog = m_new;
+    return alpha;
+  };
+
+  // Region by value: this row's key bound within tile v, and whether any
+  // bound of the workgroup cuts into the tile (then the compare is needed).
+  auto bounds = [&](int v, int& lim) {
+    const Src src = source(v);
+    if (src.in_ring) {
+      lim = src.lim_ring;
+      return src.lim_ring < kBKV;
+    }
+    lim = token + 1 - src.key0;
+    return src.key0 + kBKV > wg_first + 1;
+  };
+
+  // Iteration v reads K(v) and V(v-1) and fetches K(v+1) and V(v) into the
+  // slots that K(v-1) and V(v-2) left.  The scores of tile v are computed,
+  // then its softmax is issued between the P.V MFMAs of tile v-1, which do
+  // not depend on it; a rescale (rare) lands between P.V(v-1) and P.V(v).
+  // The accumulator is touched by no branch other than the rescale.
+  issue_k(source(0), kslot0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
+  __syncthreads();
+
+  auto scores = [&](int v, f32x16 (&S)[NKB]) {
+    const int sl = v & 1;
+    issue_k(source(v + 1), kslot0 + (sl ^ 1) * TILE);
+    issue_v(source(v), vslot0 + sl * TILE);
+    qk(kslot0 + sl * TILE, S);
+    int lim;
+    if (bounds(v, lim)) mask(S, lim);
+  };
+  bf16x8 pa[NPS], pb[NPS];
+  {
+    f32x16 S[NKB];
+    bool any;
+    scores(0, S);
+    softmax(S, pa, any);  // acc is still zero: no rescale needed
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
+  }
+  auto iteration = [&](int v, bf16x8 (&pold)[NPS], bf16x8 (&pnew)[NPS]) {
+    f32x16 S[NKB];
+    scores(v, S);
+    bool any;
+    const float alpha = softmax(S, pnew, any);
+    pv(vslot0 + ((v & 1) ^ 1) * TILE, pold);
+    if (any) {
+      // the last P.V MFMAs may still be writing acc: wait them out
+#if defined(__HIP_DEVICE_COMPILE__)
+      asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+#endif
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) scale_agprs(acc[db], alpha);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(v+1), V(v) have landed
+    __syncthreads();
+  };
+  int v = 1;
+  for (; v + 1 < T; v += 2) {
+    iteration(v, pa, pb);
+    iteration(v + 1, pb, pa);
+  }
+  if (v < T) {
+    iteration(v, pa, pb);
+    pv(vslot0 + (v & 1) * TILE, pb);
+  } else {
+    pv(vslot0 + ((v - 1) & 1) * TILE, pa);
   }
 
   // Epilogue: out = acc / l, lse = ln 2 * (m + log2 l).
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = lsum + __shfl_xor(lsum, 32);
+  const float l_norm = F32OUT ? lsum_q + __shfl_xor(lsum_q, 32) : l_tot;
   if (row_ok) {
-    const float inv = 1.f / l_tot;
+    const float inv = 1.f / l_norm;
     const int64_t obase = ((int64_t)token * p.nq + head) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
@@ -287,37 +454,37 @@ __global__ __launch_bounds__(kWaves * 64) void ring_attn_fused_kernel(FusedParam
         const int d0 = db * 32 + i4 * 8 + 4 * h;
         const f32x4 o = {acc[db][4 * i4] * inv, acc[db][4 * i4 + 1] * inv,
                          acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv};
-        if (p.out_f32) {
+        if (F32OUT) {
           *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase + d0) = o;
         } else {
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
           const bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
           *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.out) + obase + d0) = ob;
         }
       }
     }
     if (h == 0 && p.lse != nullptr)
-      p.lse[(int64_t)head * p.q_rows + token] = (m_run + __log2f(l_tot)) * kLn2;
+      p.lse[(int64_t)head * p.q_rows + token] = (mlog + __log2f(l_tot)) * kLn2;
   }
 }
 
 }  // namespace
 
+template <int D>
+static void launch_hd(const FusedParams& p, dim3 grid, dim3 block, hipStream_t stream) {
+  if (p.out_f32)
+    hipLaunchKernelGGL((ring_attn_fused_kernel<D, true>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((ring_attn_fused_kernel<D, false>), grid, block, 0, stream, p);
+}
+
 hipError_t launch_fused(const FusedParams& p, int head_dim, hipStream_t stream) {
-  const int grid = (p.grid_real + 7) / 8 * 8;
+  const dim3 grid((p.grid_real + 7) / 8 * 8);
   const dim3 block(kWaves * 64);
   switch (head_dim) {
-    case 64:
-      hipLaunchKernelGGL(ring_attn_fused_kernel<64>, dim3(grid), block, 0, stream, p);
-      break;
-    case 128:
-      hipLaunchKernelGGL(ring_attn_fused_kernel<128>, dim3(grid), block, 0, stream, p);
-      break;
-    case 256:
-      hipLaunchKernelGGL(ring_attn_fused_kernel<256>, dim3(grid), block, 0, stream, p);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 64: launch_hd<64>(p, grid, block, stream); break;
+    case 128: launch_hd<128>(p, grid, block, stream); break;
+    case 256: launch_hd<256>(p, grid, block, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
