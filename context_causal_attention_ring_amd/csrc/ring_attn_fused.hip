@@ -54,6 +54,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -75,16 +76,38 @@ __device__ __forceinline__ int swz_k(int row, int cpr) {
 }
 __device__ __forceinline__ int swz_v(int row, int cpr) { return (4 * (row & 3)) & (cpr - 1); }
 
+// The same descriptor as four dwords (for the inline-asm LDS copies):
+// base address, stride 0, size in bytes, raw-buffer format word.
+__device__ __forceinline__ i32x4 make_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // Raw buffer (stride 0): loads at byte offsets >= `bytes` return zero.
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
 
-// 16 bytes per lane from a buffer into LDS at dst + 16 * lane.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* dst, uint32_t voff,
+// 16 bytes per lane from a buffer into LDS at dst + 16 * lane
+// (buffer_load_dwordx4 ... lds; M0 holds the LDS address).  Issued through
+// inline asm so that the compiler does not make every later LDS read wait
+// for it: the kernel orders these copies itself (s_waitcnt vmcnt(0) and a
+// barrier before a slot is read, and a barrier after its last read before
+// it is refilled).
+__device__ __forceinline__ void dma16(const i32x4& rs, uint16_t* dst, uint32_t voff,
                                       uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
+#if defined(__HIP_DEVICE_COMPILE__)
+  // the low 32 bits of a generic LDS address are the LDS offset
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(m0), "v"(voff), "s"(rs), "s"(soff)
+      : "memory", "m0");
+#endif
 }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const uint16_t* base, uint32_t byte_off) {
@@ -142,7 +165,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int h = lane >> 5;   // lane half: keys / d interleave of the MFMA layouts
   const int lr = lane & 31;  // this lane's row within the wave
 
@@ -184,7 +207,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
 
   // Per-tile source, chosen by value.
   struct Src {
-    __amdgpu_buffer_rsrc_t kr, vr;
+    i32x4 kr, vr;
     uint32_t off;     // byte offset of the tile's first row
     int lim_ring;     // ring: valid keys of the shard left from this tile
     int key0;         // current: chunk position of the tile's first key
@@ -194,7 +217,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     Src s;
     s.in_ring = v < n_ring;
     if (v >= T) {  // past the walk: a zero-size fetch (fills the slot with zeros)
-      s.kr = s.vr = make_rsrc(p.k_cur, 0);
+      s.kr = s.vr = make_desc(p.k_cur, 0);
       s.off = 0;
       s.lim_ring = 0;
       s.key0 = 0;
@@ -211,15 +234,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
                               (int64_t)p.interleave);
       const int64_t base = ((int64_t)sh * p.shard_cap * p.nkv + g) * D;
       const uint32_t bytes = (uint32_t)len * rowstride;
-      s.kr = make_rsrc(p.k_cache + base, bytes);
-      s.vr = make_rsrc(p.v_cache + base, bytes);
+      s.kr = make_desc(p.k_cache + base, bytes);
+      s.vr = make_desc(p.v_cache + base, bytes);
       s.off = (uint32_t)b * kBKV * rowstride;
       s.lim_ring = (int)(len - (int64_t)b * kBKV);
       s.key0 = 0;
     } else {
       const int c = v - n_ring;
-      s.kr = make_rsrc(p.k_cur + g * D, cur_bytes);
-      s.vr = make_rsrc(p.v_cur + g * D, cur_bytes);
+      s.kr = make_desc(p.k_cur + g * D, cur_bytes);
+      s.vr = make_desc(p.v_cur + g * D, cur_bytes);
       s.off = (uint32_t)c * kBKV * rowstride;
       s.lim_ring = 0;
       s.key0 = c * kBKV;
@@ -229,24 +252,31 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
 
   // DMA: wave-instruction i of this wave fills physical chunks
   // [(wave*DPW + i)*64, +64) of a tile, lane L the chunk at +L; the lane
-  // fetches the logical chunk that the swizzle stores there.
-  uint32_t dma_k[DPW], dma_v[DPW];
-#pragma unroll
-  for (int i = 0; i < DPW; ++i) {
-    const int pch = (wave * DPW + i) * 64 + lane;
-    const int r = pch / CPR, pc = pch % CPR;
-    dma_k[i] = (uint32_t)r * rowstride + (uint32_t)((pc ^ swz_k(r, CPR)) * 16);
-    dma_v[i] = (uint32_t)r * rowstride + (uint32_t)((pc ^ swz_v(r, CPR)) * 16);
-  }
+  // fetches the logical chunk that the swizzle stores there.  The swizzles
+  // permute row bits, so for the instruction's first row R (uniform) and
+  // the lane's row r within it (disjoint bits) swz(R + r) = swz(R) ^ swz(r):
+  // the lane offset is a per-lane base XOR a uniform term, and R's rows go
+  // into the scalar offset.
+  constexpr int RPI = 64 / CPR;  // tile rows per DMA instruction
+  static_assert(RPI >= 1 && (RPI & (RPI - 1)) == 0, "rows per DMA instruction");
+  const int dma_r = lane / CPR, dma_pc = lane % CPR;
+  const uint32_t dma_kbase = (uint32_t)dma_r * rowstride + (uint32_t)((dma_pc ^ swz_k(dma_r, CPR)) << 4);
+  const uint32_t dma_vbase = (uint32_t)dma_r * rowstride + (uint32_t)((dma_pc ^ swz_v(dma_r, CPR)) << 4);
   auto issue_k = [&](const Src& s, uint16_t* dst) {
 #pragma unroll
-    for (int i = 0; i < DPW; ++i)
-      dma16(s.kr, dst + (wave * DPW + i) * 512, dma_k[i], s.off);
+    for (int i = 0; i < DPW; ++i) {
+      const int R = (wave * DPW + i) * RPI;
+      dma16(s.kr, dst + (wave * DPW + i) * 512, dma_kbase ^ (uint32_t)(swz_k(R, CPR) << 4),
+            s.off + (uint32_t)R * rowstride);
+    }
   };
   auto issue_v = [&](const Src& s, uint16_t* dst) {
 #pragma unroll
-    for (int i = 0; i < DPW; ++i)
-      dma16(s.vr, dst + (wave * DPW + i) * 512, dma_v[i], s.off);
+    for (int i = 0; i < DPW; ++i) {
+      const int R = (wave * DPW + i) * RPI;
+      dma16(s.vr, dst + (wave * DPW + i) * 512, dma_vbase ^ (uint32_t)(swz_v(R, CPR) << 4),
+            s.off + (uint32_t)R * rowstride);
+    }
   };
 
   // K operand reads: lane reads row 32 kb + lr, chunk 2s + h.  (2s + h) ^ swz
@@ -261,17 +291,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // Transposed V reads.  Lane (block b4 = lane/16, i16 = lane%16) supplies
   // row 4h + i16/4 (+8 for the second half of the 8 keys, +16 per k-step)
   // and columns 32 db + 16 (b4 & 1) + 4 (i16 & 3); it receives d =
-  // 32 db + 16 (b4 & 1) + i16 for 4 consecutive keys.
-  constexpr int NVX = NDB < 4 ? NDB : 4;
-  uint32_t vx[NVX];
+  // 32 db + 16 (b4 & 1) + i16 for 4 consecutive keys.  The d-block enters
+  // the chunk index as 4 db, i.e. the byte offset as XOR (db << 6).
+  uint32_t vbase;
   {
     const int b4 = lane >> 4, i16 = lane & 15;
     const int r = 4 * h + (i16 >> 2);
-    const int sw = swz_v(r, CPR);
-    const int cin = 2 * (b4 & 1) + ((i16 & 3) >> 1);  // chunk within the 32-col block
-#pragma unroll
-    for (int db = 0; db < NVX; ++db)
-      vx[db] = (uint32_t)(r * D * 2 + (((4 * db + cin) ^ sw) << 4) + 8 * (i16 & 1));
+    const int c0 = 2 * (b4 & 1) + ((i16 & 3) >> 1);  // chunk within the 32-col block
+    vbase = (uint32_t)(r * D * 2 + ((c0 ^ swz_v(r, CPR)) << 4) + 8 * (i16 & 1));
   }
 
   f32x16 acc[NDB];
@@ -311,7 +338,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     for (int ks = 0; ks < NPS; ++ks) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const uint32_t o = vx[db & 3] + (db >> 2) * 256 + ks * 16 * D * 2;
+        const uint32_t o = (vbase ^ (uint32_t)(db << 6)) + ks * 16 * D * 2;
         const i16x4 x1 = lds_read_tr(vt, o);
         const i16x4 x2 = lds_read_tr(vt, o + 8 * D * 2);
         const i16x8 x = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
@@ -332,10 +359,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       }
   };
 
-  // Online softmax of one tile: probabilities into pb, returns the factor
-  // the accumulator must be scaled by (1 unless some row of the wave raised
-  // its running max by more than kTau, which `any` reports).
-  auto softmax = [&](f32x16 (&S)[NKB], bf16x8 (&pb)[NPS], bool& any) {
+  // Online softmax of one tile, in place: S becomes the probabilities
+  // (fp32).  Returns the factor the accumulator must be scaled by (1 unless
+  // some row of the wave raised its running max by more than kTau, which
+  // `any` reports).  lsum is the exact fp32 row sum (for the LSE and, with
+  // bf16 output, the normalisation).  For fp32 output the normalisation
+  // instead uses lsum_q, the sum of the bf16-rounded probabilities that
+  // feed the P.V MFMA (v_dot2 against (1, 1)): numerator and denominator
+  // then weight every key identically.
+  auto softmax = [&](f32x16 (&S)[NKB], bool& any) {
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -348,36 +380,37 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     const float m_new = any ? __builtin_elementwise_maximum(mlog, mx) : mlog;
     const float alpha = (m_new == mlog) ? 1.f : __builtin_amdgcn_exp2f(mlog - m_new);
     const float m_use = m_new == kNegInf ? 0.f : m_new;
-    // lsum is the exact fp32 row sum (for the LSE and, with bf16 output,
-    // the normalisation).  For fp32 output the normalisation instead uses
-    // lsum_q, the sum of the bf16-rounded probabilities that feed the P.V
-    // MFMA (v_dot2 against (1, 1)): numerator and denominator then weight
-    // every key identically, which keeps the rounding of dominant keys out
-    // of the result.
-    float ls = 0.f, lq = 0.f;
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        S[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i], c2, -m_use));
+        ls += S[kb][i];
+      }
+    lsum = lsum * alpha + ls;
+    mlog = m_new;
+    return alpha;
+  };
+  // Probabilities -> bf16 B operands of P.V (and the bf16-rounded row sum).
+  auto pack = [&](const f32x16 (&S)[NKB], bf16x8 (&pb)[NPS], float alpha) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float lq = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i], c2, -m_use));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i + 1], c2, -m_use));
-        ls += e0 + e1;
-        const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+        const bf16x2 pr = {(__bf16)S[kb][i], (__bf16)S[kb][i + 1]};
         if (F32OUT) lq = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lq, false);
         pb[2 * kb + (i >> 3)][i & 7] = pr[0];
         pb[2 * kb + (i >> 3)][(i & 7) + 1] = pr[1];
       }
-    lsum = lsum * alpha + ls;
     if (F32OUT) lsum_q = lsum_q * alpha + lq;
-    mlog = m_new;
-    return alpha;
   };
 
   // Region by value: this row's key bound within tile v, and whether any
   // bound of the workgroup cuts into the tile (then the compare is needed).
-  auto bounds = [&](int v, int& lim) {
-    const Src src = source(v);
+  auto bounds = [&](const Src& src, int& lim) {
     if (src.in_ring) {
       lim = src.lim_ring;
       return src.lim_ring < kBKV;
@@ -389,57 +422,69 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // Iteration v reads K(v) and V(v-1) and fetches K(v+1) and V(v) into the
   // slots that K(v-1) and V(v-2) left.  The scores of tile v are computed,
   // then its softmax is issued between the P.V MFMAs of tile v-1, which do
-  // not depend on it; a rescale (rare) lands between P.V(v-1) and P.V(v).
-  // The accumulator is touched by no branch other than the rescale.
-  issue_k(source(0), kslot0);
+  // not depend on it; the bf16 packing of tile v follows P.V(v-1), and a
+  // rescale (rare) lands between P.V(v-1) and P.V(v).  The accumulator is
+  // touched by no branch other than the rescale.
+  Src src = source(0);
+  issue_k(src, kslot0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
   __syncthreads();
 
-  auto scores = [&](int v, f32x16 (&S)[NKB]) {
-    const int sl = v & 1;
-    issue_k(source(v + 1), kslot0 + (sl ^ 1) * TILE);
-    issue_v(source(v), vslot0 + sl * TILE);
-    qk(kslot0 + sl * TILE, S);
-    int lim;
-    if (bounds(v, lim)) mask(S, lim);
-  };
-  bf16x8 pa[NPS], pb[NPS];
-  {
-    f32x16 S[NKB];
-    bool any;
-    scores(0, S);
-    softmax(S, pa, any);  // acc is still zero: no rescale needed
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-  }
-  auto iteration = [&](int v, bf16x8 (&pold)[NPS], bf16x8 (&pnew)[NPS]) {
-    f32x16 S[NKB];
-    scores(v, S);
-    bool any;
-    const float alpha = softmax(S, pnew, any);
-    pv(vslot0 + ((v & 1) ^ 1) * TILE, pold);
+  bf16x8 pb[NPS];
+  bool any = false;    // the previous tile asked for a rescale ...
+  float alpha = 1.f;   // ... by this factor
+  // Rescale for tile v-1's max, between P.V(v-2) and P.V(v-1).
+  auto rescale = [&]() {
     if (any) {
-      // the last P.V MFMAs may still be writing acc: wait them out
 #if defined(__HIP_DEVICE_COMPILE__)
+      // the last P.V MFMAs may still be writing acc: wait them out
       asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
 #endif
 #pragma unroll
       for (int db = 0; db < NDB; ++db) scale_agprs(acc[db], alpha);
     }
+  };
+  // Issue the copies of tile v, compute its scores and mask them.
+  auto front = [&](int v, const Src& nxt, f32x16 (&S)[NKB]) {
+    const int sl = v & 1;
+    issue_k(nxt, kslot0 + (sl ^ 1) * TILE);
+    issue_v(src, vslot0 + sl * TILE);
+    qk(kslot0 + sl * TILE, S);
+    int lim;
+    if (bounds(src, lim)) mask(S, lim);
+  };
+  {  // tile 0: no P.V yet
+    const Src nxt = source(1);
+    f32x16 S[NKB];
+    front(0, nxt, S);
+    alpha = softmax(S, any);
+    pack(S, pb, alpha);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    src = nxt;
+  }
+  for (int v = 1; v < T; ++v) {
+    rescale();
+    const Src nxt = source(v + 1);
+    f32x16 S[NKB];
+    front(v, nxt, S);
+    // One basic block: the softmax of tile v (VALU) interleaved with the
+    // P.V MFMAs of tile v-1 and their LDS reads, then tile v's packing.
+    alpha = softmax(S, any);
+    pv(vslot0 + ((v & 1) ^ 1) * TILE, pb);
+    pack(S, pb, alpha);
+#pragma unroll
+    for (int i = 0; i < NDB * NPS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // 5 VALU
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(v+1), V(v) have landed
     __syncthreads();
-  };
-  int v = 1;
-  for (; v + 1 < T; v += 2) {
-    iteration(v, pa, pb);
-    iteration(v + 1, pb, pa);
+    src = nxt;
   }
-  if (v < T) {
-    iteration(v, pa, pb);
-    pv(vslot0 + (v & 1) * TILE, pb);
-  } else {
-    pv(vslot0 + ((v - 1) & 1) * TILE, pa);
-  }
+  rescale();
+  pv(vslot0 + ((T - 1) & 1) * TILE, pb);
 
   // Epilogue: out = acc / l, lse = ln 2 * (m + log2 l).
   const float l_tot = lsum + __shfl_xor(lsum, 32);
