@@ -41,9 +41,9 @@ struct WriteParams {
 
 // Tile geometry of the fused kernel for a head dimension.
 constexpr int kWaves = 4;           // waves per workgroup
-constexpr int kRowsPerWave = 32;    // (token, head) rows per wave (one 32-row MFMA block)
+constexpr int kRowsPerWave = 64;    // (token, head) rows per wave (two 32-row MFMA blocks)
 constexpr int kRowsPerWG = kWaves * kRowsPerWave;
-constexpr int kBKV = 64;            // keys per KV tile
+constexpr int kBKV = 32;            // keys per KV tile
 
 hipError_t launch_fused(const FusedParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_kv_cache_write(const WriteParams& p, hipStream_t stream);

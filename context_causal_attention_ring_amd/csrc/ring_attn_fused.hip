@@ -149,6 +149,7 @@ struct False { static constexpr bool value = false; };
 
 template <int D, bool F32OUT>
 __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedParams p) {
+  constexpr int NRB = kRowsPerWave / 32;  // 32-row MFMA blocks per wave
   constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
   constexpr int NDB = D / 32;             // 32-wide d blocks of the output
   constexpr int NKS = D / 16;             // k-steps of the QK^T contraction
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int h = lane >> 5;   // lane half: keys / d interleave of the MFMA layouts
-  const int lr = lane & 31;  // this lane's row within the wave
+  const int lr = lane & 31;  // this lane's row within each 32-row block
 
   // XCD-aware workgroup order (grid is a multiple of 8).
   const int nwg = gridDim.x;
@@ -178,21 +179,31 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   const int rt = p.row_tiles - 1 - (logical - g * p.row_tiles);  // long causal rows first
   const int row0 = rt * kRowsPerWG;
 
-  const int row = row0 + wave * kRowsPerWave + lr;
-  const int token = row / p.group;
-  const int head = g * p.group + (row - token * p.group);
-  const bool row_ok = token < p.real_rows;
+  // This lane's rows, one per row block.
+  int token[NRB], head[NRB];
+  bool row_ok[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int row = row0 + wave * kRowsPerWave + rb * 32 + lr;
+    token[rb] = row / p.group;
+    head[rb] = g * p.group + (row - token[rb] * p.group);
+    row_ok[rb] = token[rb] < p.real_rows;
+  }
 
-  // Q^T operand: lane holds d = 16 s + 8 h + [0, 8) of its row.  Loaded
-  // through a descriptor bounded at the real rows, so rows past them read 0.
-  bf16x8 qreg[NKS];
+  // Q^T operands: lane holds d = 16 s + 8 h + [0, 8) of each of its rows.
+  // Loaded through a descriptor bounded at the real rows (rows past read 0).
+  bf16x8 qreg[NRB][NKS];
   {
     const __amdgpu_buffer_rsrc_t qr =
         make_rsrc(p.q, (uint32_t)p.real_rows * (uint32_t)p.nq * D * 2);
-    const uint32_t qoff = ((uint32_t)token * p.nq + head) * D * 2 + 16 * h;
 #pragma unroll
-    for (int s = 0; s < NKS; ++s)
-      qreg[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff + 32 * s, 0, 0));
+    for (int rb = 0; rb < NRB; ++rb) {
+      const uint32_t qoff = ((uint32_t)token[rb] * p.nq + head[rb]) * D * 2 + 16 * h;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s)
+        qreg[rb][s] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff + 32 * s, 0, 0));
+    }
   }
 
   // Tile schedule: ring region = P shard visits of nb tiles, then the
@@ -204,8 +215,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   const int T = n_ring + n_cur;
   const uint32_t rowstride = (uint32_t)p.nkv * D * 2;  // bytes between tokens
   const uint32_t cur_bytes = (uint32_t)p.real_rows * rowstride;
+  const int full_i = (int)p.full * p.interleave;  // < 2^31: bounded by a shard's length
 
-  // Per-tile source, chosen by value.
+  // Per-tile source, chosen by value: descriptors of the region (sized to
+  // its valid rows), the tile's first byte, and the key bound.
   struct Src {
     i32x4 kr, vr;
     uint32_t off;     // byte offset of the tile's first row
@@ -229,15 +242,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       const int b = v - k * p.nb;
       int sh = p.ring_start - k;
       sh += (sh < 0) ? p.P : 0;
-      const int64_t len = p.full * p.interleave +
-                          min(max(p.rem - (int64_t)sh * p.interleave, (int64_t)0),
-                              (int64_t)p.interleave);
+      const int len = full_i + min(max((int)p.rem - sh * p.interleave, 0), p.interleave);
       const int64_t base = ((int64_t)sh * p.shard_cap * p.nkv + g) * D;
       const uint32_t bytes = (uint32_t)len * rowstride;
       s.kr = make_desc(p.k_cache + base, bytes);
       s.vr = make_desc(p.v_cache + base, bytes);
       s.off = (uint32_t)b * kBKV * rowstride;
-      s.lim_ring = (int)(len - (int64_t)b * kBKV);
+      s.lim_ring = len - b * kBKV;
       s.key0 = 0;
     } else {
       const int c = v - n_ring;
@@ -260,8 +271,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   constexpr int RPI = 64 / CPR;  // tile rows per DMA instruction
   static_assert(RPI >= 1 && (RPI & (RPI - 1)) == 0, "rows per DMA instruction");
   const int dma_r = lane / CPR, dma_pc = lane % CPR;
-  const uint32_t dma_kbase = (uint32_t)dma_r * rowstride + (uint32_t)((dma_pc ^ swz_k(dma_r, CPR)) << 4);
-  const uint32_t dma_vbase = (uint32_t)dma_r * rowstride + (uint32_t)((dma_pc ^ swz_v(dma_r, CPR)) << 4);
+  const uint32_t dma_kbase =
+      (uint32_t)dma_r * rowstride + (uint32_t)((dma_pc ^ swz_k(dma_r, CPR)) << 4);
+  const uint32_t dma_vbase =
+      (uint32_t)dma_r * rowstride + (uint32_t)((dma_pc ^ swz_v(dma_r, CPR)) << 4);
   auto issue_k = [&](const Src& s, uint16_t* dst) {
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
@@ -301,39 +314,41 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     vbase = (uint32_t)(r * D * 2 + ((c0 ^ swz_v(r, CPR)) << 4) + 8 * (i16 & 1));
   }
 
-  f32x16 acc[NDB];
+  f32x16 acc[NRB][NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-  float mlog = kNegInf;  // running max used for the exponent, log2 units
-  float lsum = 0.f;      // this lane's share of the row sum
-  float lsum_q = 0.f;    // the same over bf16-rounded probabilities (fp32 output)
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[rb][db] = f32x16{};
+  float mlog[NRB], lsum[NRB], lsum_q[NRB];  // running max (log2 units), row sums
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    mlog[rb] = kNegInf;
+    lsum[rb] = 0.f;     // exact fp32 sum of this lane's share of the keys
+    lsum_q[rb] = 0.f;   // the same over bf16-rounded probabilities (fp32 output)
+  }
   const float c2 = p.scale_log2e;
 
-  // S^T = K Q^T for one tile.  The two key blocks' chains are interleaved
-  // and each K operand is read from LDS two k-steps before its MFMA.
-  auto qk = [&](const uint16_t* kt, f32x16 (&S)[NKB]) {
-    auto kop = [&](int s, int kb) {
-      return lds_read_b128(kt, kx[s & 7] + (s >> 3) * 256 + kb * 32 * D * 2);
-    };
-    bf16x8 ka[3][NKB];
+  // S^T = K Q^T for one tile: every K operand read from LDS feeds the MFMAs
+  // of all NRB row blocks.
+  auto qk = [&](const uint16_t* kt, f32x16 (&S)[NRB][NKB]) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      S[kb] = f32x16{};
-      ka[0][kb] = kop(0, kb);
-      if (NKS > 1) ka[1][kb] = kop(1, kb);
-    }
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) S[rb][kb] = f32x16{};
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        if (s + 2 < NKS) ka[(s + 2) % 3][kb] = kop(s + 2, kb);
-        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s % 3][kb], qreg[s], S[kb], 0, 0, 0);
+        const bf16x8 a = lds_read_b128(kt, kx[s & 7] + (s >> 3) * 256 + kb * 32 * D * 2);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          S[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[rb][s], S[rb][kb], 0, 0, 0);
       }
     }
   };
 
-  // O^T += V^T P^T for one tile.
-  auto pv = [&](const uint16_t* vt, const bf16x8 (&pb)[NPS]) {
+  // O^T += V^T P^T for one tile: every V operand feeds all row blocks.
+  auto pv = [&](const uint16_t* vt, const bf16x8 (&pb)[NRB][NPS]) {
 #pragma unroll
     for (int ks = 0; ks < NPS; ++ks) {
 #pragma unroll
@@ -342,98 +357,113 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
         const i16x4 x1 = lds_read_tr(vt, o);
         const i16x4 x2 = lds_read_tr(vt, o + 8 * D * 2);
         const i16x8 x = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), pb[ks],
-                                                          acc[db], 0, 0, 0);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, x);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          acc[rb][db] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[rb][ks], acc[rb][db], 0, 0, 0);
       }
     }
   };
 
-  // Region by value: keys with index >= lim in the tile are masked.
-  auto mask = [&](f32x16 (&S)[NKB], int lim) {
+  // Region by value: keys with index >= lim[rb] in the tile are masked.
+  auto mask = [&](f32x16 (&S)[NRB][NKB], const int (&lim)[NRB]) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb * 32 + (i >> 2) * 8 + 4 * h + (i & 3);
-        S[kb][i] = key < lim ? S[kb][i] : kNegInf;
-      }
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb * 32 + (i >> 2) * 8 + 4 * h + (i & 3);
+          S[rb][kb][i] = key < lim[rb] ? S[rb][kb][i] : kNegInf;
+        }
   };
 
   // Online softmax of one tile, in place: S becomes the probabilities
-  // (fp32).  Returns the factor the accumulator must be scaled by (1 unless
-  // some row of the wave raised its running max by more than kTau, which
-  // `any` reports).  lsum is the exact fp32 row sum (for the LSE and, with
-  // bf16 output, the normalisation).  For fp32 output the normalisation
-  // instead uses lsum_q, the sum of the bf16-rounded probabilities that
-  // feed the P.V MFMA (v_dot2 against (1, 1)): numerator and denominator
-  // then weight every key identically.
-  auto softmax = [&](f32x16 (&S)[NKB], bool& any) {
-    float mx = kNegInf;
+  // (fp32).  alpha[rb] is the factor the accumulator must be scaled by (1
+  // unless some row of the wave raised its running max by more than kTau;
+  // the return value reports whether any did).  lsum is the exact fp32 row
+  // sum (for the LSE and, with bf16 output, the normalisation); for fp32
+  // output the normalisation uses lsum_q instead (see pack).
+  auto softmax = [&](f32x16 (&S)[NRB][NKB], float (&alpha)[NRB]) {
+    bool any = false;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int rb = 0; rb < NRB; ++rb) {
+      float mx = kNegInf;
 #pragma unroll
-      for (int i = 0; i < 16; i += 2)
-        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(S[kb][i], S[kb][i + 1]));
-    mx = wave_max_pair(mx) * c2;  // scale > 0, so max commutes with the scaling
-    const bool need = mx > mlog + kTau<F32OUT>;
-    any = __builtin_amdgcn_ballot_w64(need) != 0;
-    const float m_new = any ? __builtin_elementwise_maximum(mlog, mx) : mlog;
-    const float alpha = (m_new == mlog) ? 1.f : __builtin_amdgcn_exp2f(mlog - m_new);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    float ls = 0.f;
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+        for (int i = 0; i < 16; i += 2)
+          mx = __builtin_elementwise_maximum(
+              mx, __builtin_elementwise_maximum(S[rb][kb][i], S[rb][kb][i + 1]));
+      mx = wave_max_pair(mx) * c2;  // scale > 0, so max commutes with the scaling
+      const bool need = mx > mlog[rb] + kTau<F32OUT>;
+      const bool anyrb = __builtin_amdgcn_ballot_w64(need) != 0;
+      const float m_new = anyrb ? __builtin_elementwise_maximum(mlog[rb], mx) : mlog[rb];
+      alpha[rb] = (m_new == mlog[rb]) ? 1.f : __builtin_amdgcn_exp2f(mlog[rb] - m_new);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      float ls = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        S[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i], c2, -m_use));
-        ls += S[kb][i];
-      }
-    lsum = lsum * alpha + ls;
-    mlog = m_new;
-    return alpha;
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          S[rb][kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rb][kb][i], c2, -m_use));
+          ls += S[rb][kb][i];
+        }
+      lsum[rb] = lsum[rb] * alpha[rb] + ls;
+      mlog[rb] = m_new;
+      any |= anyrb;
+    }
+    return any;
   };
-  // Probabilities -> bf16 B operands of P.V (and the bf16-rounded row sum).
-  auto pack = [&](const f32x16 (&S)[NKB], bf16x8 (&pb)[NPS], float alpha) {
+  // Probabilities -> bf16 B operands of P.V.  For fp32 output also the sum
+  // of the bf16-rounded probabilities (v_dot2 against (1, 1)): numerator
+  // and denominator then weight every key identically.
+  auto pack = [&](const f32x16 (&S)[NRB][NKB], bf16x8 (&pb)[NRB][NPS], const float (&alpha)[NRB]) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float lq = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int rb = 0; rb < NRB; ++rb) {
+      float lq = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const bf16x2 pr = {(__bf16)S[kb][i], (__bf16)S[kb][i + 1]};
-        if (F32OUT) lq = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lq, false);
-        pb[2 * kb + (i >> 3)][i & 7] = pr[0];
-        pb[2 * kb + (i >> 3)][(i & 7) + 1] = pr[1];
-      }
-    if (F32OUT) lsum_q = lsum_q * alpha + lq;
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const bf16x2 pr = {(__bf16)S[rb][kb][i], (__bf16)S[rb][kb][i + 1]};
+          if (F32OUT) lq = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lq, false);
+          pb[rb][2 * kb + (i >> 3)][i & 7] = pr[0];
+          pb[rb][2 * kb + (i >> 3)][(i & 7) + 1] = pr[1];
+        }
+      if (F32OUT) lsum_q[rb] = lsum_q[rb] * alpha[rb] + lq;
+    }
   };
 
-  // Region by value: this row's key bound within tile v, and whether any
+  // Region by value: each row's key bound within the tile, and whether any
   // bound of the workgroup cuts into the tile (then the compare is needed).
-  auto bounds = [&](const Src& src, int& lim) {
+  auto bounds = [&](const Src& src, int (&lim)[NRB]) {
     if (src.in_ring) {
-      lim = src.lim_ring;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) lim[rb] = src.lim_ring;
       return src.lim_ring < kBKV;
     }
-    lim = token + 1 - src.key0;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) lim[rb] = token[rb] + 1 - src.key0;
     return src.key0 + kBKV > wg_first + 1;
   };
 
   // Iteration v reads K(v) and V(v-1) and fetches K(v+1) and V(v) into the
   // slots that K(v-1) and V(v-2) left.  The scores of tile v are computed,
   // then its softmax is issued between the P.V MFMAs of tile v-1, which do
-  // not depend on it; the bf16 packing of tile v follows P.V(v-1), and a
-  // rescale (rare) lands between P.V(v-1) and P.V(v).  The accumulator is
-  // touched by no branch other than the rescale.
+  // not depend on it, then tile v's bf16 packing; the rare rescale for tile
+  // v's max is applied at the top of the next iteration, between P.V(v-1)
+  // and P.V(v).  The accumulator is touched by no branch but the rescale.
   Src src = source(0);
   issue_k(src, kslot0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
   __syncthreads();
 
-  bf16x8 pb[NPS];
-  bool any = false;    // the previous tile asked for a rescale ...
-  float alpha = 1.f;   // ... by this factor
-  // Rescale for tile v-1's max, between P.V(v-2) and P.V(v-1).
+  bf16x8 pb[NRB][NPS];
+  bool any = false;       // the previous tile asked for a rescale ...
+  float alpha[NRB];       // ... by these factors
   auto rescale = [&]() {
     if (any) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -441,23 +471,25 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
 #endif
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) scale_agprs(acc[db], alpha);
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) scale_agprs(acc[rb][db], alpha[rb]);
     }
   };
   // Issue the copies of tile v, compute its scores and mask them.
-  auto front = [&](int v, const Src& nxt, f32x16 (&S)[NKB]) {
+  auto front = [&](int v, const Src& nxt, f32x16 (&S)[NRB][NKB]) {
     const int sl = v & 1;
     issue_k(nxt, kslot0 + (sl ^ 1) * TILE);
     issue_v(src, vslot0 + sl * TILE);
     qk(kslot0 + sl * TILE, S);
-    int lim;
+    int lim[NRB];
     if (bounds(src, lim)) mask(S, lim);
   };
   {  // tile 0: no P.V yet
     const Src nxt = source(1);
-    f32x16 S[NKB];
+    f32x16 S[NRB][NKB];
     front(0, nxt, S);
-    alpha = softmax(S, any);
+    any = softmax(S, alpha);
     pack(S, pb, alpha);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
@@ -466,18 +498,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   for (int v = 1; v < T; ++v) {
     rescale();
     const Src nxt = source(v + 1);
-    f32x16 S[NKB];
+    f32x16 S[NRB][NKB];
     front(v, nxt, S);
     // One basic block: the softmax of tile v (VALU) interleaved with the
     // P.V MFMAs of tile v-1 and their LDS reads, then tile v's packing.
-    alpha = softmax(S, any);
+    any = softmax(S, alpha);
     pv(vslot0 + ((v & 1) ^ 1) * TILE, pb);
     pack(S, pb, alpha);
 #pragma unroll
     for (int i = 0; i < NDB * NPS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // 5 VALU
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
+      }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(v+1), V(v) have landed
     __syncthreads();
@@ -487,18 +522,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   pv(vslot0 + ((T - 1) & 1) * TILE, pb);
 
   // Epilogue: out = acc / l, lse = ln 2 * (m + log2 l).
-  const float l_tot = lsum + __shfl_xor(lsum, 32);
-  const float l_norm = F32OUT ? lsum_q + __shfl_xor(lsum_q, 32) : l_tot;
-  if (row_ok) {
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const float l_tot = lsum[rb] + __shfl_xor(lsum[rb], 32);
+    const float l_norm = F32OUT ? lsum_q[rb] + __shfl_xor(lsum_q[rb], 32) : l_tot;
+    if (!row_ok[rb]) continue;
     const float inv = 1.f / l_norm;
-    const int64_t obase = ((int64_t)token * p.nq + head) * D;
+    const int64_t obase = ((int64_t)token[rb] * p.nq + head[rb]) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d0 = db * 32 + i4 * 8 + 4 * h;
-        const f32x4 o = {acc[db][4 * i4] * inv, acc[db][4 * i4 + 1] * inv,
-                         acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv};
+        const f32x4 o = {acc[rb][db][4 * i4] * inv, acc[rb][db][4 * i4 + 1] * inv,
+                         acc[rb][db][4 * i4 + 2] * inv, acc[rb][db][4 * i4 + 3] * inv};
         if (F32OUT) {
           *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase + d0) = o;
         } else {
@@ -508,7 +545,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       }
     }
     if (h == 0 && p.lse != nullptr)
-      p.lse[(int64_t)head * p.q_rows + token] = (mlog + __log2f(l_tot)) * kLn2;
+      p.lse[(int64_t)head[rb] * p.q_rows + token[rb]] = (mlog[rb] + __log2f(l_tot)) * kLn2;
   }
 }
 
