@@ -47,6 +47,26 @@ def alg_bytes(w, with_write):
     return b
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "ring_attn_fused_32k_hbm_traffic.md")
+FUSED_SOURCE = os.path.join(ROOT, "context_causal_attention_ring_amd", "csrc", "ring_attn_fused.hip")
+
+
+def measured_traffic(path=TRAFFIC_SUMMARY):
+    """HBM bytes per fused launch from the committed rocprofv3 counter summary,
+    or None when it was taken on a different kernel source (or is absent)."""
+    import hashlib
+    if not os.path.exists(path):
+        return None
+    rec = None
+    for line in open(path):
+        if line.startswith("traffic-json:"):
+            rec = json.loads(line.split(":", 1)[1])
+    if rec is None:
+        return None
+    sha = hashlib.sha256(open(FUSED_SOURCE, "rb").read()).hexdigest()
+    return rec["bytes_per_launch"] if rec.get("source_sha256") == sha else None
+
+
 def setup(w, device):
     import torch
     import context_causal_attention_ring_amd as ra
@@ -108,8 +128,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="32k", help="workload name (default: 32k)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per fused launch")
+    ap.add_argument("--traffic", default=TRAFFIC_SUMMARY,
+                    help="rocprofv3 summary holding the measured HBM bytes per fused launch")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for counter calibration)")
     args = ap.parse_args()
@@ -184,9 +204,7 @@ def main():
     F = alg_flops(w)
     value = F / (ms_per_step * 1e-3) / 1e12
     achieved = F / (kern_ms_avg * 1e-3) / 1e12
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+    traffic = measured_traffic(args.traffic) if w.name == "32k" else None
     props = torch.cuda.get_device_properties(dev)
     res = {
         "metric": METRIC,

@@ -22,8 +22,9 @@
 //    operands, which leaves the contraction unchanged).  The fp32
 //    accumulator (64 rows x HD) lives in the AGPRs.
 //  * K/V tiles of 32 keys go HBM -> LDS by buffer_load ... lds (no register
-//    staging), three LDS slots deep: while tile v's scores are computed,
-//    tile v+1 is in flight and tile v-1's values are still being consumed.
+//    staging) into two K and two V slots: while tile v's scores are
+//    computed, K of tile v+1 and V of tile v are in flight and the values of
+//    tile v-1 are still being consumed.
 //    Rows are stored with a 16-byte-chunk XOR swizzle chosen per operand so
 //    that K reads (32 rows, one chunk) and transposed V reads
 //    (ds_read_b64_tr_b16, 4 rows x 4 chunks) are both bank-conflict free.
@@ -38,7 +39,8 @@
 //    accumulator is rescaled only when some row's max grows by more than
 //    kTau (a wave vote), so the common tile costs max, fma, exp2, add and
 //    a bf16 pack per score.  The softmax of tile v is issued between the
-//    P.V MFMAs of tile v-1, which do not depend on it.
+//    P.V MFMAs of tile v-1, which do not depend on it, in a hand-ordered
+//    block (one MFMA pair, one V operand read, a slice of softmax work).
 //  * Workgroup ids are remapped so that the workgroups resident on one XCD
 //    share a KV head and walk the same tiles, keeping the re-streamed K/V in
 //    that XCD's L2.
@@ -140,8 +142,13 @@ __device__ __forceinline__ void scale_agprs(f32x16& a, float alpha) {
 }
 
 __device__ __forceinline__ float wave_max_pair(float x) {
-  // max with the lane 32 apart (the other half of the same row's keys)
-  return __builtin_elementwise_maximum(x, __shfl_xor(x, 32));
+  // max with the lane 32 apart (the other half of the same row's keys):
+  // v_permlane32_swap exchanges the two lane halves, and the max over
+  // {own, both swap results} holds the partner's value in every lane.
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __builtin_elementwise_maximum(
+      __builtin_elementwise_maximum(x, __uint_as_float(r[0])), __uint_as_float(r[1]));
 }
 
 struct True { static constexpr bool value = true; };
@@ -160,9 +167,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   constexpr int DPW = kBKV * CPR / (64 * kWaves);  // DMA instructions per wave per tile
   static_assert(DPW >= 1 && DPW * 64 * kWaves == kBKV * CPR, "tile must split over the waves");
   // LDS: two K slots then two V slots.
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * TILE];
+  constexpr int NSLOT = 2;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * NSLOT * TILE];
   uint16_t* const kslot0 = lds;
-  uint16_t* const vslot0 = lds + 2 * TILE;
+  uint16_t* const vslot0 = lds + NSLOT * TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -329,21 +337,28 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   const float c2 = p.scale_log2e;
 
   // S^T = K Q^T for one tile: every K operand read from LDS feeds the MFMAs
-  // of all NRB row blocks.
+  // of all NRB row blocks.  Operands are read two k-steps ahead and the
+  // schedule alternates one LDS read with the MFMAs of one step.
   auto qk = [&](const uint16_t* kt, f32x16 (&S)[NRB][NKB]) {
+    static_assert(NKB == 1, "one 32-key block per tile");
+    auto kop = [&](int s) { return lds_read_b128(kt, kx[s & 7] + (s >> 3) * 256); };
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) S[rb][kb] = f32x16{};
+    for (int rb = 0; rb < NRB; ++rb) S[rb][0] = f32x16{};
+    bf16x8 ka[3];
+    ka[0] = kop(0);
+    ka[1] = kop(1);
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
+      if (s + 2 < NKS) ka[(s + 2) % 3] = kop(s + 2);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 a = lds_read_b128(kt, kx[s & 7] + (s >> 3) * 256 + kb * 32 * D * 2);
+      for (int rb = 0; rb < NRB; ++rb)
+        S[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s % 3], qreg[rb][s], S[rb][0], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the first two LDS reads
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-          S[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[rb][s], S[rb][kb], 0, 0, 0);
-      }
+    for (int s = 0; s < NKS; ++s) {
+      if (s + 2 < NKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);                 // NRB MFMAs
     }
   };
 
@@ -456,9 +471,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // not depend on it, then tile v's bf16 packing; the rare rescale for tile
   // v's max is applied at the top of the next iteration, between P.V(v-1)
   // and P.V(v).  The accumulator is touched by no branch but the rescale.
-  Src src = source(0);
-  issue_k(src, kslot0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
+  Src s0 = source(0), s1 = source(1);  // tiles v, v+1
+  issue_k(s0, kslot0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
   __syncthreads();
 
   bf16x8 pb[NRB][NPS];
@@ -476,50 +491,113 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
         for (int db = 0; db < NDB; ++db) scale_agprs(acc[rb][db], alpha[rb]);
     }
   };
-  // Issue the copies of tile v, compute its scores and mask them.
-  auto front = [&](int v, const Src& nxt, f32x16 (&S)[NRB][NKB]) {
-    const int sl = v & 1;
-    issue_k(nxt, kslot0 + (sl ^ 1) * TILE);
-    issue_v(src, vslot0 + sl * TILE);
+  int sl = 0;  // LDS slot of tile v
+  // Issue the copies of K(v+1) and V(v), compute tile v's scores, mask them.
+  auto front = [&](f32x16 (&S)[NRB][NKB]) {
+    issue_k(s1, kslot0 + (sl ^ 1) * TILE);
+    issue_v(s0, vslot0 + sl * TILE);
     qk(kslot0 + sl * TILE, S);
     int lim[NRB];
-    if (bounds(src, lim)) mask(S, lim);
+    if (bounds(s0, lim)) mask(S, lim);
+  };
+  auto advance = [&](int v) {
+    s0 = s1;
+    s1 = source(v + 2);
+    sl ^= 1;
   };
   {  // tile 0: no P.V yet
-    const Src nxt = source(1);
     f32x16 S[NRB][NKB];
-    front(0, nxt, S);
+    front(S);
     any = softmax(S, alpha);
     pack(S, pb, alpha);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(1), V(0) have landed
     __syncthreads();
-    src = nxt;
+    advance(0);
   }
+  // P.V of the previous tile with the softmax of the current one, hand
+  // ordered: slot t issues the MFMAs of P.V step t (one V operand, read two
+  // slots ahead, for every row block) and then a fixed slice of softmax
+  // work; sched_barrier keeps slices in their slots so the VALU and
+  // transcendental work runs under the MFMAs.  Softmax work units, in
+  // dependency order: the in-lane max of each row block, the cross-lane
+  // reduction and new running max, one exp2 per score, the row sums.
+  auto pv_softmax = [&](const uint16_t* vt, f32x16 (&S)[NRB][NKB], float (&al)[NRB]) {
+    constexpr int NT = NPS * NDB;                  // P.V steps
+    constexpr int NE = NRB * NKB * 16;              // exp2 units
+    constexpr int NU = NRB + 1 + NE + 1;            // all units
+    auto vop = [&](int t) {
+      const int ks = t / NDB, db = t % NDB;
+      const uint32_t o = (vbase ^ (uint32_t)(db << 6)) + ks * 16 * D * 2;
+      const i16x4 x1 = lds_read_tr(vt, o);
+      const i16x4 x2 = lds_read_tr(vt, o + 8 * D * 2);
+      const i16x8 x = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
+      return __builtin_bit_cast(bf16x8, x);
+    };
+    float mx[NRB], m_use[NRB], ls[NRB];
+    bool any = false;
+    auto unit = [&](int u) {
+      if (u < NRB) {  // in-lane max of row block u
+        float m = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2)
+            m = __builtin_elementwise_maximum(
+                m, __builtin_elementwise_maximum(S[u][kb][i], S[u][kb][i + 1]));
+        mx[u] = m;
+      } else if (u == NRB) {  // cross-lane max, vote, new running max
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const float m = wave_max_pair(mx[rb]) * c2;  // scale > 0: max commutes
+          const bool need = m > mlog[rb] + kTau<F32OUT>;
+          const bool anyrb = __builtin_amdgcn_ballot_w64(need) != 0;
+          const float m_new = anyrb ? __builtin_elementwise_maximum(mlog[rb], m) : mlog[rb];
+          al[rb] = (m_new == mlog[rb]) ? 1.f : __builtin_amdgcn_exp2f(mlog[rb] - m_new);
+          m_use[rb] = m_new == kNegInf ? 0.f : m_new;
+          mlog[rb] = m_new;
+          ls[rb] = 0.f;
+          any |= anyrb;
+        }
+      } else if (u < NRB + 1 + NE) {  // one probability
+        const int q = u - NRB - 1;
+        const int rb = q / (NKB * 16), kb = (q / 16) % NKB, i = q % 16;
+        S[rb][kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rb][kb][i], c2, -m_use[rb]));
+        ls[rb] += S[rb][kb][i];
+      } else {  // row sums
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) lsum[rb] = lsum[rb] * al[rb] + ls[rb];
+      }
+    };
+    bf16x8 va[3];
+    va[0] = vop(0);
+    if (NT > 1) va[1] = vop(1);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int ks = t / NDB, db = t % NDB;
+      if (t + 2 < NT) va[(t + 2) % 3] = vop(t + 2);
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+        acc[rb][db] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t % 3], pb[rb][ks], acc[rb][db], 0, 0, 0);
+      // units [t*NU/NT, (t+1)*NU/NT), the rest after the last slot
+#pragma unroll
+      for (int u = t * NU / NT; u < (t + 1) * NU / NT; ++u) unit(u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return any;
+  };
   for (int v = 1; v < T; ++v) {
     rescale();
-    const Src nxt = source(v + 1);
     f32x16 S[NRB][NKB];
-    front(v, nxt, S);
-    // One basic block: the softmax of tile v (VALU) interleaved with the
-    // P.V MFMAs of tile v-1 and their LDS reads, then tile v's packing.
-    any = softmax(S, alpha);
-    pv(vslot0 + ((v & 1) ^ 1) * TILE, pb);
+    front(S);
+    any = pv_softmax(vslot0 + (sl ^ 1) * TILE, S, alpha);
     pack(S, pb, alpha);
-#pragma unroll
-    for (int i = 0; i < NDB * NPS; ++i) {
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
-      }
-    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(v+1), V(v) have landed
     __syncthreads();
-    src = nxt;
+    advance(v);
   }
   rescale();
-  pv(vslot0 + ((T - 1) & 1) * TILE, pb);
+  pv(vslot0 + (sl ^ 1) * TILE, pb);
 
   // Epilogue: out = acc / l, lse = ln 2 * (m + log2 l).
 #pragma unroll
