@@ -108,8 +108,10 @@ int ring_attn_prefill(const void* q, const void* k_cache, const void* v_cache, c
   if (d.out_dtype != RA_DTYPE_BF16 && d.out_dtype != RA_DTYPE_FP32)
     return fail(RA_ERR_INVALID_ARG, "out_dtype must be RA_DTYPE_BF16 or RA_DTYPE_FP32; got %d",
                 d.out_dtype);
-  if (!std::isfinite(d.scale))
-    return fail(RA_ERR_INVALID_ARG, "scale must be finite (0 selects 1/sqrt(head_dim))");
+  if (!std::isfinite(d.scale) || d.scale < 0.f)
+    return fail(RA_ERR_INVALID_ARG,
+                "scale must be finite and >= 0 (0 selects 1/sqrt(head_dim)); got %g",
+                (double)d.scale);
   const int32_t NQ = d.num_q_heads, NKV = d.num_kv_heads, HD = d.head_dim;
   const int32_t group = NQ / NKV;
 

@@ -77,7 +77,8 @@ typedef struct {
   int32_t head_rows;    /* 0 <= head_rows <= q_rows (scheduling metadata) */
   int32_t real_rows;    /* 0 <= real_rows <= q_rows */
   int64_t shard_cap;    /* slots allocated per shard, >= 1 */
-  float scale;          /* softmax scale; 0 selects 1/sqrt(HD) */
+  float scale;          /* softmax scale, finite and > 0; 0 selects
+                           1/sqrt(HD); negative scales are rejected */
   int32_t out_dtype;    /* ra_dtype_t of `out` */
 } ra_dims_t;
 

@@ -71,6 +71,8 @@ BAD_PREFILL = [
     (dict(d=dims(q_rows=-5, real_rows=0, head_rows=0)), 1, "q_rows"),
     (dict(d=dims(out_dtype=7)), 1, "out_dtype"),
     (dict(d=dims(scale=float("inf"))), 1, "scale"),
+    (dict(d=dims(scale=-0.125)), 1, "scale"),
+    (dict(d=dims(scale=float("nan"))), 1, "scale"),
     (dict(d=dims(), out=None), 1, "NULL"),
     (dict(d=dims(), ptrs=(FAKE + 8, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000,
                           FAKE + 0x4000000)), 1, "aligned"),
