@@ -20,7 +20,9 @@
 //    probabilities are already laid out as the B operand of O^T = V^T P^T
 //    (the key order inside a 16-key step is permuted identically on both
 //    operands, which leaves the contraction unchanged).  The fp32
-//    accumulator (64 rows x HD) lives in the AGPRs.
+//    accumulator (64 rows x HD) lives in the AGPRs; at HD = 256 the score
+//    MFMAs are one asm block that writes the scores to VGPRs, where the
+//    softmax reads them.
 //  * K/V tiles of 32 keys go HBM -> LDS by buffer_load ... lds (no register
 //    staging) into two K and two V slots: while tile v's scores are
 //    computed, K of tile v+1 and V of tile v are in flight and the values of
@@ -150,6 +152,71 @@ __device__ __forceinline__ float wave_max_pair(float x) {
   return __builtin_elementwise_maximum(
       __builtin_elementwise_maximum(x, __uint_as_float(r[0])), __uint_as_float(r[1]));
 }
+
+// S^T = K Q^T of one 32-key tile for two 32-row blocks at HD = 256, as one
+// asm block so that the scores land in VGPRs (the softmax reads them with
+// VALU instructions).  With every MFMA in AGPR form the compiler would
+// produce the scores in AGPRs and copy them out, and at this register
+// pressure it also copies Q operands around and spills.
+//   ka[j]  LDS byte address of this lane's K row at chunk (2j + h) ^ swizzle;
+//          k-step s reads ka[s % 8] + 256 (s / 8)
+//   q      the Q^T operands of the two row blocks, 16 k-steps each
+// K operands are read two k-steps ahead into a ring of three registers;
+// LDS reads complete in order, so lgkmcnt(2) before step s means the read
+// of step s has landed.  The leading s_nop covers a VALU write of an
+// operand just before the first MFMA reads it; the trailing ones cover the
+// last MFMA's result before VALU instructions read the scores.
+#define RA_KREAD(t, a, off) "ds_read_b128 %[" #t "], %[" #a "] offset:" #off "\n\t"
+#define RA_QK2(t, step, c0, c1)                                              \
+  "v_mfma_f32_32x32x16_bf16 %[s0], %[" #t "], %[q0_" #step "], " c0 "\n\t" \
+  "v_mfma_f32_32x32x16_bf16 %[s1], %[" #t "], %[q1_" #step "], " c1 "\n\t"
+#define RA_QK(t, step) RA_QK2(t, step, "%[s0]", "%[s1]")
+#define RA_WAIT(n) "s_waitcnt lgkmcnt(" #n ")\n\t"
+__device__ __forceinline__ void qk_hd256(f32x16& s0, f32x16& s1, const bf16x8 (&q)[2][16],
+                                         const uint32_t (&ka)[8]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  bf16x8 t0, t1, t2;
+  asm volatile(
+      "s_nop 1\n\t"
+      RA_KREAD(t0, a0, 0) RA_KREAD(t1, a1, 0)
+      RA_KREAD(t2, a2, 0) RA_WAIT(2) RA_QK2(t0, 0, "0", "0")
+      RA_KREAD(t0, a3, 0) RA_WAIT(2) RA_QK(t1, 1)
+      RA_KREAD(t1, a4, 0) RA_WAIT(2) RA_QK(t2, 2)
+      RA_KREAD(t2, a5, 0) RA_WAIT(2) RA_QK(t0, 3)
+      RA_KREAD(t0, a6, 0) RA_WAIT(2) RA_QK(t1, 4)
+      RA_KREAD(t1, a7, 0) RA_WAIT(2) RA_QK(t2, 5)
+      RA_KREAD(t2, a0, 256) RA_WAIT(2) RA_QK(t0, 6)
+      RA_KREAD(t0, a1, 256) RA_WAIT(2) RA_QK(t1, 7)
+      RA_KREAD(t1, a2, 256) RA_WAIT(2) RA_QK(t2, 8)
+      RA_KREAD(t2, a3, 256) RA_WAIT(2) RA_QK(t0, 9)
+      RA_KREAD(t0, a4, 256) RA_WAIT(2) RA_QK(t1, 10)
+      RA_KREAD(t1, a5, 256) RA_WAIT(2) RA_QK(t2, 11)
+      RA_KREAD(t2, a6, 256) RA_WAIT(2) RA_QK(t0, 12)
+      RA_KREAD(t0, a7, 256) RA_WAIT(2) RA_QK(t1, 13)
+      RA_WAIT(1) RA_QK(t2, 14)
+      RA_WAIT(0) RA_QK(t0, 15)
+      "s_nop 7\n\t"
+      "s_nop 7"
+      : [s0] "=&v"(s0), [s1] "=&v"(s1), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2)
+      : [q0_0] "v"(q[0][0]), [q0_1] "v"(q[0][1]), [q0_2] "v"(q[0][2]), [q0_3] "v"(q[0][3]),
+        [q0_4] "v"(q[0][4]), [q0_5] "v"(q[0][5]), [q0_6] "v"(q[0][6]), [q0_7] "v"(q[0][7]),
+        [q0_8] "v"(q[0][8]), [q0_9] "v"(q[0][9]), [q0_10] "v"(q[0][10]), [q0_11] "v"(q[0][11]),
+        [q0_12] "v"(q[0][12]), [q0_13] "v"(q[0][13]), [q0_14] "v"(q[0][14]),
+        [q0_15] "v"(q[0][15]),
+        [q1_0] "v"(q[1][0]), [q1_1] "v"(q[1][1]), [q1_2] "v"(q[1][2]), [q1_3] "v"(q[1][3]),
+        [q1_4] "v"(q[1][4]), [q1_5] "v"(q[1][5]), [q1_6] "v"(q[1][6]), [q1_7] "v"(q[1][7]),
+        [q1_8] "v"(q[1][8]), [q1_9] "v"(q[1][9]), [q1_10] "v"(q[1][10]), [q1_11] "v"(q[1][11]),
+        [q1_12] "v"(q[1][12]), [q1_13] "v"(q[1][13]), [q1_14] "v"(q[1][14]),
+        [q1_15] "v"(q[1][15]),
+        [a0] "v"(ka[0]), [a1] "v"(ka[1]), [a2] "v"(ka[2]), [a3] "v"(ka[3]), [a4] "v"(ka[4]),
+        [a5] "v"(ka[5]), [a6] "v"(ka[6]), [a7] "v"(ka[7])
+      : "memory");
+#endif
+}
+#undef RA_KREAD
+#undef RA_QK2
+#undef RA_QK
+#undef RA_WAIT
 
 struct True { static constexpr bool value = true; };
 struct False { static constexpr bool value = false; };
@@ -338,27 +405,37 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
 
   // S^T = K Q^T for one tile: every K operand read from LDS feeds the MFMAs
   // of all NRB row blocks.  Operands are read two k-steps ahead and the
-  // schedule alternates one LDS read with the MFMAs of one step.
+  // schedule alternates one LDS read with the MFMAs of one step (at
+  // HD = 256 as one asm block, the scores in VGPRs).
   auto qk = [&](const uint16_t* kt, f32x16 (&S)[NRB][NKB]) {
     static_assert(NKB == 1, "one 32-key block per tile");
-    auto kop = [&](int s) { return lds_read_b128(kt, kx[s & 7] + (s >> 3) * 256); };
+    if constexpr (D == 256 && NRB == 2) {
+      const uint32_t k0 = (uint32_t)(uintptr_t)kt;  // LDS offset of the slot
+      uint32_t ka[8];
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) S[rb][0] = f32x16{};
-    bf16x8 ka[3];
-    ka[0] = kop(0);
-    ka[1] = kop(1);
+      for (int j = 0; j < 8; ++j) ka[j] = kx[j] + k0;
+      qk_hd256(S[0][0], S[1][0], qreg, ka);
+    } else {
+      auto kop = [&](int s) { return lds_read_b128(kt, kx[s & 7] + (s >> 3) * 256); };
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      if (s + 2 < NKS) ka[(s + 2) % 3] = kop(s + 2);
+      for (int rb = 0; rb < NRB; ++rb) S[rb][0] = f32x16{};
+      bf16x8 ka[3];
+      ka[0] = kop(0);
+      ka[1] = kop(1);
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
-        S[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s % 3], qreg[rb][s], S[rb][0], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the first two LDS reads
+      for (int s = 0; s < NKS; ++s) {
+        if (s + 2 < NKS) ka[(s + 2) % 3] = kop(s + 2);
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      if (s + 2 < NKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);                 // NRB MFMAs
+        for (int rb = 0; rb < NRB; ++rb)
+          S[rb][0] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s % 3], qreg[rb][s], S[rb][0], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the first two LDS reads
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        if (s + 2 < NKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);                 // NRB MFMAs
+      }
     }
   };
 
