@@ -48,13 +48,22 @@ def alg_bytes(w, with_write):
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "ring_attn_fused_32k_hbm_traffic.md")
-FUSED_SOURCE = os.path.join(ROOT, "context_causal_attention_ring_amd", "csrc", "ring_attn_fused.hip")
+FUSED_SOURCES = [os.path.join(ROOT, "context_causal_attention_ring_amd", "csrc", f)
+                 for f in ("ring_attn_fused.hip", "tile_hd256.inc")]
+
+
+def fused_source_sha():
+    """sha256 over the fused kernel's sources (the kernel and its generated tile block)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in FUSED_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(path=TRAFFIC_SUMMARY):
     """HBM bytes per fused launch from the committed rocprofv3 counter summary,
     or None when it was taken on a different kernel source (or is absent)."""
-    import hashlib
     if not os.path.exists(path):
         return None
     rec = None
@@ -63,8 +72,7 @@ def measured_traffic(path=TRAFFIC_SUMMARY):
             rec = json.loads(line.split(":", 1)[1])
     if rec is None:
         return None
-    sha = hashlib.sha256(open(FUSED_SOURCE, "rb").read()).hexdigest()
-    return rec["bytes_per_launch"] if rec.get("source_sha256") == sha else None
+    return rec["bytes_per_launch"] if rec.get("source_sha256") == fused_source_sha() else None
 
 
 def setup(w, device):

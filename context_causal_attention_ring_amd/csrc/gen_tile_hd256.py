@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Writes tile_hd256.inc: the instruction block of one 32-key tile of the
+fused ring + current attention kernel at HD = 256 (a wave owns two 32-row
+blocks; the accumulator O^T is 2 x 8 tiles of 32 x 32 fp32 in AGPRs).
+
+One block, in order:
+  1. S^T = K Q^T of tile v: 32 MFMAs, K operands read from LDS two k-steps
+     ahead; the first two V operands of step 3 are read at the end.
+  2. Only when the tile is cut by a key bound (a uniform flag): the scores
+     of keys at or past each row's bound become -inf.
+  3. O^T += V^T P^T of tile v-1: 32 MFMAs.  After each MFMA an even share
+     (by issue cost) of tile v's online softmax is issued: the row max (two
+     in-lane max3 chains, one v_permlane32_swap exchange with lane ^ 32),
+     the lazy running-max vote, one FMA + exp2 per score, the row sums, and
+     the bf16 packing of the probabilities into the next P.V operands.
+The block is a single asm statement so that the softmax stays in the MFMAs'
+shadow (as separate C++ it was sunk past the tile's barrier).  The scores
+live in clobbered VGPRs v[212:243] and the operand ring in v[244:255]; both
+are dead outside the block.
+
+Hazards respected inside the block (gfx950): a VALU op never reads the
+result of a transcendental in the next slot; two wait states between a VALU
+write and v_permlane32_swap, and between an SGPR write and its use as a lane
+mask; MFMA results are read by VALU only after a later MFMA and an s_nop.
+
+Usage: python gen_tile_hd256.py            (rewrites the .inc)
+       python gen_tile_hd256.py --check    (exit 1 if the .inc is stale)
+"""
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+OUT = os.path.join(HERE, "tile_hd256.inc")
+
+NKS = 16           # 16-wide k-steps of QK^T (HD / 16)
+NDB = 8            # 32-wide d blocks of the output (HD / 32)
+NPS = 2            # 16-key steps of P.V per 32-key tile
+NT = NPS * NDB     # P.V steps; each issues one MFMA per row block
+NRB = 2            # 32-row blocks per wave
+Q0 = 52            # Q^T operands (pinned): row block rb, k-step k -> v[Q0 + 64 rb + 4 k : +3]
+PB = (180, 196)    # bf16 probabilities (pinned), two buffers: [rb][ks] -> v[PB + 8 rb + 4 ks : +3]
+S0 = 212           # scores (clobbered): row block rb, key slot i -> v[S0 + 16 rb + i]
+RING0 = 244        # operand ring (clobbered): group j -> v[RING0 + 4j : RING0 + 4j + 3]
+
+# Issue cost of one instruction, in units of one full-rate VALU op (measured
+# on gfx950: v_exp_f32 is half rate; SALU and s_nop issue in about a cycle).
+COST = {"valu": 1.0, "trans": 2.0, "salu": 0.5, "nop": 0.5}
+
+
+def grp(j, half=None):
+    b = RING0 + 4 * (j % 3)
+    if half is None:
+        return f"v[{b}:{b + 3}]"
+    return f"v[{b + 2 * half}:{b + 2 * half + 1}]"
+
+
+def s(rb, i):
+    return f"v{S0 + 16 * rb + i}"
+
+
+def qop(rb, k):
+    b = Q0 + 64 * rb + 4 * k
+    return f"v[{b}:{b + 3}]"
+
+
+def pbop(buf, rb, ks):
+    b = PB[buf] + 8 * rb + 4 * ks
+    return f"v[{b}:{b + 3}]"
+
+
+def pbreg(buf, rb, j):
+    """VGPR of pair j (keys 2j, 2j + 1) of row block rb in buffer buf."""
+    return f"v{PB[buf] + 8 * rb + j}"
+
+
+def stile(rb):
+    return f"v[{S0 + 16 * rb}:{S0 + 16 * rb + 15}]"
+
+
+# K step k uses ring group k % 3; V step t uses group (t + 1) % 3, so that
+# the first two V operands can be read while the last K operands are in use.
+def kgroup(k):
+    return k % 3
+
+
+def vgroup(t):
+    return (t + 1) % 3
+
+
+def kread(k):
+    return f"ds_read_b128 {grp(kgroup(k))}, %[ka{k % 8}] offset:%[ko{k // 8}]"
+
+
+def vreads(t):
+    """Two transposing reads (keys 0-7 and 8-15 of the step) of V operand t."""
+    ks, db = divmod(t, NDB)
+    g = vgroup(t)
+    return [f"ds_read_b64_tr_b16 {grp(g, h)}, %[va{db % 4}] offset:%[vo{ks}{db // 4}{h}]"
+            for h in (0, 1)]
+
+
+def qk_part():
+    out = ["s_nop 1", kread(0), kread(1)]
+    for k in range(NKS):
+        if k + 2 < NKS:
+            out.append(kread(k + 2))
+            wait = 2
+        elif k == NKS - 2:
+            out += vreads(0)
+            wait = 3
+        else:
+            out += vreads(1)
+            wait = 4
+        out.append(f"s_waitcnt lgkmcnt({wait})")
+        for rb in range(NRB):
+            c = "0" if k == 0 else stile(rb)
+            out.append(f"v_mfma_f32_32x32x16_bf16 {stile(rb)}, {grp(kgroup(k))}, "
+                       f"{qop(rb, k)}, {c}")
+    return out
+
+
+def mask_part():
+    """Keys at or past the row's bound -> -inf, only when the flag is set.
+    Lane half h holds keys 8 (i / 4) + 4 h + i % 4 of the tile; lim = bound
+    - 4 h, so key slot i is kept iff 8 (i / 4) + i % 4 < lim."""
+    out = ["s_cmp_eq_u32 %[mflag], 0", "s_cbranch_scc1 1f", "s_nop 7", "s_nop 7"]
+    for rb in range(NRB):
+        for i in range(16):
+            c = 8 * (i // 4) + i % 4
+            out.append(f"v_sub_u32 %[a0], {c}, %[lim{rb}]")   # < 0 iff kept
+            out.append("v_ashrrev_i32 %[a0], 31, %[a0]")      # all ones iff kept
+            out.append(f"v_bfi_b32 {s(rb, i)}, %[a0], {s(rb, i)}, %[ninf]")
+    out.append("1:")
+    return out
+
+
+def softmax_ops(pout):
+    """The online softmax of tile v as (kind, text) in dependency order."""
+    ops = [("nop", "s_nop 4")]  # the last score MFMAs' results (after one more MFMA)
+    for rb in range(NRB):  # threshold for the lazy rescale: mlog + tau
+        ops.append(("valu", f"v_add_f32 %[th{rb}], %[tau], %[ml{rb}]"))
+    # In-lane max of the 16 scores of each row: two max3 chains per row block.
+    chains = [((0, 1, 2), (3, 4, 5)), ((6, 7), (8, 9)), ((10, 11), (12, 13)), ((14, 15), None)]
+    for ca, cb in chains:
+        for rb in range(NRB):
+            for name, c in (("a", ca), ("b", cb)):
+                if c is None:
+                    continue
+                src = [s(rb, i) for i in c]
+                if len(c) == 2:
+                    src = [f"%[{name}{rb}]"] + src
+                ops.append(("valu", f"v_max3_f32 %[{name}{rb}], {', '.join(src)}"))
+    # The two halves of a row live in lanes l and l ^ 32: the in-lane max
+    # goes into both swap operands, the halves are exchanged, max taken.
+    for rb in range(NRB):
+        ops.append(("valu", f"v_max_f32 %[b{rb}], %[a{rb}], %[b{rb}]"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_mov_b32 %[a{rb}], %[b{rb}]"))
+    ops.append(("nop", "s_nop 1"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_permlane32_swap_b32 %[a{rb}], %[b{rb}]"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_max_f32 %[a{rb}], %[a{rb}], %[b{rb}]"))
+    for rb in range(NRB):  # to log2 units; the scale is positive, so max commutes
+        ops.append(("valu", f"v_mul_f32 %[a{rb}], %[c2], %[a{rb}]"))
+    # Lazy running max: rows whose max grew by more than tau vote; if any row
+    # of the block voted, every row of it takes the exact new max.
+    for rb in range(NRB):
+        ops.append(("valu", f"v_cmp_gt_f32_e64 %[c{rb}], %[a{rb}], %[th{rb}]"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_max_f32 %[b{rb}], %[ml{rb}], %[a{rb}]"))
+    ops.append(("salu", "s_or_b64 %[any], %[c0], %[c1]"))
+    for rb in range(NRB):
+        ops.append(("salu", f"s_cmp_lg_u64 %[c{rb}], 0"))
+        ops.append(("salu", f"s_cselect_b64 %[c{rb}], -1, 0"))
+    ops.append(("nop", "s_nop 1"))
+    for rb in range(NRB):  # m_new
+        ops.append(("valu", f"v_cndmask_b32_e64 %[b{rb}], %[ml{rb}], %[b{rb}], %[c{rb}]"))
+    # m_use = max(m_new, -FLT_MAX): a row that has seen only masked keys
+    # subtracts a finite value, so its probabilities are exp2(-inf) = 0.
+    for rb in range(NRB):
+        ops.append(("valu", f"v_max_f32 %[a{rb}], 0xff7fffff, %[b{rb}]"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_sub_f32 %[al{rb}], %[ml{rb}], %[a{rb}]"))
+    for rb in range(NRB):
+        ops.append(("trans", f"v_exp_f32 %[al{rb}], %[al{rb}]"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_mov_b32 %[ml{rb}], %[b{rb}]"))
+    # One FMA + exp2 per score; each probability is added to the tile's row
+    # sum r after the next FMA (a transcendental's result is not read in the
+    # next slot), and each pair of keys is packed to bf16 once both are
+    # summed.  The tile sum is formed first and then l = l * alpha + r: added
+    # one by one to the running sum, the many tiny probabilities of a peaky
+    # row would be rounded away against it.
+    streams = []
+    for rb in range(NRB):
+        st = []
+        for i in range(16):
+            st.append(("valu", f"v_fma_f32 {s(rb, i)}, {s(rb, i)}, %[c2], -%[a{rb}]"))
+            if i == 2:
+                st.append(("valu", f"v_add_f32 %[r{rb}], {s(rb, 0)}, {s(rb, 1)}"))
+            elif i > 2:
+                st.append(("valu", f"v_add_f32 %[r{rb}], %[r{rb}], {s(rb, i - 1)}"))
+            if i >= 2 and i % 2 == 0:
+                j = i // 2 - 1
+                st.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, j)}, {s(rb, 2 * j)}, "
+                                   f"{s(rb, 2 * j + 1)}"))
+            st.append(("trans", f"v_exp_f32 {s(rb, i)}, {s(rb, i)}"))
+        streams.append(st)
+    for k in range(max(len(x) for x in streams)):
+        for st in streams:
+            if k < len(st):
+                ops.append(st[k])
+    for rb in range(NRB):
+        ops.append(("valu", f"v_add_f32 %[r{rb}], %[r{rb}], {s(rb, 15)}"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_fma_f32 %[l{rb}], %[l{rb}], %[al{rb}], %[r{rb}]"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, 7)}, {s(rb, 14)}, {s(rb, 15)}"))
+    return ops
+
+
+def assign(ops, ngaps):
+    """Split the ops into ngaps consecutive groups of even cumulative cost."""
+    total = sum(COST[k] for k, _ in ops)
+    per = total / ngaps
+    gaps = [[] for _ in range(ngaps)]
+    acc, g = 0.0, 0
+    for kind, text in ops:
+        while g < ngaps - 1 and acc + COST[kind] / 2 > per * (g + 1):
+            g += 1
+        gaps[g].append(text)
+        acc += COST[kind]
+    return gaps, per
+
+
+def pv_part(pin):
+    gaps, per = assign(softmax_ops(1 - pin), NRB * NT)
+    out = []
+    for t in range(NT):
+        ks, db = divmod(t, NDB)
+        out.append(f"s_waitcnt lgkmcnt({2 if t + 1 < NT else 0})")
+        for rb in range(NRB):
+            out.append(f"v_mfma_f32_32x32x16_bf16 %[acc{rb}{db}], {grp(vgroup(t))}, "
+                       f"{pbop(pin, rb, ks)}, %[acc{rb}{db}]")
+            if rb == NRB - 1 and t + 2 < NT:
+                out += vreads(t + 2)
+            out += gaps[NRB * t + rb]
+    return out, per
+
+
+def macro(name, lines, sep="\\n\\t"):
+    out = [f"#define {name} \\"]
+    for ln in lines:
+        out.append(f'  "{ln}{sep}" \\')
+    out.append('  ""')
+    return out
+
+
+def operand_list(name, items):
+    out = [f"#define {name} \\"]
+    for i, it in enumerate(items):
+        out.append(f"  {it}{',' if i + 1 < len(items) else ''} \\")
+    out.append("")
+    return out
+
+
+def render():
+    out = ["// Generated by gen_tile_hd256.py -- edit the generator, not this file.",
+           "// One 32-key tile at HD = 256: S^T = K Q^T, the optional key-bound mask,",
+           "// and O^T += V^T P^T of the previous tile with this tile's online softmax",
+           "// in its shadow.  Variant P<b> reads the bf16 probabilities from buffer b",
+           "// and writes the new ones to buffer 1 - b.  Operands are bound by the asm",
+           "// statement in ring_attn_fused.hip."]
+    per = None
+    for pin in (0, 1):
+        pv, per = pv_part(pin)
+        out.append(f"// P.V block of variant P{pin}: about {per:.1f} full-rate VALU issue slots"
+                   " of softmax work per MFMA.")
+        out += macro(f"RA_TILE_HD256_ASM_P{pin}", qk_part() + mask_part() + pv)
+    q = [f'[q{rb}_{k}] "{{{qop(rb, k)}}}"(q[{rb}][{k}])' for rb in range(NRB) for k in range(NKS)]
+    out += operand_list("RA_TILE_HD256_Q_OPERANDS", q)
+    for buf in (0, 1):
+        ins = [f'"{{{pbop(buf, rb, ks)}}}"(pin[{rb}][{ks}])' for rb in range(NRB)
+               for ks in range(NPS)]
+        outs = [f'"=&{{{pbop(buf, rb, ks)}}}"(pout[{rb}][{ks}])' for rb in range(NRB)
+                for ks in range(NPS)]
+        out += operand_list(f"RA_TILE_HD256_PB_IN{buf}", ins)
+        out += operand_list(f"RA_TILE_HD256_PB_OUT{buf}", outs)
+    clob = [f'"v{r}"' for r in range(S0, RING0 + 12)]
+    out += operand_list("RA_TILE_HD256_CLOBBERS", clob)
+    return "\n".join(out) + "\n"
+
+
+def main():
+    text = render()
+    if "--check" in sys.argv:
+        cur = open(OUT).read() if os.path.exists(OUT) else ""
+        if cur != text:
+            print(f"{OUT} is stale: run {os.path.basename(__file__)}", file=sys.stderr)
+            return 1
+        return 0
+    with open(OUT, "w") as f:
+        f.write(text)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

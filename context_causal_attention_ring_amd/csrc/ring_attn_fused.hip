@@ -51,6 +51,9 @@
 namespace ra {
 namespace {
 
+// Lambdas of the kernel are inlined: their captures must stay in registers.
+#define RA_INLINE __attribute__((always_inline))
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -59,6 +62,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -104,12 +108,17 @@ __device__ __forceinline__ void dma16(const i32x4& rs, uint16_t* dst, uint32_t v
 #if defined(__HIP_DEVICE_COMPILE__)
   // the low 32 bits of a generic LDS address are the LDS offset
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  // the descriptor and the scalar offset are wave-uniform by construction;
+  // readfirstlane keeps them in SGPRs where the analysis cannot prove it
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  const i32x4 r = {__builtin_amdgcn_readfirstlane(rs[0]), __builtin_amdgcn_readfirstlane(rs[1]),
+                   __builtin_amdgcn_readfirstlane(rs[2]), __builtin_amdgcn_readfirstlane(rs[3])};
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
       "buffer_load_dwordx4 %1, %2, %3 offen lds"
       :
-      : "s"(m0), "v"(voff), "s"(rs), "s"(soff)
+      : "s"(m0), "v"(voff), "s"(r), "s"(so)
       : "memory", "m0");
 #endif
 }
@@ -153,73 +162,69 @@ __device__ __forceinline__ float wave_max_pair(float x) {
       __builtin_elementwise_maximum(x, __uint_as_float(r[0])), __uint_as_float(r[1]));
 }
 
-// S^T = K Q^T of one 32-key tile for two 32-row blocks at HD = 256, as one
-// asm block so that the scores land in VGPRs (the softmax reads them with
-// VALU instructions).  With every MFMA in AGPR form the compiler would
-// produce the scores in AGPRs and copy them out, and at this register
-// pressure it also copies Q operands around and spills.
-//   ka[j]  LDS byte address of this lane's K row at chunk (2j + h) ^ swizzle;
-//          k-step s reads ka[s % 8] + 256 (s / 8)
-//   q      the Q^T operands of the two row blocks, 16 k-steps each
-// K operands are read two k-steps ahead into a ring of three registers;
-// LDS reads complete in order, so lgkmcnt(2) before step s means the read
-// of step s has landed.  The leading s_nop covers a VALU write of an
-// operand just before the first MFMA reads it; the trailing ones cover the
-// last MFMA's result before VALU instructions read the scores.
-#define RA_KREAD(t, a, off) "ds_read_b128 %[" #t "], %[" #a "] offset:" #off "\n\t"
-#define RA_QK2(t, step, c0, c1)                                              \
-  "v_mfma_f32_32x32x16_bf16 %[s0], %[" #t "], %[q0_" #step "], " c0 "\n\t" \
-  "v_mfma_f32_32x32x16_bf16 %[s1], %[" #t "], %[q1_" #step "], " c1 "\n\t"
-#define RA_QK(t, step) RA_QK2(t, step, "%[s0]", "%[s1]")
-#define RA_WAIT(n) "s_waitcnt lgkmcnt(" #n ")\n\t"
-__device__ __forceinline__ void qk_hd256(f32x16& s0, f32x16& s1, const bf16x8 (&q)[2][16],
-                                         const uint32_t (&ka)[8]) {
+// One 32-key tile at HD = 256 as a single instruction block (generated:
+// tile_hd256.inc; this binds its operands).  In order: S^T = K Q^T of tile
+// v from the K slot at KOFF; if mflag, scores of keys at or past each row's
+// bound (lim = bound - 4 h) become -inf; then O^T += V^T P^T of tile v-1
+// (V slot at VOFF, bf16 probabilities pin) with tile v's online softmax in
+// the MFMAs' shadow.  On return pout holds tile v's bf16 probabilities, ml
+// and l the updated running max (log2 units) and row sums, al the factor the
+// accumulator must be scaled by, and `any` is non-zero when some row of the
+// wave asked for that rescale (al == 1 for every row otherwise).
+//   ka[j]  LDS address of this lane's K row at chunk (2j + h) ^ swizzle;
+//          k-step s reads ka[s % 8] + KOFF + 256 (s / 8)
+//   va[d]  LDS address of this lane's transposed V read for d blocks d and
+//          d + 4; step (ks, db) reads va[db % 4] + VOFF + 8192 ks + 256
+//          (db / 4), and + 4096 for keys 8..15
+// Q and the two probability buffers are pinned to v[52:211] (buffer PIN is
+// read, 1 - PIN written); scores live in v[212:243] and the operand ring in
+// v[244:255] (clobbered).
+#include "tile_hd256.inc"
+#define RA_TILE_STATE_OPERANDS                                                                  \
+  [acc00] "+a"(acc[0][0]), [acc01] "+a"(acc[0][1]), [acc02] "+a"(acc[0][2]),                   \
+      [acc03] "+a"(acc[0][3]), [acc04] "+a"(acc[0][4]), [acc05] "+a"(acc[0][5]),               \
+      [acc06] "+a"(acc[0][6]), [acc07] "+a"(acc[0][7]), [acc10] "+a"(acc[1][0]),               \
+      [acc11] "+a"(acc[1][1]), [acc12] "+a"(acc[1][2]), [acc13] "+a"(acc[1][3]),               \
+      [acc14] "+a"(acc[1][4]), [acc15] "+a"(acc[1][5]), [acc16] "+a"(acc[1][6]),               \
+      [acc17] "+a"(acc[1][7]), [ml0] "+v"(ml[0]), [ml1] "+v"(ml[1]), [l0] "+v"(l[0]),          \
+      [l1] "+v"(l[1]), [al0] "=&v"(al[0]), [al1] "=&v"(al[1]), [any] "=&s"(any),              \
+      [a0] "=&v"(a0), [b0] "=&v"(b0), [a1] "=&v"(a1), [b1] "=&v"(b1), [th0] "=&v"(th0),       \
+      [th1] "=&v"(th1), [r0] "=&v"(r0), [r1] "=&v"(r1), [c0] "=&s"(c0), [c1] "=&s"(c1)
+#define RA_TILE_INPUT_OPERANDS                                                                  \
+  [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [ka2] "v"(ka[2]), [ka3] "v"(ka[3]), [ka4] "v"(ka[4]),    \
+      [ka5] "v"(ka[5]), [ka6] "v"(ka[6]), [ka7] "v"(ka[7]), [va0] "v"(va[0]), [va1] "v"(va[1]), \
+      [va2] "v"(va[2]), [va3] "v"(va[3]), [c2] "s"(c2), [tau] "s"(tau), [mflag] "s"(mflag),     \
+      [lim0] "v"(lim[0]), [lim1] "v"(lim[1]), [ninf] "v"(ninf), [ko0] "i"(KOFF),                \
+      [ko1] "i"(KOFF + 256), [vo000] "i"(VOFF), [vo001] "i"(VOFF + 4096),                       \
+      [vo010] "i"(VOFF + 256), [vo011] "i"(VOFF + 256 + 4096), [vo100] "i"(VOFF + 8192),        \
+      [vo101] "i"(VOFF + 8192 + 4096), [vo110] "i"(VOFF + 8192 + 256),                          \
+      [vo111] "i"(VOFF + 8192 + 256 + 4096)
+template <uint32_t KOFF, uint32_t VOFF, int PIN>
+__device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], const bf16x8 (&pin)[2][2],
+                                           bf16x8 (&pout)[2][2], const bf16x8 (&q)[2][16],
+                                           const uint32_t (&ka)[8], const uint32_t (&va)[4],
+                                           float (&ml)[2], float (&l)[2], float (&al)[2],
+                                           uint64_t& any, float c2, float tau, uint32_t mflag,
+                                           const int (&lim)[2]) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  bf16x8 t0, t1, t2;
-  asm volatile(
-      "s_nop 1\n\t"
-      RA_KREAD(t0, a0, 0) RA_KREAD(t1, a1, 0)
-      RA_KREAD(t2, a2, 0) RA_WAIT(2) RA_QK2(t0, 0, "0", "0")
-      RA_KREAD(t0, a3, 0) RA_WAIT(2) RA_QK(t1, 1)
-      RA_KREAD(t1, a4, 0) RA_WAIT(2) RA_QK(t2, 2)
-      RA_KREAD(t2, a5, 0) RA_WAIT(2) RA_QK(t0, 3)
-      RA_KREAD(t0, a6, 0) RA_WAIT(2) RA_QK(t1, 4)
-      RA_KREAD(t1, a7, 0) RA_WAIT(2) RA_QK(t2, 5)
-      RA_KREAD(t2, a0, 256) RA_WAIT(2) RA_QK(t0, 6)
-      RA_KREAD(t0, a1, 256) RA_WAIT(2) RA_QK(t1, 7)
-      RA_KREAD(t1, a2, 256) RA_WAIT(2) RA_QK(t2, 8)
-      RA_KREAD(t2, a3, 256) RA_WAIT(2) RA_QK(t0, 9)
-      RA_KREAD(t0, a4, 256) RA_WAIT(2) RA_QK(t1, 10)
-      RA_KREAD(t1, a5, 256) RA_WAIT(2) RA_QK(t2, 11)
-      RA_KREAD(t2, a6, 256) RA_WAIT(2) RA_QK(t0, 12)
-      RA_KREAD(t0, a7, 256) RA_WAIT(2) RA_QK(t1, 13)
-      RA_WAIT(1) RA_QK(t2, 14)
-      RA_WAIT(0) RA_QK(t0, 15)
-      "s_nop 7\n\t"
-      "s_nop 7"
-      : [s0] "=&v"(s0), [s1] "=&v"(s1), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2)
-      : [q0_0] "v"(q[0][0]), [q0_1] "v"(q[0][1]), [q0_2] "v"(q[0][2]), [q0_3] "v"(q[0][3]),
-        [q0_4] "v"(q[0][4]), [q0_5] "v"(q[0][5]), [q0_6] "v"(q[0][6]), [q0_7] "v"(q[0][7]),
-        [q0_8] "v"(q[0][8]), [q0_9] "v"(q[0][9]), [q0_10] "v"(q[0][10]), [q0_11] "v"(q[0][11]),
-        [q0_12] "v"(q[0][12]), [q0_13] "v"(q[0][13]), [q0_14] "v"(q[0][14]),
-        [q0_15] "v"(q[0][15]),
-        [q1_0] "v"(q[1][0]), [q1_1] "v"(q[1][1]), [q1_2] "v"(q[1][2]), [q1_3] "v"(q[1][3]),
-        [q1_4] "v"(q[1][4]), [q1_5] "v"(q[1][5]), [q1_6] "v"(q[1][6]), [q1_7] "v"(q[1][7]),
-        [q1_8] "v"(q[1][8]), [q1_9] "v"(q[1][9]), [q1_10] "v"(q[1][10]), [q1_11] "v"(q[1][11]),
-        [q1_12] "v"(q[1][12]), [q1_13] "v"(q[1][13]), [q1_14] "v"(q[1][14]),
-        [q1_15] "v"(q[1][15]),
-        [a0] "v"(ka[0]), [a1] "v"(ka[1]), [a2] "v"(ka[2]), [a3] "v"(ka[3]), [a4] "v"(ka[4]),
-        [a5] "v"(ka[5]), [a6] "v"(ka[6]), [a7] "v"(ka[7])
-      : "memory");
+  float a0, b0, a1, b1, th0, th1, r0, r1;
+  uint64_t c0, c1;
+  const float ninf = kNegInf;
+  if constexpr (PIN == 0) {
+    asm volatile(RA_TILE_HD256_ASM_P0
+                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_PB_OUT1
+                 : RA_TILE_HD256_Q_OPERANDS, RA_TILE_HD256_PB_IN0, RA_TILE_INPUT_OPERANDS
+                 : RA_TILE_HD256_CLOBBERS, "memory", "scc");
+  } else {
+    asm volatile(RA_TILE_HD256_ASM_P1
+                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_PB_OUT0
+                 : RA_TILE_HD256_Q_OPERANDS, RA_TILE_HD256_PB_IN1, RA_TILE_INPUT_OPERANDS
+                 : RA_TILE_HD256_CLOBBERS, "memory", "scc");
+  }
 #endif
 }
-#undef RA_KREAD
-#undef RA_QK2
-#undef RA_QK
-#undef RA_WAIT
-
-struct True { static constexpr bool value = true; };
-struct False { static constexpr bool value = false; };
+#undef RA_TILE_STATE_OPERANDS
+#undef RA_TILE_INPUT_OPERANDS
 
 template <int D, bool F32OUT>
 __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedParams p) {
@@ -231,13 +236,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   constexpr int NKB = kBKV / 32;          // 32-key blocks per tile
   constexpr int NPS = kBKV / 16;          // 16-key steps of P.V per tile
   constexpr int TILE = kBKV * D;          // elements of one K or V tile
+  constexpr uint32_t TILE_B = TILE * 2;   // bytes of one K or V tile
   constexpr int DPW = kBKV * CPR / (64 * kWaves);  // DMA instructions per wave per tile
   static_assert(DPW >= 1 && DPW * 64 * kWaves == kBKV * CPR, "tile must split over the waves");
-  // LDS: two K slots then two V slots.
+  constexpr bool ASM256 = D == 256 && NRB == 2 && NKB == 1;  // hand-scheduled tile body
+  // LDS: K slots 0, 1 then V slots 0, 1.  Slot offsets are compile-time
+  // constants because the tile loop is unrolled over the two slots.
   constexpr int NSLOT = 2;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * NSLOT * TILE];
-  uint16_t* const kslot0 = lds;
-  uint16_t* const vslot0 = lds + NSLOT * TILE;
+  auto kslot = [&](int s) RA_INLINE { return lds + s * TILE; };
+  auto vslot = [&](int s) RA_INLINE { return lds + (NSLOT + s) * TILE; };
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;  // LDS byte address of the slots
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -289,6 +298,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   const int n_cur = wg_last / kBKV + 1;
   const int T = n_ring + n_cur;
   const uint32_t rowstride = (uint32_t)p.nkv * D * 2;  // bytes between tokens
+  const uint32_t tile_stride = kBKV * rowstride;       // bytes between tiles
   const uint32_t cur_bytes = (uint32_t)p.real_rows * rowstride;
   const int full_i = (int)p.full * p.interleave;  // < 2^31: bounded by a shard's length
 
@@ -301,37 +311,43 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     int key0;         // current: chunk position of the tile's first key
     bool in_ring;
   };
-  auto source = [&](int v) {
+  // The walk, one tile per call: shard visit k (ring order), tile b within
+  // it, then the current tiles c; past the end, zero-size fetches (the
+  // slot fills with zeros).  Everything here is wave-uniform.
+  int wk = p.nb > 0 ? 0 : p.P, wb = 0, wc = 0;
+  i32x4 vis_k, vis_v;
+  int vis_len = 0;
+  auto next_src = [&]() RA_INLINE {
     Src s;
-    s.in_ring = v < n_ring;
-    if (v >= T) {  // past the walk: a zero-size fetch (fills the slot with zeros)
-      s.kr = s.vr = make_desc(p.k_cur, 0);
-      s.off = 0;
-      s.lim_ring = 0;
+    if (wk < p.P) {
+      if (wb == 0) {  // a new shard visit: its descriptors and length
+        int sh = p.ring_start - wk;
+        sh += (sh < 0) ? p.P : 0;
+        vis_len = full_i + min(max((int)p.rem - sh * p.interleave, 0), p.interleave);
+        const int64_t base = ((int64_t)sh * p.shard_cap * p.nkv + g) * D;
+        const uint32_t bytes = (uint32_t)vis_len * rowstride;
+        vis_k = make_desc(p.k_cache + base, bytes);
+        vis_v = make_desc(p.v_cache + base, bytes);
+      }
+      s.kr = vis_k;
+      s.vr = vis_v;
+      s.off = (uint32_t)wb * tile_stride;
+      s.lim_ring = vis_len - wb * kBKV;
       s.key0 = 0;
-      s.in_ring = false;
-      return s;
-    }
-    if (s.in_ring) {
-      const int k = v / p.nb;
-      const int b = v - k * p.nb;
-      int sh = p.ring_start - k;
-      sh += (sh < 0) ? p.P : 0;
-      const int len = full_i + min(max((int)p.rem - sh * p.interleave, 0), p.interleave);
-      const int64_t base = ((int64_t)sh * p.shard_cap * p.nkv + g) * D;
-      const uint32_t bytes = (uint32_t)len * rowstride;
-      s.kr = make_desc(p.k_cache + base, bytes);
-      s.vr = make_desc(p.v_cache + base, bytes);
-      s.off = (uint32_t)b * kBKV * rowstride;
-      s.lim_ring = len - b * kBKV;
-      s.key0 = 0;
+      s.in_ring = true;
+      if (++wb == p.nb) {
+        wb = 0;
+        ++wk;
+      }
     } else {
-      const int c = v - n_ring;
-      s.kr = make_desc(p.k_cur + g * D, cur_bytes);
-      s.vr = make_desc(p.v_cur + g * D, cur_bytes);
-      s.off = (uint32_t)c * kBKV * rowstride;
+      const bool live = wc < n_cur;
+      s.kr = make_desc(p.k_cur + g * D, live ? cur_bytes : 0u);
+      s.vr = make_desc(p.v_cur + g * D, live ? cur_bytes : 0u);
+      s.off = live ? (uint32_t)wc * tile_stride : 0u;
       s.lim_ring = 0;
-      s.key0 = c * kBKV;
+      s.key0 = wc * kBKV;
+      s.in_ring = false;
+      wc += live ? 1 : 0;
     }
     return s;
   };
@@ -350,7 +366,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       (uint32_t)dma_r * rowstride + (uint32_t)((dma_pc ^ swz_k(dma_r, CPR)) << 4);
   const uint32_t dma_vbase =
       (uint32_t)dma_r * rowstride + (uint32_t)((dma_pc ^ swz_v(dma_r, CPR)) << 4);
-  auto issue_k = [&](const Src& s, uint16_t* dst) {
+  auto issue_k = [&](const Src& s, uint16_t* dst) RA_INLINE {
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int R = (wave * DPW + i) * RPI;
@@ -358,7 +374,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
             s.off + (uint32_t)R * rowstride);
     }
   };
-  auto issue_v = [&](const Src& s, uint16_t* dst) {
+  auto issue_v = [&](const Src& s, uint16_t* dst) RA_INLINE {
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int R = (wave * DPW + i) * RPI;
@@ -388,12 +404,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     const int c0 = 2 * (b4 & 1) + ((i16 & 3) >> 1);  // chunk within the 32-col block
     vbase = (uint32_t)(r * D * 2 + ((c0 ^ swz_v(r, CPR)) << 4) + 8 * (i16 & 1));
   }
+  // Absolute LDS addresses for the hand-scheduled body: K reads ka[j] + slot,
+  // V reads va[db % 4] + slot (d blocks 4..7 add 256: bit 8 of vbase is 0).
+  uint32_t ka[8], va[4];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ka[j] = lds0 + kx[j % NKX];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) va[d] = lds0 + (vbase ^ (uint32_t)(d << 6));
 
   f32x16 acc[NRB][NDB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[rb][db] = f32x16{};
+  bf16x8 pb[NRB][NPS];  // bf16 probabilities of the previous tile (B operands of P.V)
+  bf16x8 pbuf[2][NRB][NPS];  // the same, double-buffered by tile parity (HD = 256 body)
   float mlog[NRB], lsum[NRB], lsum_q[NRB];  // running max (log2 units), row sums
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
@@ -405,42 +430,31 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
 
   // S^T = K Q^T for one tile: every K operand read from LDS feeds the MFMAs
   // of all NRB row blocks.  Operands are read two k-steps ahead and the
-  // schedule alternates one LDS read with the MFMAs of one step (at
-  // HD = 256 as one asm block, the scores in VGPRs).
-  auto qk = [&](const uint16_t* kt, f32x16 (&S)[NRB][NKB]) {
-    static_assert(NKB == 1, "one 32-key block per tile");
-    if constexpr (D == 256 && NRB == 2) {
-      const uint32_t k0 = (uint32_t)(uintptr_t)kt;  // LDS offset of the slot
-      uint32_t ka[8];
+  // schedule alternates one LDS read with the MFMAs of one step.
+  auto qk = [&](const uint16_t* kt, f32x16 (&S)[NRB][NKB]) RA_INLINE {
+    auto kop = [&](int s) RA_INLINE { return lds_read_b128(kt, kx[s & 7] + (s >> 3) * 256); };
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ka[j] = kx[j] + k0;
-      qk_hd256(S[0][0], S[1][0], qreg, ka);
-    } else {
-      auto kop = [&](int s) { return lds_read_b128(kt, kx[s & 7] + (s >> 3) * 256); };
+    for (int rb = 0; rb < NRB; ++rb) S[rb][0] = f32x16{};
+    bf16x8 kq[3];
+    kq[0] = kop(0);
+    kq[1] = kop(1);
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) S[rb][0] = f32x16{};
-      bf16x8 ka[3];
-      ka[0] = kop(0);
-      ka[1] = kop(1);
+    for (int s = 0; s < NKS; ++s) {
+      if (s + 2 < NKS) kq[(s + 2) % 3] = kop(s + 2);
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        if (s + 2 < NKS) ka[(s + 2) % 3] = kop(s + 2);
+      for (int rb = 0; rb < NRB; ++rb)
+        S[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[s % 3], qreg[rb][s], S[rb][0], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the first two LDS reads
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-          S[rb][0] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s % 3], qreg[rb][s], S[rb][0], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the first two LDS reads
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        if (s + 2 < NKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);                 // NRB MFMAs
-      }
+    for (int s = 0; s < NKS; ++s) {
+      if (s + 2 < NKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);                 // NRB MFMAs
     }
   };
 
   // O^T += V^T P^T for one tile: every V operand feeds all row blocks.
-  auto pv = [&](const uint16_t* vt, const bf16x8 (&pb)[NRB][NPS]) {
+  auto pv = [&](const uint16_t* vt, const bf16x8 (&pb)[NRB][NPS]) RA_INLINE {
 #pragma unroll
     for (int ks = 0; ks < NPS; ++ks) {
 #pragma unroll
@@ -459,16 +473,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   };
 
   // Region by value: keys with index >= lim[rb] in the tile are masked.
-  auto mask = [&](f32x16 (&S)[NRB][NKB], const int (&lim)[NRB]) {
+  // Lane half h holds keys (i / 4) * 8 + 4 h + i % 4 of each 32-key block,
+  // so the compare is against the constant (i / 4) * 8 + i % 4.
+  auto mask = [&](f32x16 (&S)[NRB][NKB], const int (&lim)[NRB]) RA_INLINE {
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int l = lim[rb] - 4 * h;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb * 32 + (i >> 2) * 8 + 4 * h + (i & 3);
-          S[rb][kb][i] = key < lim[rb] ? S[rb][kb][i] : kNegInf;
-        }
+        for (int i = 0; i < 16; ++i)
+          S[rb][kb][i] = kb * 32 + (i >> 2) * 8 + (i & 3) < l ? S[rb][kb][i] : kNegInf;
+    }
   };
 
   // Online softmax of one tile, in place: S becomes the probabilities
@@ -477,7 +493,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // the return value reports whether any did).  lsum is the exact fp32 row
   // sum (for the LSE and, with bf16 output, the normalisation); for fp32
   // output the normalisation uses lsum_q instead (see pack).
-  auto softmax = [&](f32x16 (&S)[NRB][NKB], float (&alpha)[NRB]) {
+  auto softmax = [&](f32x16 (&S)[NRB][NKB], float (&alpha)[NRB]) RA_INLINE {
     bool any = false;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
@@ -511,7 +527,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // Probabilities -> bf16 B operands of P.V.  For fp32 output also the sum
   // of the bf16-rounded probabilities (v_dot2 against (1, 1)): numerator
   // and denominator then weight every key identically.
-  auto pack = [&](const f32x16 (&S)[NRB][NKB], bf16x8 (&pb)[NRB][NPS], const float (&alpha)[NRB]) {
+  auto pack = [&](const f32x16 (&S)[NRB][NKB], bf16x8 (&pb)[NRB][NPS], const float (&alpha)[NRB]) RA_INLINE {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
@@ -531,7 +547,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
 
   // Region by value: each row's key bound within the tile, and whether any
   // bound of the workgroup cuts into the tile (then the compare is needed).
-  auto bounds = [&](const Src& src, int (&lim)[NRB]) {
+  auto bounds = [&](const Src& src, int (&lim)[NRB]) RA_INLINE {
     if (src.in_ring) {
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) lim[rb] = src.lim_ring;
@@ -542,67 +558,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     return src.key0 + kBKV > wg_first + 1;
   };
 
-  // Iteration v reads K(v) and V(v-1) and fetches K(v+1) and V(v) into the
-  // slots that K(v-1) and V(v-2) left.  The scores of tile v are computed,
-  // then its softmax is issued between the P.V MFMAs of tile v-1, which do
-  // not depend on it, then tile v's bf16 packing; the rare rescale for tile
-  // v's max is applied at the top of the next iteration, between P.V(v-1)
-  // and P.V(v).  The accumulator is touched by no branch but the rescale.
-  Src s0 = source(0), s1 = source(1);  // tiles v, v+1
-  issue_k(s0, kslot0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
-  __syncthreads();
-
-  bf16x8 pb[NRB][NPS];
-  bool any = false;       // the previous tile asked for a rescale ...
-  float alpha[NRB];       // ... by these factors
-  auto rescale = [&]() {
-    if (any) {
-#if defined(__HIP_DEVICE_COMPILE__)
-      // the last P.V MFMAs may still be writing acc: wait them out
-      asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
-#endif
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) scale_agprs(acc[rb][db], alpha[rb]);
-    }
-  };
-  int sl = 0;  // LDS slot of tile v
-  // Issue the copies of K(v+1) and V(v), compute tile v's scores, mask them.
-  auto front = [&](f32x16 (&S)[NRB][NKB]) {
-    issue_k(s1, kslot0 + (sl ^ 1) * TILE);
-    issue_v(s0, vslot0 + sl * TILE);
-    qk(kslot0 + sl * TILE, S);
-    int lim[NRB];
-    if (bounds(s0, lim)) mask(S, lim);
-  };
-  auto advance = [&](int v) {
-    s0 = s1;
-    s1 = source(v + 2);
-    sl ^= 1;
-  };
-  {  // tile 0: no P.V yet
-    f32x16 S[NRB][NKB];
-    front(S);
-    any = softmax(S, alpha);
-    pack(S, pb, alpha);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(1), V(0) have landed
-    __syncthreads();
-    advance(0);
-  }
-  // P.V of the previous tile with the softmax of the current one, hand
-  // ordered: slot t issues the MFMAs of P.V step t (one V operand, read two
-  // slots ahead, for every row block) and then a fixed slice of softmax
-  // work; sched_barrier keeps slices in their slots so the VALU and
-  // transcendental work runs under the MFMAs.  Softmax work units, in
-  // dependency order: the in-lane max of each row block, the cross-lane
-  // reduction and new running max, one exp2 per score, the row sums.
-  auto pv_softmax = [&](const uint16_t* vt, f32x16 (&S)[NRB][NKB], float (&al)[NRB]) {
+  // P.V of the previous tile with the softmax of the current one (generic
+  // head dims), hand ordered: slot t issues the MFMAs of P.V step t (one V
+  // operand, read two slots ahead, for every row block) and then a fixed
+  // slice of softmax work.  Softmax work units, in dependency order: the
+  // in-lane max of each row block, the cross-lane reduction and new running
+  // max, one exp2 per score, the row sums.
+  auto pv_softmax = [&](const uint16_t* vt, f32x16 (&S)[NRB][NKB], float (&al)[NRB]) RA_INLINE {
     constexpr int NT = NPS * NDB;                  // P.V steps
     constexpr int NE = NRB * NKB * 16;              // exp2 units
     constexpr int NU = NRB + 1 + NE + 1;            // all units
-    auto vop = [&](int t) {
+    auto vop = [&](int t) RA_INLINE {
       const int ks = t / NDB, db = t % NDB;
       const uint32_t o = (vbase ^ (uint32_t)(db << 6)) + ks * 16 * D * 2;
       const i16x4 x1 = lds_read_tr(vt, o);
@@ -612,7 +578,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     };
     float mx[NRB], m_use[NRB], ls[NRB];
     bool any = false;
-    auto unit = [&](int u) {
+    auto unit = [&](int u) RA_INLINE {
       if (u < NRB) {  // in-lane max of row block u
         float m = kNegInf;
 #pragma unroll
@@ -645,17 +611,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
         for (int rb = 0; rb < NRB; ++rb) lsum[rb] = lsum[rb] * al[rb] + ls[rb];
       }
     };
-    bf16x8 va[3];
-    va[0] = vop(0);
-    if (NT > 1) va[1] = vop(1);
+    bf16x8 vq[3];
+    vq[0] = vop(0);
+    if (NT > 1) vq[1] = vop(1);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int ks = t / NDB, db = t % NDB;
-      if (t + 2 < NT) va[(t + 2) % 3] = vop(t + 2);
+      if (t + 2 < NT) vq[(t + 2) % 3] = vop(t + 2);
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
         acc[rb][db] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t % 3], pb[rb][ks], acc[rb][db], 0, 0, 0);
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[t % 3], pb[rb][ks], acc[rb][db], 0, 0, 0);
       // units [t*NU/NT, (t+1)*NU/NT), the rest after the last slot
 #pragma unroll
       for (int u = t * NU / NT; u < (t + 1) * NU / NT; ++u) unit(u);
@@ -663,18 +629,127 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     }
     return any;
   };
-  for (int v = 1; v < T; ++v) {
-    rescale();
-    f32x16 S[NRB][NKB];
-    front(S);
-    any = pv_softmax(vslot0 + (sl ^ 1) * TILE, S, alpha);
-    pack(S, pb, alpha);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(v+1), V(v) have landed
-    __syncthreads();
-    advance(v);
+
+  // Iteration v reads K(v) and V(v-1) and fetches K(v+1) and V(v) into the
+  // slots that K(v-1) and V(v-2) left; tile v lives in slot v & 1.  The
+  // scores of tile v are computed, then its softmax is issued between the
+  // P.V MFMAs of tile v-1, which do not depend on it, then tile v's bf16
+  // packing; the rare rescale for tile v's max is applied at the top of the
+  // next iteration, between P.V(v-1) and P.V(v).  The accumulator is touched
+  // by no branch but the rescale.  Tile 0 runs the same body: its "previous"
+  // V slot is filled with zeros and the probabilities start at zero.
+  Src s0 = next_src(), s1 = next_src();  // tiles v, v+1
+  {
+    Src zero = s0;
+    zero.vr = make_desc(p.v_cur, 0);  // a zero-size fetch: the slot fills with zeros
+    zero.off = 0;
+    issue_k(s0, kslot(0));
+    issue_v(zero, vslot(1));
   }
-  rescale();
-  pv(vslot0 + (sl ^ 1) * TILE, pb);
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int ks = 0; ks < NPS; ++ks) pb[rb][ks] = pbuf[0][rb][ks] = pbuf[1][rb][ks] = bf16x8{};
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+  __syncthreads();
+
+  bool any = false;       // the previous tile asked for a rescale ...
+  float alpha[NRB];       // ... by these factors
+  auto rescale = [&]() RA_INLINE {
+    if (any) {
+#if defined(__HIP_DEVICE_COMPILE__)
+      // the last P.V MFMAs may still be writing acc: wait them out
+      asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+#endif
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) scale_agprs(acc[rb][db], alpha[rb]);
+    }
+  };
+  // For fp32 output: the row sums over the bf16-rounded probabilities.
+  auto sum_rounded = [&](const bf16x8 (&pb)[NRB][NPS]) RA_INLINE {
+    if constexpr (F32OUT) {
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        float lq = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < NPS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const bf16x2 pr = {pb[rb][ks][e], pb[rb][ks][e + 1]};
+            lq = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lq, false);
+          }
+        lsum_q[rb] = lsum_q[rb] * alpha[rb] + lq;
+      }
+    }
+  };
+  // One tile.  `last` runs the block once more after the walk: its score
+  // tile is fully masked, so only the P.V of the final tile has an effect.
+  auto body = [&](auto slot, bool last) RA_INLINE {
+    constexpr int SL = decltype(slot)::value;  // slot of tile v
+    rescale();
+    if (!last) {
+      issue_k(s1, kslot(SL ^ 1));
+      issue_v(s0, vslot(SL));
+    }
+    int lim[NRB];
+    bool cut = bounds(s0, lim);
+    if (last) {
+      cut = true;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) lim[rb] = -kBKV;
+    }
+    if constexpr (ASM256) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) lim[rb] -= 4 * h;
+      uint64_t anyf;
+      // tile v's probabilities go to buffer v & 1 = SL; tile v-1's are read
+      tile_hd256<SL * TILE_B, (NSLOT + (SL ^ 1)) * TILE_B, SL ^ 1>(
+          acc, pbuf[SL ^ 1], pbuf[SL], qreg, ka, va, mlog, lsum, alpha, anyf, c2, kTau<F32OUT>,
+          __builtin_amdgcn_readfirstlane(cut ? 1u : 0u), lim);
+      any = anyf != 0;
+      sum_rounded(pbuf[SL]);
+    } else {
+      f32x16 S[NRB][NKB];
+      qk(kslot(SL), S);
+      if (cut) mask(S, lim);
+      any = pv_softmax(vslot(SL ^ 1), S, alpha);
+      pack(S, pb, alpha);
+    }
+    if (!last) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(v+1), V(v) have landed
+      __syncthreads();
+      s0 = s1;
+      s1 = next_src();
+    }
+  };
+  if constexpr (ASM256) {
+    // Tiles 0 .. T-1, two per trip so that slot offsets are constants, and
+    // one more pass of the block, v = T, for the P.V of the last tile: its
+    // score tile is fully masked and the K slot holds the zero tile fetched
+    // past the walk.
+    for (int v = 0;;) {
+      body(std::integral_constant<int, 0>{}, v == T);
+      if (v++ == T) break;
+      body(std::integral_constant<int, 1>{}, v == T);
+      if (v++ == T) break;
+    }
+  } else {
+    for (int v = 0; v < T;) {
+      body(std::integral_constant<int, 0>{}, false);
+      if (++v == T) break;
+      body(std::integral_constant<int, 1>{}, false);
+      ++v;
+    }
+    // P.V of the last tile, T - 1, whose V is in slot (T - 1) & 1.
+    rescale();
+    if (T & 1)
+      pv(vslot(0), pb);
+    else
+      pv(vslot(1), pb);
+  }
 
   // Epilogue: out = acc / l, lse = ln 2 * (m + log2 l).
 #pragma unroll

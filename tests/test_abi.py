@@ -127,3 +127,13 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ra, "_lib", None)
     with pytest.raises(ImportError):
         ra.lib()
+
+
+def test_generated_tile_block_is_current():
+    """The HD = 256 tile block is generated; the committed include must be
+    what its generator writes (else the kernel runs a stale schedule)."""
+    import subprocess
+    import sys
+    gen = os.path.join(ROOT, "context_causal_attention_ring_amd", "csrc", "gen_tile_hd256.py")
+    res = subprocess.run([sys.executable, gen, "--check"], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
