@@ -27,8 +27,9 @@ there is nothing to compare them with.
 from .stripe import (shard_lengths, stripe_position, stripe, destripe,
                      kv_cache_write_ref)
 from .attention import (bf16_bits_to_f64, attention_rows, ring_attention,
-                        ring_online, two_pass_merge)
+                        ring_online, two_pass_merge, rank_positions, zigzag_pieces)
 
 __all__ = ["shard_lengths", "stripe_position", "stripe", "destripe",
            "kv_cache_write_ref", "bf16_bits_to_f64", "attention_rows",
-           "ring_attention", "ring_online", "two_pass_merge"]
+           "ring_attention", "ring_online", "two_pass_merge", "rank_positions",
+           "zigzag_pieces"]

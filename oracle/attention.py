@@ -21,6 +21,13 @@ method's steps (ring rounds, then current blocks, one running (m, l, acc)).
 Conventions (readings where the pages are silent): GQA heads are contiguous
 groups, query head ``h`` uses KV head ``h // (NQ // NKV)``; ``lse`` is the
 natural-log log-sum-exp of the scaled scores, laid out ``[NQ, rows]``.
+
+Rank layout (Design section: the current phase keeps a two-sequence (head,
+tail) structure).  In the default layout chunk row ``i`` sits at chunk
+position ``i``.  With ``positions`` given, row ``i`` of the query tensor sits
+at chunk position ``positions[i]`` while the current K/V stay in token order
+(Design subtlety 1), so row ``i`` sees current tokens ``0..positions[i]``.
+``rank_positions`` gives the positions of one rank's (head, tail) pieces.
 """
 import math
 import numpy as np
@@ -32,19 +39,39 @@ def bf16_bits_to_f64(bits):
     return b.view(np.float32).astype(np.float64)
 
 
+def rank_positions(head_rows, tail_rows, head_pos, tail_pos):
+    """Chunk positions of a rank's query rows: the head piece (rows
+    ``0..head_rows-1``) starts at chunk position ``head_pos``, the tail piece
+    (the remaining ``tail_rows`` rows) at ``tail_pos``."""
+    return np.concatenate([head_pos + np.arange(head_rows),
+                           tail_pos + np.arange(tail_rows)]).astype(np.int64)
+
+
+def zigzag_pieces(chunk, ranks, r):
+    """(head_pos, tail_pos, piece) of rank ``r`` when a chunk of ``chunk``
+    tokens is cut into ``2 * ranks`` equal pieces and rank ``r`` owns pieces
+    ``r`` and ``2 * ranks - 1 - r`` (the load-balanced context-parallel
+    layout: every rank gets one early and one late piece)."""
+    piece = chunk // (2 * ranks)
+    assert piece * 2 * ranks == chunk
+    return r * piece, (2 * ranks - 1 - r) * piece, piece
+
+
 def attention_rows(q, k_tok, v_tok, k_cur, v_cur, rows, scale,
-                   cache=True, current=True, row_block=64):
+                   cache=True, current=True, row_block=64, positions=None):
     """Softmax attention of the chosen chunk rows, plain definition.
 
     q      [C, NQ, HD]   chunk queries (any float dtype; bf16 values are exact)
     k_tok  [L, NKV, HD]  cached keys in token order (L = cache_len)
     v_tok  [L, NKV, HD]
-    k_cur  [C, NKV, HD]  current keys in token order, row j at position L + j
-    v_cur  [C, NKV, HD]
+    k_cur  [N, NKV, HD]  current keys in token order, row j at position L + j
+    v_cur  [N, NKV, HD]
     rows   iterable of chunk row indices to evaluate (real rows only)
+    positions  chunk position of each row of ``q`` (default: row i at i)
 
-    Row ``i`` sees cache tokens ``0..L-1`` (if ``cache``) and current tokens
-    ``0..i`` (if ``current``); its scores are ``scale * q . k`` in fp64, and
+    Row ``i`` at chunk position ``p = positions[i]`` sees cache tokens
+    ``0..L-1`` (if ``cache``) and current tokens ``0..p`` (if
+    ``current``); its scores are ``scale * q . k`` in fp64, and
     ``out = sum_j e^(s_j - m) v_j / l``, ``l = sum_j e^(s_j - m)``,
     ``lse = m + ln l`` with ``m`` the row's max score.  The sum over j is
     taken in two parts: the cache part, identical for every row, as one
@@ -59,6 +86,7 @@ def attention_rows(q, k_tok, v_tok, k_cur, v_cur, rows, scale,
     L = k_tok.shape[0] if cache else 0
     NKV = k_cur.shape[1]
     G = NQ // NKV
+    pos = np.arange(C) if positions is None else np.asarray(positions)
     out = np.zeros((len(rows), NQ, HD))
     lse = np.full((NQ, len(rows)), -np.inf)
     for g in range(NKV):
@@ -72,8 +100,8 @@ def attention_rows(q, k_tok, v_tok, k_cur, v_cur, rows, scale,
             nb = len(blk)
             Qb = np.stack([np.asarray(q[i, hs], np.float64) for i in blk])      # [nb, G, HD]
             Sc = scale * (Qb.reshape(nb * G, HD) @ Kc.T).reshape(nb, G, L)     # cache scores
-            Sn = [scale * (Qb[b] @ Kn[:(i + 1 if current else 0)].T)          # current scores
-                  for b, i in enumerate(blk)]                                  # [G, i+1] each
+            Sn = [scale * (Qb[b] @ Kn[:(pos[i] + 1 if current else 0)].T)     # current scores
+                  for b, i in enumerate(blk)]                                  # [G, p+1] each
             # row max over both parts (-inf when a row sees nothing)
             m = np.full((nb, G), -np.inf)
             for b in range(nb):
@@ -85,7 +113,7 @@ def attention_rows(q, k_tok, v_tok, k_cur, v_cur, rows, scale,
             Ec = np.exp(Sc - m_safe[:, :, None])                                # [nb, G, L]
             Oc = (Ec.reshape(nb * G, L) @ Vc).reshape(nb, G, HD)
             for b, i in enumerate(blk):
-                En = np.exp(Sn[b] - m_safe[b][:, None])                          # [G, i+1]
+                En = np.exp(Sn[b] - m_safe[b][:, None])                          # [G, p+1]
                 l = Ec[b].sum(axis=1) + En.sum(axis=1)
                 if not (l > 0).all():
                     continue
@@ -95,17 +123,18 @@ def attention_rows(q, k_tok, v_tok, k_cur, v_cur, rows, scale,
 
 
 def ring_attention(q, k_cache, v_cache, k_cur, v_cur, cache_len, P,
-                   interleave, rows, scale):
+                   interleave, rows, scale, positions=None):
     """The fused launch's result from a striped cache: de-stripe the shards
     with the cache map, then ``attention_rows``."""
     from .stripe import destripe
     k_tok = destripe(np.asarray(k_cache), cache_len, P, interleave)
     v_tok = destripe(np.asarray(v_cache), cache_len, P, interleave)
-    return attention_rows(q, k_tok, v_tok, k_cur, v_cur, rows, scale)
+    return attention_rows(q, k_tok, v_tok, k_cur, v_cur, rows, scale,
+                          positions=positions)
 
 
 def ring_online(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, interleave,
-                rows, scale, ring_start=0, block=64):
+                rows, scale, ring_start=0, block=64, positions=None):
     """The method's own walk, in fp64, one chunk row at a time.
 
     Per row: running max ``m`` = -inf, normaliser ``l`` = 0, accumulator
@@ -113,7 +142,7 @@ def ring_online(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, interleave,
     ``(ring_start - k) mod P`` and its valid slots in blocks of ``block``
     (no causal mask: every cached token precedes the chunk).  Current
     region: current tokens in blocks of ``block``, keeping only tokens at or
-    before the row (causal).  Each block updates the shared state with
+    before the row's chunk position (causal).  Each block updates the shared state with
     ``m' = max(m, max s)``, ``acc = e^(m-m') acc + sum e^(s-m') v``,
     ``l = e^(m-m') l + sum e^(s-m')``.  Finally ``out = acc / l`` and
     ``lse = m + ln l``.  Same return layout as ``attention_rows``.
@@ -128,6 +157,7 @@ def ring_online(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, interleave,
     vc = np.asarray(v_cache, np.float64)
     kcur = np.asarray(k_cur, np.float64)
     vcur = np.asarray(v_cur, np.float64)
+    pos = np.arange(C) if positions is None else np.asarray(positions)
     out = np.zeros((len(rows), NQ, HD))
     lse = np.full((NQ, len(rows)), -np.inf)
     for r, i in enumerate(rows):
@@ -155,8 +185,8 @@ def ring_online(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, interleave,
                 for b0 in range(0, lens[s_id], block):
                     b1 = min(b0 + block, lens[s_id])
                     visit(kc[s_id, b0:b1, g], vc[s_id, b0:b1, g])
-            for c0 in range(0, i + 1, block):        # current region, causal
-                c1 = min(c0 + block, i + 1)
+            for c0 in range(0, pos[i] + 1, block):   # current region, causal
+                c1 = min(c0 + block, pos[i] + 1)
                 visit(kcur[c0:c1, g], vcur[c0:c1, g])
             out[r, hs] = acc / l[:, None]
             lse[hs, r] = m + np.log(l)

@@ -232,7 +232,7 @@ def test_bf16_bits_decode():
 # --- mutation checks: a plausible mistake in the oracle must fail a pin ---
 
 MUTATIONS = [
-    ("Kn[:(i + 1 if current else 0)]", "Kn[:(i + 2 if current else 0)]"),        # causal off by one
+    ("Kn[:(pos[i] + 1 if current else 0)]", "Kn[:(pos[i] + 2 if current else 0)]"),  # causal off by one
     ("hs = slice(g * G, (g + 1) * G)", "hs = slice(g, NQ, NKV)"),               # interleaved GQA map
     ("Oc = (Ec.reshape", "Oc = 0 * (Ec.reshape"),                               # cache values dropped
     ("Sc = scale * (Qb", "Sc = -scale * (Qb"),                                  # sign of cache scores
