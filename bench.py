@@ -31,19 +31,21 @@ METRIC = "fused ring attention TFLOP/s + % bf16 MFMA peak; ms/chunk at 32k ctx"
 
 
 def alg_flops(w):
-    """QK^T + PV flops over visible (row, key) pairs of the real rows."""
-    rows = w.real_rows
-    pairs = rows * w.cache_len + rows * (rows + 1) // 2
+    """QK^T + PV flops over visible (row, key) pairs of the real rows: a row
+    at chunk position p sees the cache and current tokens 0..p."""
+    pos = w.positions[:w.real_rows]
+    pairs = w.real_rows * w.cache_len + sum(p + 1 for p in pos)
     return 4 * w.hd * w.nq * pairs
 
 
 def alg_bytes(w, with_write):
     """Q + visible K/V once + out + LSE (+ the write's read and write)."""
     row = w.nkv * w.hd * 2
+    cur_seen = max(w.positions[:w.real_rows]) + 1 if w.real_rows else 0
     b = w.real_rows * w.nq * w.hd * 2 * 2 + w.real_rows * w.nq * 4
-    b += 2 * (w.cache_len + w.real_rows) * row
+    b += 2 * (w.cache_len + cur_seen) * row
     if with_write:
-        b += 2 * 2 * w.real_rows * row
+        b += 2 * 2 * w.n_cur_real * row
     return b
 
 
@@ -87,7 +89,8 @@ def setup(w, device):
     d["v_cache"] = torch.full(shape, float("nan"), device=device, dtype=torch.bfloat16)
     layout = ra.StripeLayout(w.interleave, 0)
     dims = ra.make_dims(d["q"], d["k_cur"], w.shard_cap, real_rows=w.real_rows,
-                        head_rows=w.head_rows, scale=w.scale)
+                        head_rows=w.head_rows, scale=w.scale, head_pos=w.head_pos,
+                        tail_pos=w.tail_start)
     if w.cache_len:
         k_tok = t["k_cache_tok"].to(device)
         v_tok = t["v_cache_tok"].to(device)
@@ -117,9 +120,9 @@ def cpu_baseline(w, t, budget_s=12.0):
     while done < len(order) and elapsed < budget_s:
         rows = order[done:done + blk]
         t0 = time.perf_counter()
-        oracle.attention_rows(*args, rows, w.scale)
+        oracle.attention_rows(*args, rows, w.scale, positions=w.positions)
         elapsed += time.perf_counter() - t0
-        flops += sum(4 * w.hd * w.nq * (w.cache_len + i + 1) for i in rows)
+        flops += sum(4 * w.hd * w.nq * (w.cache_len + w.positions[i] + 1) for i in rows)
         done += len(rows)
         blk = min(64, blk * 2)
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads,
@@ -172,7 +175,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        ra.kv_cache_write(d["k_cur"], d["v_cur"], w.real_rows, d["k_cache"], d["v_cache"],
+        ra.kv_cache_write(d["k_cur"], d["v_cur"], w.n_cur_real, d["k_cache"], d["v_cache"],
                           w.cache_len, w.P, layout, dims)
         if ev is not None:
             ev[0].record(stream)
@@ -228,7 +231,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: fused ring+current prefill of one {w.q_rows}-row "
-                               f"chunk (head {w.head_rows} + tail {w.tail_rows}) over "
+                               f"chunk share (head {w.head_rows} rows at chunk position "
+                               f"{w.head_pos} + tail {w.tail_rows} at {w.tail_start}, "
+                               f"{w.n_cur} current tokens) over "
                                f"{w.cache_len} cached tokens in P={w.P} striped shards, "
                                f"NQ={w.nq} NKV={w.nkv} HD={w.hd}, plus the strided "
                                f"kv_cache_write of the chunk",

@@ -32,6 +32,8 @@ class Dims(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("q_rows", ctypes.c_int32),
                 ("head_rows", ctypes.c_int32), ("real_rows", ctypes.c_int32),
+                ("head_pos", ctypes.c_int32), ("tail_pos", ctypes.c_int32),
+                ("cur_len", ctypes.c_int32),
                 ("shard_cap", ctypes.c_int64), ("scale", ctypes.c_float),
                 ("out_dtype", ctypes.c_int32)]
 
@@ -118,28 +120,35 @@ def kv_cache_write(k_cur, v_cur, n_tokens, k_cache, v_cache, cache_len, P, strip
                                 ctypes.byref(dims), _stream(stream)))
 
 
-def make_dims(q, k_cur, shard_cap, real_rows=None, head_rows=None, scale=0.0, out_fp32=False):
+def make_dims(q, k_cur, shard_cap, real_rows=None, head_rows=None, scale=0.0, out_fp32=False,
+              head_pos=0, tail_pos=None):
+    """Dims for q [C, NQ, HD] and token-order k_cur [cur_len, NKV, HD].  The
+    default layout is contiguous: head piece at chunk position 0, tail piece
+    right after it."""
     C, NQ, HD = q.shape
     NKV = k_cur.shape[1]
-    return Dims(num_q_heads=NQ, num_kv_heads=NKV, head_dim=HD, q_rows=C,
-                head_rows=C if head_rows is None else head_rows,
-                real_rows=C if real_rows is None else real_rows, shard_cap=shard_cap,
-                scale=scale, out_dtype=RA_DTYPE_FP32 if out_fp32 else RA_DTYPE_BF16)
+    head_rows = C if head_rows is None else head_rows
+    return Dims(num_q_heads=NQ, num_kv_heads=NKV, head_dim=HD, q_rows=C, head_rows=head_rows,
+                real_rows=C if real_rows is None else real_rows, head_pos=head_pos,
+                tail_pos=head_pos + head_rows if tail_pos is None else tail_pos,
+                cur_len=k_cur.shape[0], shard_cap=shard_cap, scale=scale,
+                out_dtype=RA_DTYPE_FP32 if out_fp32 else RA_DTYPE_BF16)
 
 
 def prefill(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, interleave=1, ring_start=0,
             real_rows=None, head_rows=None, scale=0.0, out_fp32=False, with_lse=True,
-            stream=None):
+            stream=None, head_pos=0, tail_pos=None):
     """Allocate out/lse with torch and run ring_attn_prefill.
 
     q [C, NQ, HD] bf16, k_cache/v_cache [P, shard_cap, NKV, HD] bf16,
-    k_cur/v_cur [C, NKV, HD] bf16 (token order).  Returns (out, lse)."""
+    k_cur/v_cur [cur_len, NKV, HD] bf16 (token order).  Returns (out, lse)."""
     import torch
     C, NQ, HD = q.shape
     out = torch.empty(C, NQ, HD, device=q.device,
                       dtype=torch.float32 if out_fp32 else torch.bfloat16)
     lse = torch.empty(NQ, C, device=q.device, dtype=torch.float32) if with_lse else None
-    dims = make_dims(q, k_cur, k_cache.shape[1], real_rows, head_rows, scale, out_fp32)
+    dims = make_dims(q, k_cur, k_cache.shape[1], real_rows, head_rows, scale, out_fp32,
+                     head_pos, tail_pos)
     ring_attn_prefill(q, k_cache, v_cache, k_cur, v_cur, cache_len, P,
                       StripeLayout(interleave, ring_start), out, lse, dims, stream)
     return out, lse

@@ -11,7 +11,7 @@ struct FusedParams {
   const uint16_t* q;        // bf16 [C, NQ, HD]
   const uint16_t* k_cache;  // bf16 [P, shard_cap, NKV, HD]
   const uint16_t* v_cache;
-  const uint16_t* k_cur;    // bf16 [C, NKV, HD], token order
+  const uint16_t* k_cur;    // bf16 [cur_len, NKV, HD], token order
   const uint16_t* v_cur;
   void* out;                // [C, NQ, HD] bf16 | fp32
   float* lse;               // [NQ, C] or nullptr
@@ -22,6 +22,8 @@ struct FusedParams {
   int32_t nb;               // ring tiles per shard visit (max shard length / BKV, rounded up)
   int32_t nq, nkv, group;   // group = NQ / NKV
   int32_t q_rows, real_rows;
+  int32_t head_rows;        // rows of the head piece; the rest is the tail piece
+  int32_t head_pos, tail_pos;  // chunk positions of the first head / tail row
   int32_t row_tiles;        // workgroups per KV head
   int32_t grid_real;        // row_tiles * NKV
   int32_t out_f32;

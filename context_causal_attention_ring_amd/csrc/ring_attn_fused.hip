@@ -263,14 +263,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   const int rt = p.row_tiles - 1 - (logical - g * p.row_tiles);  // long causal rows first
   const int row0 = rt * kRowsPerWG;
 
-  // This lane's rows, one per row block.
-  int token[NRB], head[NRB];
+  // This lane's rows, one per row block: query row `token` (head or tail
+  // piece) at chunk position pos.
+  auto chunk_pos = [&](int t) RA_INLINE {
+    return t < p.head_rows ? p.head_pos + t : p.tail_pos + (t - p.head_rows);
+  };
+  int token[NRB], head[NRB], pos[NRB];
   bool row_ok[NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const int row = row0 + wave * kRowsPerWave + rb * 32 + lr;
     token[rb] = row / p.group;
     head[rb] = g * p.group + (row - token[rb] * p.group);
+    pos[rb] = chunk_pos(token[rb]);
     row_ok[rb] = token[rb] < p.real_rows;
   }
 
@@ -291,15 +296,26 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   }
 
   // Tile schedule: ring region = P shard visits of nb tiles, then the
-  // current tiles up to this workgroup's last real token.
-  const int wg_last = min(p.real_rows - 1, (row0 + kRowsPerWG - 1) / p.group);
-  const int wg_first = row0 / p.group;
+  // current tiles up to the largest chunk position among this workgroup's
+  // real rows.  The rows [t0, t1] may straddle the head/tail boundary, so
+  // the position range is taken over both pieces.
+  const int t0 = row0 / p.group;
+  const int t1 = min(p.real_rows - 1, (row0 + kRowsPerWG - 1) / p.group);
+  int wg_min_pos, wg_max_pos;
+  if (t1 < p.head_rows || t0 >= p.head_rows) {
+    wg_min_pos = chunk_pos(t0);
+    wg_max_pos = chunk_pos(t1);
+  } else {
+    wg_min_pos = min(chunk_pos(t0), p.tail_pos);
+    wg_max_pos = max(chunk_pos(p.head_rows - 1), chunk_pos(t1));
+  }
   const int n_ring = p.P * p.nb;
-  const int n_cur = wg_last / kBKV + 1;
+  const int n_cur = wg_max_pos / kBKV + 1;
   const int T = n_ring + n_cur;
   const uint32_t rowstride = (uint32_t)p.nkv * D * 2;  // bytes between tokens
   const uint32_t tile_stride = kBKV * rowstride;       // bytes between tiles
-  const uint32_t cur_bytes = (uint32_t)p.real_rows * rowstride;
+  // current tokens past the last position any row here sees load as zeros
+  const uint32_t cur_bytes = (uint32_t)(wg_max_pos + 1) * rowstride;
   const int full_i = (int)p.full * p.interleave;  // < 2^31: bounded by a shard's length
 
   // Per-tile source, chosen by value: descriptors of the region (sized to
@@ -554,8 +570,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       return src.lim_ring < kBKV;
     }
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) lim[rb] = token[rb] + 1 - src.key0;
-    return src.key0 + kBKV > wg_first + 1;
+    for (int rb = 0; rb < NRB; ++rb) lim[rb] = pos[rb] + 1 - src.key0;
+    return src.key0 + kBKV > wg_min_pos + 1;
   };
 
   // P.V of the previous tile with the softmax of the current one (generic

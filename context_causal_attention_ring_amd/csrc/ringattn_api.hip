@@ -105,6 +105,23 @@ int ring_attn_prefill(const void* q, const void* k_cache, const void* v_cache, c
     return fail(RA_ERR_INVALID_ARG, "head_rows must be in [0, q_rows=%d]; got %d", C, d.head_rows);
   if (d.real_rows < 0 || d.real_rows > C)
     return fail(RA_ERR_INVALID_ARG, "real_rows must be in [0, q_rows=%d]; got %d", C, d.real_rows);
+  if (d.head_pos < 0 || d.tail_pos < 0 || d.cur_len < 0)
+    return fail(RA_ERR_INVALID_ARG, "head_pos (%d), tail_pos (%d) and cur_len (%d) must be >= 0",
+                d.head_pos, d.tail_pos, d.cur_len);
+  // The largest chunk position among the real rows (-1 when there are none).
+  int64_t max_pos = -1;
+  if (d.real_rows > 0) {
+    const int32_t real_head = d.real_rows < d.head_rows ? d.real_rows : d.head_rows;
+    if (real_head > 0) max_pos = (int64_t)d.head_pos + real_head - 1;
+    if (d.real_rows > d.head_rows) {
+      const int64_t t = (int64_t)d.tail_pos + (d.real_rows - d.head_rows) - 1;
+      max_pos = t > max_pos ? t : max_pos;
+    }
+  }
+  if (max_pos >= d.cur_len)
+    return fail(RA_ERR_INVALID_ARG,
+                "real rows reach chunk position %lld but k_cur/v_cur hold cur_len=%d tokens",
+                (long long)max_pos, d.cur_len);
   if (d.out_dtype != RA_DTYPE_BF16 && d.out_dtype != RA_DTYPE_FP32)
     return fail(RA_ERR_INVALID_ARG, "out_dtype must be RA_DTYPE_BF16 or RA_DTYPE_FP32; got %d",
                 d.out_dtype);
@@ -134,15 +151,15 @@ int ring_attn_prefill(const void* q, const void* k_cache, const void* v_cache, c
       return fail(RA_ERR_INVALID_ARG, "every tensor pointer must be 16-byte aligned");
 
   // 32-bit buffer offsets: a shard visit reads at most max_len + BKV rows,
-  // the current region at most q_rows + BKV rows.
+  // the current region at most cur_len + BKV rows.
   const int64_t rowstride = (int64_t)NKV * HD * 2;
   const int64_t lim31 = (int64_t)1 << 31;
   if ((max_len + ra::kBKV) * rowstride >= lim31)
     return fail(RA_ERR_UNSUPPORTED, "a shard of %lld tokens x %lld bytes exceeds 2 GiB",
                 (long long)max_len, (long long)rowstride);
-  if (((int64_t)C + ra::kBKV) * rowstride >= lim31)
-    return fail(RA_ERR_UNSUPPORTED, "the current chunk (%d tokens x %lld bytes) exceeds 2 GiB", C,
-                (long long)rowstride);
+  if (((int64_t)d.cur_len + ra::kBKV) * rowstride >= lim31)
+    return fail(RA_ERR_UNSUPPORTED, "the current chunk (%d tokens x %lld bytes) exceeds 2 GiB",
+                d.cur_len, (long long)rowstride);
   const int64_t rows_total = (int64_t)d.real_rows * group;
   if (rows_total + ra::kRowsPerWG >= lim31 / 2)
     return fail(RA_ERR_UNSUPPORTED, "real_rows * (NQ/NKV) = %lld is too large",
@@ -150,7 +167,7 @@ int ring_attn_prefill(const void* q, const void* k_cache, const void* v_cache, c
 
   // Outputs must not alias inputs.
   const int64_t q_bytes = (int64_t)C * NQ * HD * 2;
-  const int64_t cur_bytes = (int64_t)C * NKV * HD * 2;
+  const int64_t cur_bytes = (int64_t)d.cur_len * NKV * HD * 2;
   const int64_t cache_bytes = (int64_t)P * d.shard_cap * NKV * HD * 2;
   const int64_t out_bytes = (int64_t)C * NQ * HD * (d.out_dtype == RA_DTYPE_FP32 ? 4 : 2);
   const int64_t lse_bytes = (int64_t)NQ * C * 4;
@@ -188,6 +205,9 @@ int ring_attn_prefill(const void* q, const void* k_cache, const void* v_cache, c
   p.group = group;
   p.q_rows = C;
   p.real_rows = d.real_rows;
+  p.head_rows = d.head_rows;
+  p.head_pos = d.head_pos;
+  p.tail_pos = d.tail_pos;
   p.row_tiles = (int32_t)((rows_total + ra::kRowsPerWG - 1) / ra::kRowsPerWG);
   p.grid_real = p.row_tiles * NKV;
   p.out_f32 = d.out_dtype == RA_DTYPE_FP32;

@@ -62,20 +62,34 @@ typedef struct {
   int32_t ring_start; /* in [0, P) */
 } ra_stripe_layout_t;
 
-/* Shapes.  The chunk has q_rows = C rows: a head sequence of head_rows rows
- * followed by a tail sequence (Design section: the launch keeps the two
- * sequences, both padded to full length, and the caller discards pad rows).
- * Chunk row i is the token at global position cache_len + i.  Rows
- * [0, real_rows) are real; rows [real_rows, q_rows) are pads: their current
- * K/V are never read as keys and their out/lse entries are not written. */
+/* Shapes.  The query rows are a head piece of head_rows rows followed by a
+ * tail piece of q_rows - head_rows rows (Design section: the current phase
+ * keeps its two-sequence (head, tail) structure, both padded to full
+ * length, and the caller discards pad rows).  The pieces sit at chunk
+ * positions head_pos and tail_pos: query row i is the token at chunk
+ * position
+ *     pos(i) = head_pos + i                for i <  head_rows,
+ *              tail_pos + (i - head_rows)  for i >= head_rows,
+ * i.e. at global position cache_len + pos(i), and it sees current tokens
+ * 0..pos(i).  The contiguous layout is head_pos = 0, tail_pos = head_rows;
+ * the load-balanced context-parallel layout gives rank r of R the pieces r
+ * and 2R-1-r of a chunk cut into 2R.  The current K/V hold cur_len tokens
+ * of the chunk in token order (Design, first subtlety).  Rows [0, real_rows)
+ * are real; rows [real_rows, q_rows) are pads: their out/lse entries are
+ * not written, and current tokens past the last real row's position are
+ * never read as keys. */
 typedef struct {
   int32_t num_q_heads;  /* NQ >= 1 */
   int32_t num_kv_heads; /* NKV >= 1, NQ % NKV == 0; query head h reads KV
                            head h / (NQ / NKV) */
   int32_t head_dim;     /* HD in {64, 128, 256} */
   int32_t q_rows;       /* C >= 0 */
-  int32_t head_rows;    /* 0 <= head_rows <= q_rows (scheduling metadata) */
+  int32_t head_rows;    /* 0 <= head_rows <= q_rows */
   int32_t real_rows;    /* 0 <= real_rows <= q_rows */
+  int32_t head_pos;     /* chunk position of query row 0, >= 0 */
+  int32_t tail_pos;     /* chunk position of query row head_rows, >= 0 */
+  int32_t cur_len;      /* tokens in k_cur / v_cur; every real row's
+                           position must be < cur_len */
   int64_t shard_cap;    /* slots allocated per shard, >= 1 */
   float scale;          /* softmax scale, finite and > 0; 0 selects
                            1/sqrt(HD); negative scales are rejected */
@@ -89,14 +103,14 @@ typedef struct {
  *   q        bf16 [C, NQ, HD]             chunk queries
  *   k_cache  bf16 [P, shard_cap, NKV, HD] striped cache keys (read only)
  *   v_cache  bf16 [P, shard_cap, NKV, HD] striped cache values (read only)
- *   k_cur    bf16 [C, NKV, HD]  current keys, TOKEN order: row i is
- *                               position cache_len + i
- *   v_cur    bf16 [C, NKV, HD]  current values, token order
+ *   k_cur    bf16 [cur_len, NKV, HD]  current keys, TOKEN order: row j is
+ *                               global position cache_len + j
+ *   v_cur    bf16 [cur_len, NKV, HD]  current values, token order
  *   cache_len  number of cached positions, >= 0 (0: no ring region)
  *   P          number of shards, >= 1
- *   out      [C, NQ, HD] bf16 or fp32 (dims->out_dtype); real rows get
+ *   out      [C, NQ, HD] bf16 or fp32 (dims->out_dtype); real row i gets
  *            softmax(scale * q k^T) v over cache positions [0, cache_len)
- *            and current rows 0..i
+ *            and current tokens 0..pos(i)
  *   lse      fp32 [NQ, C] natural-log log-sum-exp of the scaled scores of
  *            each real row, or NULL to skip
  *

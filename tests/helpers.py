@@ -52,14 +52,15 @@ class Case:
     def oracle_rows(self, rows):
         t, w = self.t, self.w
         return oracle.attention_rows(f64(t["q"]), f64(t["k_cache_tok"]), f64(t["v_cache_tok"]),
-                                     f64(t["k_cur"]), f64(t["v_cur"]), rows, w.scale)
+                                     f64(t["k_cur"]), f64(t["v_cur"]), rows, w.scale,
+                                     positions=w.positions)
 
 
 def sample_rows(w, n_random, seed=0):
     """Rows for sampled parity at full size: first/last rows of the head and
     tail sequences, the real/pad boundary, and seeded random real rows."""
     real = w.real_rows
-    fixed = {0, 1, w.head_rows - 1, w.head_rows, real - 1, real - 2}
+    fixed = {0, 1, w.head_rows - 1, w.head_rows, w.head_rows + 1, real - 1, real - 2}
     fixed = {r for r in fixed if 0 <= r < real}
     rng = np.random.default_rng(seed)
     rand = set(rng.choice(real, size=min(n_random, real), replace=False).tolist())

@@ -44,7 +44,8 @@ def test_shard_len_matches_oracle(P, I):
 
 def dims(**kw):
     base = dict(num_q_heads=4, num_kv_heads=1, head_dim=64, q_rows=128, head_rows=64,
-                real_rows=128, shard_cap=320, scale=0.0, out_dtype=0)
+                real_rows=128, head_pos=0, tail_pos=64, cur_len=128, shard_cap=320, scale=0.0,
+                out_dtype=0)
     base.update(kw)
     return ra.Dims(**base)
 
@@ -80,6 +81,13 @@ BAD_PREFILL = [
     (dict(d=dims(), out=FAKE + 0x10), 1, "overlaps"),
     (dict(d=dims(), lse=FAKE + 0x3000000), 1, "overlaps"),
     (dict(d=dims(num_kv_heads=1, head_dim=256, shard_cap=1 << 23), cache_len=1 << 24), 2, "2 GiB"),
+    (dict(d=dims(head_pos=-1)), 1, "head_pos"),
+    (dict(d=dims(tail_pos=-3)), 1, "tail_pos"),
+    (dict(d=dims(cur_len=-1)), 1, "cur_len"),
+    (dict(d=dims(cur_len=127)), 1, "cur_len=127"),                   # tail reaches position 127
+    (dict(d=dims(head_pos=40, tail_pos=0, cur_len=103)), 1, "position 103"),  # head reaches 103
+    (dict(d=dims(num_kv_heads=1, head_dim=256, cur_len=1 << 22, q_rows=4, head_rows=4,
+                 real_rows=4, tail_pos=4)), 2, "2 GiB"),
 ]
 
 
@@ -88,6 +96,14 @@ def test_prefill_rejects_bad_arguments(kw, code, msg):
     rc = call_prefill(**kw)
     assert rc == code
     assert msg in ra.lib().ra_last_error().decode()
+
+
+def test_pad_rows_do_not_need_current_tokens():
+    # the tail piece is all pads (real_rows == head_rows): its positions may
+    # lie past cur_len; validation passes and fails only later on the
+    # overlap check planted here, i.e. after the position checks
+    rc = call_prefill(dims(real_rows=64, tail_pos=4000, cur_len=64), out=FAKE + 0x10)
+    assert rc == 1 and "overlaps" in ra.lib().ra_last_error().decode()
 
 
 def test_prefill_no_real_rows_is_a_no_op():

@@ -44,8 +44,10 @@ def run(case, out_fp32=False, ring_start=0, fill_out=SENTINEL):
                      dtype=torch.float32 if out_fp32 else torch.bfloat16)
     lse = torch.full((NQ, C), fill_out, device="cuda", dtype=torch.float32)
     dims = ra.make_dims(d["q"], d["k_cur"], w.shard_cap, real_rows=w.real_rows,
-                        head_rows=w.head_rows, scale=w.scale, out_fp32=out_fp32)
+                        head_rows=w.head_rows, scale=w.scale, out_fp32=out_fp32,
+                        head_pos=w.head_pos, tail_pos=w.tail_start)
     print(f"[gpu] ring_attn_prefill {w.name} C={C} L={w.cache_len} P={w.P} I={w.interleave} "
+          f"head={w.head_rows}@{w.head_pos} tail={w.tail_rows}@{w.tail_start} cur={w.n_cur} "
           f"NQ={NQ} NKV={w.nkv} HD={HD} real={w.real_rows} start={ring_start}", flush=True)
     ra.ring_attn_prefill(d["q"], d["k_cache"], d["v_cache"], d["k_cur"], d["v_cur"], w.cache_len,
                          w.P, ra.StripeLayout(w.interleave, ring_start), out, lse, dims)
@@ -239,3 +241,63 @@ def test_32k_write_then_prefill():
     assert np.array_equal(bits(d["k_cache"].cpu()), kc_ref)
     assert np.array_equal(bits(d["v_cache"].cpu()), vc_ref)
     compare(case, out, lse, sample_rows(w, 16, seed=5), TOL_BF16)
+
+
+# ---------------------------------------------------------------- rank layout (head/tail pieces)
+
+def chunk128(name, **kw):
+    """A 128-token chunk in the contiguous layout (the base of rank shares)."""
+    return small(name, head_rows=64, tail_rows=64, **kw)
+
+
+RANK_CASES = [
+    workloads.CONFIGS["tiny_rank1of2"],
+    workloads.rank_share(chunk128("r-hd64", hd=64, real_rows=128), 4, 0, name="r-hd64-rank0of4"),
+    workloads.rank_share(chunk128("r-hd128", cache_len=333, real_rows=100), 4, 1,
+                         name="r-hd128-partial-tail"),   # tail [96, 112): 4 real rows
+    workloads.rank_share(chunk128("r-hd256", nq=16, nkv=1, hd=256, cache_len=257, P=2,
+                                  real_rows=75), 4, 2, name="r-hd256-pad-tail"),  # tail all pad
+    workloads.rank_share(chunk128("r-nocache", nq=4, nkv=2, hd=256, cache_len=0, P=1,
+                                  real_rows=128), 2, 0, name="r-nocache"),
+]
+
+
+@pytest.mark.parametrize("w", RANK_CASES, ids=lambda w: w.name)
+def test_rank_layout_parity(w):
+    case = Case(w).to_device()
+    out, lse = run(case)
+    compare(case, out, lse, list(range(w.real_rows)), TOL_BF16)
+    check_pads_untouched(case, out, lse)
+
+
+@pytest.mark.parametrize("name,n_random", [("32k_rank3of8", None), ("128k_rank0of8", None),
+                                           ("128k_rank2of8", 48)])
+def test_rank_layout_full_size(name, n_random):
+    w = workloads.CONFIGS[name]
+    case = Case(w).to_device()
+    out, lse = run(case)
+    rows = list(range(w.real_rows)) if n_random is None else sample_rows(w, n_random, seed=w.seed)
+    compare(case, out, lse, rows, TOL_BF16)
+    check_pads_untouched(case, out, lse)
+
+
+def test_rank_shares_reassemble_the_chunk():
+    """Every rank's share, fed the rows of one chunk at its piece positions,
+    reproduces (bitwise in the LSE's ordering-free sense: within rounding)
+    the contiguous launch over the whole chunk."""
+    full = chunk128("reassemble", hd=256, cache_len=300, real_rows=128)
+    fcase = Case(full).to_device()
+    fout, flse = run(fcase)
+    ranks = 4
+    for r in range(ranks):
+        w = workloads.rank_share(full, ranks, r)
+        case = Case(w)
+        pos = w.positions
+        case.t["q"] = fcase.t["q"][pos]           # the chunk's own rows at the rank's positions
+        case.t["k_cur"], case.t["v_cur"] = fcase.t["k_cur"], fcase.t["v_cur"]
+        case.t["k_cache_tok"], case.t["v_cache_tok"] = fcase.t["k_cache_tok"], fcase.t["v_cache_tok"]
+        case.kc, case.vc = fcase.kc, fcase.vc
+        case.to_device()
+        out, lse = run(case)
+        assert (out.float() - fout[pos].float()).abs().max().item() <= TOL_BF16
+        assert (lse - flse[:, pos]).abs().max().item() <= TOL_LSE
