@@ -139,6 +139,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="32k", help="workload name (default: 32k)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-two-launch", action="store_true",
+                    help="skip timing the two-launch comparator (cache-only + current-only + merge)")
     ap.add_argument("--traffic", default=TRAFFIC_SUMMARY,
                     help="rocprofv3 summary holding the measured HBM bytes per fused launch")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -199,6 +201,32 @@ def main():
     kern_ms_avg = sum(kern_ms) / len(kern_ms)
     ms_per_step = total_s * 1e3 / args.steps
 
+    # The removed two-launch variant as a comparator: cache-only launch,
+    # current-only launch, LSE merge (same write before it).
+    two = None
+    if not args.no_two_launch:
+        C = w.q_rows  # partials in the model dtype (bf16) with fp32 LSEs, merged in fp32
+        parts = (torch.empty(C, w.nq, w.hd, device=dev, dtype=torch.bfloat16),
+                 torch.empty(w.nq, C, device=dev),
+                 torch.empty(C, w.nq, w.hd, device=dev, dtype=torch.bfloat16),
+                 torch.empty(w.nq, C, device=dev))
+
+        def step2():
+            ra.kv_cache_write(d["k_cur"], d["v_cur"], w.n_cur_real, d["k_cache"], d["v_cache"],
+                              w.cache_len, w.P, layout, dims)
+            ra.two_launch_prefill(d["q"], d["k_cache"], d["v_cache"], d["k_cur"], d["v_cur"],
+                                  w.cache_len, w.P, layout, d["out"], d["lse"], dims, parts)
+        for _ in range(args.warmup):
+            step2()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            step2()
+        torch.cuda.synchronize()
+        ms2 = (time.perf_counter() - t1) * 1e3 / args.steps
+        del parts
+        two = {"ms_per_step": round(ms2, 4), "fused_time_reduction": None}
+
     # Cold-cache view: evict the Infinity Cache with a 512 MiB write before each step.
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     cold = []
@@ -249,6 +277,9 @@ def main():
                      "kernel_ms_avg": round(kern_ms_avg, 4)},
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
+    if two is not None:
+        two["fused_time_reduction"] = round(1 - ms_per_step / two["ms_per_step"], 4)
+        res["two_launch"] = two
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, t)
     print(json.dumps(res), flush=True)

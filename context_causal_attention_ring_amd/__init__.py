@@ -13,15 +13,17 @@ import ctypes
 import os
 
 __all__ = ["StripeLayout", "Dims", "RingAttnError", "lib", "ring_attn_prefill",
-           "kv_cache_write", "ra_shard_len", "ra_version", "prefill", "LIB_PATH",
-           "EXPORTED_SYMBOLS"]
+           "ring_attn_partial", "merge_attn_states", "kv_cache_write", "ra_shard_len",
+           "ra_version", "prefill", "two_launch_prefill", "LIB_PATH", "EXPORTED_SYMBOLS",
+           "RA_REGION_CACHE", "RA_REGION_CURRENT"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn.so")
-EXPORTED_SYMBOLS = ("ring_attn_prefill", "kv_cache_write", "ra_shard_len", "ra_last_error",
-                    "ra_version")
+EXPORTED_SYMBOLS = ("ring_attn_prefill", "ring_attn_partial", "merge_attn_states",
+                    "kv_cache_write", "ra_shard_len", "ra_last_error", "ra_version")
 
 RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP = 0, 1, 2, 3
 RA_DTYPE_BF16, RA_DTYPE_FP32 = 0, 1
+RA_REGION_CACHE, RA_REGION_CURRENT = 1, 2
 
 
 class StripeLayout(ctypes.Structure):
@@ -59,6 +61,11 @@ def lib():
         L.ring_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i32, StripeLayout, vp, vp,
                                         ctypes.POINTER(Dims), vp]
         L.ring_attn_prefill.restype = ctypes.c_int
+        L.ring_attn_partial.argtypes = [vp, vp, vp, vp, vp, i64, i32, StripeLayout, i32, vp, vp,
+                                        ctypes.POINTER(Dims), vp]
+        L.ring_attn_partial.restype = ctypes.c_int
+        L.merge_attn_states.argtypes = [vp, vp, vp, vp, i32, vp, vp, ctypes.POINTER(Dims), vp]
+        L.merge_attn_states.restype = ctypes.c_int
         L.kv_cache_write.argtypes = [vp, vp, i32, vp, vp, i64, i32, StripeLayout,
                                      ctypes.POINTER(Dims), vp]
         L.kv_cache_write.restype = ctypes.c_int
@@ -112,6 +119,25 @@ def ring_attn_prefill(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_la
                                    _ptr(lse), ctypes.byref(dims), _stream(stream)))
 
 
+def ring_attn_partial(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout, regions,
+                      out, lse, dims, stream=None):
+    """Same arguments as the C entry point, with torch tensors for buffers."""
+    _check(lib().ring_attn_partial(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_cur),
+                                   _ptr(v_cur), cache_len, P, stripe_layout, regions, _ptr(out),
+                                   _ptr(lse), ctypes.byref(dims), _stream(stream)))
+
+
+def merge_attn_states(o1, lse1, o2, lse2, out, lse, dims, stream=None):
+    """Same arguments as the C entry point, with torch tensors for buffers
+    (the partials' dtype is taken from o1)."""
+    import torch
+    if o1.dtype != o2.dtype:
+        raise ValueError("o1 and o2 must have the same dtype")
+    parts = RA_DTYPE_FP32 if o1.dtype == torch.float32 else RA_DTYPE_BF16
+    _check(lib().merge_attn_states(_ptr(o1), _ptr(lse1), _ptr(o2), _ptr(lse2), parts, _ptr(out),
+                                   _ptr(lse), ctypes.byref(dims), _stream(stream)))
+
+
 def kv_cache_write(k_cur, v_cur, n_tokens, k_cache, v_cache, cache_len, P, stripe_layout, dims,
                    stream=None):
     """Same arguments as the C entry point, with torch tensors for buffers."""
@@ -152,3 +178,20 @@ def prefill(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, interleave=1, ring_
     ring_attn_prefill(q, k_cache, v_cache, k_cur, v_cur, cache_len, P,
                       StripeLayout(interleave, ring_start), out, lse, dims, stream)
     return out, lse
+
+
+def two_launch_prefill(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout, out, lse,
+                       dims, parts, stream=None):
+    """The removed two-launch variant: cache-only launch, current-only launch,
+    LSE merge.  ``parts`` = (o1, lse1, o2, lse2): caller-allocated buffers of
+    the partial outputs [C, NQ, HD] (bf16, the model dtype, or fp32) and
+    their fp32 LSEs [NQ, C]."""
+    import torch
+    o1, l1, o2, l2 = parts
+    d = Dims.from_buffer_copy(dims)
+    d.out_dtype = RA_DTYPE_FP32 if o1.dtype == torch.float32 else RA_DTYPE_BF16
+    ring_attn_partial(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
+                      RA_REGION_CACHE, o1, l1, d, stream)
+    ring_attn_partial(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
+                      RA_REGION_CURRENT, o2, l2, d, stream)
+    merge_attn_states(o1, l1, o2, l2, out, lse, dims, stream)

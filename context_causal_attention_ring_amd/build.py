@@ -10,7 +10,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libringattn.so")
-SOURCES = ["ringattn_api.hip", "ring_attn_fused.hip", "kv_cache_write.hip"]
+SOURCES = ["ringattn_api.hip", "ring_attn_fused.hip", "kv_cache_write.hip",
+           "merge_attn_states.hip"]
 ARCH = os.environ.get("RINGATTN_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -27,7 +27,20 @@ struct FusedParams {
   int32_t row_tiles;        // workgroups per KV head
   int32_t grid_real;        // row_tiles * NKV
   int32_t out_f32;
+  int32_t regions;          // 1: cache (ring) only, 2: current only, 3: both
   float scale_log2e;        // softmax scale * log2(e)
+};
+
+// Arguments of the log-sum-exp merge of two partial attentions.
+struct MergeParams {
+  const void* o1;           // [C, NQ, HD] bf16 | fp32 (parts_f32)
+  const float* lse1;        // fp32 [NQ, C]
+  const void* o2;
+  const float* lse2;
+  void* out;                // [C, NQ, HD] bf16 | fp32
+  float* lse;               // [NQ, C] or nullptr
+  int32_t q_rows, real_rows, nq, hd;
+  int32_t parts_f32, out_f32;
 };
 
 struct WriteParams {
@@ -49,5 +62,6 @@ constexpr int kBKV = 32;            // keys per KV tile
 
 hipError_t launch_fused(const FusedParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_kv_cache_write(const WriteParams& p, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 
 }  // namespace ra

@@ -309,8 +309,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     wg_min_pos = min(chunk_pos(t0), p.tail_pos);
     wg_max_pos = max(chunk_pos(p.head_rows - 1), chunk_pos(t1));
   }
-  const int n_ring = p.P * p.nb;
-  const int n_cur = wg_max_pos / kBKV + 1;
+  // A partial launch walks one region only (its result is merged later).
+  const int n_ring = (p.regions & 1) ? p.P * p.nb : 0;
+  const int n_cur = (p.regions & 2) ? wg_max_pos / kBKV + 1 : 0;
   const int T = n_ring + n_cur;
   const uint32_t rowstride = (uint32_t)p.nkv * D * 2;  // bytes between tokens
   const uint32_t tile_stride = kBKV * rowstride;       // bytes between tiles
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // The walk, one tile per call: shard visit k (ring order), tile b within
   // it, then the current tiles c; past the end, zero-size fetches (the
   // slot fills with zeros).  Everything here is wave-uniform.
-  int wk = p.nb > 0 ? 0 : p.P, wb = 0, wc = 0;
+  int wk = n_ring > 0 ? 0 : p.P, wb = 0, wc = 0;
   i32x4 vis_k, vis_v;
   int vis_len = 0;
   auto next_src = [&]() RA_INLINE {
@@ -773,7 +774,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     const float l_tot = lsum[rb] + __shfl_xor(lsum[rb], 32);
     const float l_norm = F32OUT ? lsum_q[rb] + __shfl_xor(lsum_q[rb], 32) : l_tot;
     if (!row_ok[rb]) continue;
-    const float inv = 1.f / l_norm;
+    // a row that saw no key (possible in a one-region launch) gets out = 0
+    // and lse = -inf (m = -inf, log2 0 = -inf)
+    const float inv = l_norm > 0.f ? 1.f / l_norm : 0.f;
     const int64_t obase = ((int64_t)token[rb] * p.nq + head[rb]) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {

@@ -92,10 +92,16 @@ int ra_shard_len(int64_t cache_len, int32_t P, ra_stripe_layout_t stripe_layout,
   return RA_OK;
 }
 
-int ring_attn_prefill(const void* q, const void* k_cache, const void* v_cache, const void* k_cur,
-                      const void* v_cur, int64_t cache_len, int32_t P,
-                      ra_stripe_layout_t stripe_layout, void* out, float* lse,
-                      const ra_dims_t* dims, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// ring_attn_prefill over the regions selected by `regions` (1: cache, 2:
+// current, 3: both).
+int prefill_regions(const void* q, const void* k_cache, const void* v_cache, const void* k_cur,
+                    const void* v_cur, int64_t cache_len, int32_t P,
+                    ra_stripe_layout_t stripe_layout, int32_t regions, void* out, float* lse,
+                    const ra_dims_t* dims, void* stream) {
   if (int rc = check_heads(dims)) return rc;
   if (int rc = check_layout(P, stripe_layout, cache_len)) return rc;
   const ra_dims_t& d = *dims;
@@ -211,6 +217,7 @@ int ring_attn_prefill(const void* q, const void* k_cache, const void* v_cache, c
   p.row_tiles = (int32_t)((rows_total + ra::kRowsPerWG - 1) / ra::kRowsPerWG);
   p.grid_real = p.row_tiles * NKV;
   p.out_f32 = d.out_dtype == RA_DTYPE_FP32;
+  p.regions = regions;
   const float scale = d.scale == 0.f ? 1.f / std::sqrt((float)HD) : d.scale;
   p.scale_log2e = scale * 1.4426950408889634f;
   if ((int64_t)p.nb * P >= lim31)
@@ -219,6 +226,91 @@ int ring_attn_prefill(const void* q, const void* k_cache, const void* v_cache, c
   hipError_t e = ra::launch_fused(p, HD, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(RA_ERR_HIP, "fused attention launch failed: %s", hipGetErrorString(e));
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ring_attn_prefill(const void* q, const void* k_cache, const void* v_cache, const void* k_cur,
+                      const void* v_cur, int64_t cache_len, int32_t P,
+                      ra_stripe_layout_t stripe_layout, void* out, float* lse,
+                      const ra_dims_t* dims, void* stream) {
+  return prefill_regions(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
+                         RA_REGION_CACHE | RA_REGION_CURRENT, out, lse, dims, stream);
+}
+
+int ring_attn_partial(const void* q, const void* k_cache, const void* v_cache, const void* k_cur,
+                      const void* v_cur, int64_t cache_len, int32_t P,
+                      ra_stripe_layout_t stripe_layout, int32_t regions, void* out, float* lse,
+                      const ra_dims_t* dims, void* stream) {
+  if (regions != RA_REGION_CACHE && regions != RA_REGION_CURRENT &&
+      regions != (RA_REGION_CACHE | RA_REGION_CURRENT))
+    return fail(RA_ERR_INVALID_ARG, "regions must be RA_REGION_CACHE, RA_REGION_CURRENT or both; "
+                "got %d", regions);
+  return prefill_regions(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout, regions,
+                         out, lse, dims, stream);
+}
+
+int merge_attn_states(const void* o1, const float* lse1, const void* o2, const float* lse2,
+                      int32_t parts_dtype, void* out, float* lse, const ra_dims_t* dims,
+                      void* stream) {
+  if (!dims) return fail(RA_ERR_INVALID_ARG, "dims must not be NULL");
+  const ra_dims_t& d = *dims;
+  if (d.num_q_heads < 1) return fail(RA_ERR_INVALID_ARG, "num_q_heads must be >= 1; got %d",
+                                     d.num_q_heads);
+  if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256)
+    return fail(RA_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256; got %d", d.head_dim);
+  if (d.q_rows < 0) return fail(RA_ERR_INVALID_ARG, "q_rows must be >= 0; got %d", d.q_rows);
+  if (d.real_rows < 0 || d.real_rows > d.q_rows)
+    return fail(RA_ERR_INVALID_ARG, "real_rows must be in [0, q_rows=%d]; got %d", d.q_rows,
+                d.real_rows);
+  if (d.out_dtype != RA_DTYPE_BF16 && d.out_dtype != RA_DTYPE_FP32)
+    return fail(RA_ERR_INVALID_ARG, "out_dtype must be RA_DTYPE_BF16 or RA_DTYPE_FP32; got %d",
+                d.out_dtype);
+  if (parts_dtype != RA_DTYPE_BF16 && parts_dtype != RA_DTYPE_FP32)
+    return fail(RA_ERR_INVALID_ARG, "parts_dtype must be RA_DTYPE_BF16 or RA_DTYPE_FP32; got %d",
+                parts_dtype);
+  if ((int64_t)d.q_rows * d.num_q_heads * d.head_dim >= ((int64_t)1 << 40))
+    return fail(RA_ERR_UNSUPPORTED, "q_rows * num_q_heads * head_dim is too large");
+  if (d.real_rows == 0) return RA_OK;
+  if (!o1 || !lse1 || !o2 || !lse2 || !out)
+    return fail(RA_ERR_INVALID_ARG, "o1, lse1, o2, lse2 and out must not be NULL");
+  const void* ptrs[] = {o1, lse1, o2, lse2, out, lse};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr))
+      return fail(RA_ERR_INVALID_ARG, "every tensor pointer must be 16-byte aligned");
+  const int64_t elems = (int64_t)d.q_rows * d.num_q_heads * d.head_dim;
+  const int64_t o_bytes = elems * (parts_dtype == RA_DTYPE_FP32 ? 4 : 2);
+  const int64_t l_bytes = (int64_t)d.q_rows * d.num_q_heads * 4;
+  const int64_t out_bytes = elems * (d.out_dtype == RA_DTYPE_FP32 ? 4 : 2);
+  struct R { const void* p; int64_t n; };
+  const R ins[] = {{o1, o_bytes}, {lse1, l_bytes}, {o2, o_bytes}, {lse2, l_bytes}};
+  for (const R& r : ins) {
+    if (overlaps(out, out_bytes, r.p, r.n))
+      return fail(RA_ERR_INVALID_ARG, "out overlaps an input tensor");
+    if (overlaps(lse, l_bytes, r.p, r.n))
+      return fail(RA_ERR_INVALID_ARG, "lse overlaps an input tensor");
+  }
+  if (overlaps(out, out_bytes, lse, l_bytes))
+    return fail(RA_ERR_INVALID_ARG, "out and lse overlap");
+  ra::MergeParams p{};
+  p.o1 = o1;
+  p.lse1 = lse1;
+  p.o2 = o2;
+  p.lse2 = lse2;
+  p.out = out;
+  p.lse = lse;
+  p.q_rows = d.q_rows;
+  p.real_rows = d.real_rows;
+  p.nq = d.num_q_heads;
+  p.hd = d.head_dim;
+  p.parts_f32 = parts_dtype == RA_DTYPE_FP32;
+  p.out_f32 = d.out_dtype == RA_DTYPE_FP32;
+  hipError_t e = ra::launch_merge(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(RA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   return RA_OK;
 }
 

@@ -53,6 +53,12 @@ typedef enum {
 
 typedef enum { RA_DTYPE_BF16 = 0, RA_DTYPE_FP32 = 1 } ra_dtype_t;
 
+/* Key regions of one launch (ring_attn_partial). */
+typedef enum {
+  RA_REGION_CACHE = 1,  /* the P cache shards (ring rounds) */
+  RA_REGION_CURRENT = 2 /* the causal current chunk */
+} ra_region_t;
+
 /* Stripe layout of the cache.  ring_start is the first shard visited; the
  * visit order is ring_start, ring_start-1, ... (mod P), the order in which a
  * rank sees its neighbours' shards arrive.  The result does not depend on it
@@ -122,6 +128,44 @@ int ring_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
                       const void* k_cur, const void* v_cur, int64_t cache_len,
                       int32_t P, ra_stripe_layout_t stripe_layout, void* out,
                       float* lse, const ra_dims_t* dims, void* stream);
+
+/*
+ * ring_attn_partial -- the same launch restricted to some key regions:
+ * regions = RA_REGION_CACHE (the cache-only ring launch), RA_REGION_CURRENT
+ * (the causal current phase alone) or both (= ring_attn_prefill).  The
+ * Summary section describes the removed two-launch variant (a cache-only
+ * ring launch plus an LSE merge); these calls and merge_attn_states rebuild
+ * it as the fused launch's comparator.  Arguments as ring_attn_prefill; a
+ * real row that sees no key in the chosen regions (a cache-only launch with
+ * cache_len == 0) gets out = 0 and lse = -inf.  For merging, keep the LSE.
+ */
+int ring_attn_partial(const void* q, const void* k_cache, const void* v_cache,
+                      const void* k_cur, const void* v_cur, int64_t cache_len,
+                      int32_t P, ra_stripe_layout_t stripe_layout, int32_t regions,
+                      void* out, float* lse, const ra_dims_t* dims, void* stream);
+
+/*
+ * merge_attn_states -- log-sum-exp merge of two partial attentions of the
+ * same rows over disjoint key sets (the merge of the removed two-launch
+ * variant, Summary section).  For every real row and query head:
+ *     lse = log(exp(lse1) + exp(lse2)),
+ *     out = exp(lse1 - lse) * o1 + exp(lse2 - lse) * o2,
+ * a part with lse = -inf weighted 0; out = 0 and lse = -inf when both are.
+ *
+ *   o1, o2      [C, NQ, HD] partial outputs, bf16 or fp32 (parts_dtype)
+ *   lse1, lse2  fp32 [NQ, C]       their natural-log LSEs
+ *   parts_dtype ra_dtype_t of o1 and o2 (the merge itself runs in fp32)
+ *   out         [C, NQ, HD] bf16 or fp32 (dims->out_dtype)
+ *   lse         fp32 [NQ, C] merged LSE, or NULL to skip
+ *   dims        uses num_q_heads, head_dim, q_rows, real_rows, out_dtype
+ *
+ * Pad rows (>= real_rows) are not written.  out and lse must not overlap an
+ * input.  Returns RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED or
+ * RA_ERR_HIP.
+ */
+int merge_attn_states(const void* o1, const float* lse1, const void* o2, const float* lse2,
+                      int32_t parts_dtype, void* out, float* lse, const ra_dims_t* dims,
+                      void* stream);
 
 /*
  * kv_cache_write -- strided write of the chunk's current K/V into the

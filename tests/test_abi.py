@@ -111,6 +111,54 @@ def test_prefill_no_real_rows_is_a_no_op():
     assert call_prefill(dims(real_rows=0)) == 0
 
 
+@pytest.mark.parametrize("regions", [0, 4, -1])
+def test_partial_rejects_bad_regions(regions):
+    q, kc, vc, kcur, vcur = FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000, FAKE + 0x4000000
+    rc = ra.lib().ring_attn_partial(q, kc, vc, kcur, vcur, 512, 2, ra.StripeLayout(1, 0), regions,
+                                    FAKE + 0x8000000, None, ctypes.byref(dims()), None)
+    assert rc == 1 and "regions" in ra.lib().ra_last_error().decode()
+
+
+def test_partial_validates_like_prefill():
+    q, kc, vc, kcur, vcur = FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000, FAKE + 0x4000000
+    rc = ra.lib().ring_attn_partial(q, kc, vc, kcur, vcur, 512, 0, ra.StripeLayout(1, 0),
+                                    ra.RA_REGION_CACHE, FAKE + 0x8000000, None,
+                                    ctypes.byref(dims()), None)
+    assert rc == 1 and "P must" in ra.lib().ra_last_error().decode()
+
+
+def call_merge(d, ptrs=None, out=FAKE + 0x8000000, lse=None, parts=1):
+    o1, l1, o2, l2 = ptrs or (FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000)
+    return ra.lib().merge_attn_states(o1, l1, o2, l2, parts, out, lse, ctypes.byref(d), None)
+
+
+BAD_MERGE = [
+    (dict(d=dims(head_dim=80)), 2, "head_dim"),
+    (dict(d=dims(num_q_heads=0)), 1, "num_q_heads"),
+    (dict(d=dims(real_rows=200)), 1, "real_rows"),
+    (dict(d=dims(out_dtype=3)), 1, "out_dtype"),
+    (dict(d=dims(), out=None), 1, "NULL"),
+    (dict(d=dims(), ptrs=(FAKE, 0, FAKE + 0x2000000, FAKE + 0x3000000)), 1, "NULL"),
+    (dict(d=dims(), ptrs=(FAKE + 4, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000)), 1,
+     "aligned"),
+    (dict(d=dims(), out=FAKE + 0x2000100), 1, "overlaps"),
+    (dict(d=dims(), lse=FAKE + 0x3000000), 1, "overlaps"),
+    (dict(d=dims(), lse=FAKE + 0x8000100), 1, "out and lse overlap"),
+    (dict(d=dims(), parts=2), 1, "parts_dtype"),
+    (dict(d=dims(), parts=0, out=FAKE + 0x2000100), 1, "overlaps"),   # bf16 o2 is 64 KiB
+]
+
+
+@pytest.mark.parametrize("kw,code,msg", BAD_MERGE)
+def test_merge_rejects_bad_arguments(kw, code, msg):
+    assert call_merge(**kw) == code
+    assert msg in ra.lib().ra_last_error().decode()
+
+
+def test_merge_no_real_rows_is_a_no_op():
+    assert call_merge(dims(real_rows=0)) == 0
+
+
 def call_write(d, n=128, cache_len=512, P=2, layout=(1, 0), ptrs=None):
     kcur, vcur, kc, vc = ptrs or (FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000)
     return ra.lib().kv_cache_write(kcur, vcur, n, kc, vc, cache_len, P, ra.StripeLayout(*layout),

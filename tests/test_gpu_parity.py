@@ -301,3 +301,99 @@ def test_rank_shares_reassemble_the_chunk():
         out, lse = run(case)
         assert (out.float() - fout[pos].float()).abs().max().item() <= TOL_BF16
         assert (lse - flse[:, pos]).abs().max().item() <= TOL_LSE
+
+
+# ---------------------------------------------------------------- two-launch comparator
+
+def run_partial(case, regions, out_fp32=True):
+    w, d = case.w, case.d
+    C, NQ, HD = w.q_rows, w.nq, w.hd
+    out = torch.full((C, NQ, HD), SENTINEL, device="cuda",
+                     dtype=torch.float32 if out_fp32 else torch.bfloat16)
+    lse = torch.full((NQ, C), SENTINEL, device="cuda", dtype=torch.float32)
+    dims = ra.make_dims(d["q"], d["k_cur"], w.shard_cap, real_rows=w.real_rows,
+                        head_rows=w.head_rows, scale=w.scale, out_fp32=out_fp32,
+                        head_pos=w.head_pos, tail_pos=w.tail_start)
+    print(f"[gpu] ring_attn_partial {w.name} regions={regions} C={C} L={w.cache_len}", flush=True)
+    ra.ring_attn_partial(d["q"], d["k_cache"], d["v_cache"], d["k_cur"], d["v_cur"], w.cache_len,
+                         w.P, ra.StripeLayout(w.interleave, 0), regions, out, lse, dims)
+    torch.cuda.synchronize()
+    return out, lse, dims
+
+
+PARTIAL_CASES = [workloads.CONFIGS["tiny"], FULL_CASES[1], FULL_CASES[2], RANK_CASES[2]]
+
+
+@pytest.mark.parametrize("parts_fp32", [True, False], ids=["fp32-parts", "bf16-parts"])
+@pytest.mark.parametrize("w", PARTIAL_CASES, ids=lambda w: w.name)
+def test_partials_and_merge(w, parts_fp32):
+    """Cache-only and current-only launches against the oracle's one-region
+    attention, and their LSE merge against the full definition."""
+    case = Case(w).to_device()
+    rows = list(range(w.real_rows))
+    t = case.t
+    args = (f64(t["q"]), f64(t["k_cache_tok"]), f64(t["v_cache_tok"]), f64(t["k_cur"]),
+            f64(t["v_cur"]), rows, w.scale)
+    o1, l1, dims = run_partial(case, ra.RA_REGION_CACHE, out_fp32=parts_fp32)
+    o2, l2, _ = run_partial(case, ra.RA_REGION_CURRENT, out_fp32=parts_fp32)
+    r1, rl1 = oracle.attention_rows(*args, current=False, positions=w.positions)
+    r2, rl2 = oracle.attention_rows(*args, cache=False, positions=w.positions)
+    # The partial outputs are fp32, but P.V takes bf16 probabilities: a
+    # current-only row sees as few as one or two keys, so nothing averages
+    # the 2^-9 rounding of a weight out (two keys with |v - v'| ~ 4 give up to
+    # ~4e-3).  The fp32-output bar of the configurations assumes rows that
+    # average over many cached keys; here the bf16 bar applies, and the LSE
+    # (an exact fp32 sum) keeps its own.
+    for o, l, r, rl in ((o1, l1, r1, rl1), (o2, l2, r2, rl2)):
+        o, l = o.cpu().double().numpy()[rows], l.cpu().double().numpy()[:, rows]
+        assert np.abs(o - r).max() <= TOL_BF16
+        fin = np.isfinite(rl)
+        assert (np.isneginf(l) == ~fin).all() and np.abs(l[fin] - rl[fin]).max() <= TOL_LSE
+    out = torch.full((w.q_rows, w.nq, w.hd), SENTINEL, device="cuda", dtype=torch.bfloat16)
+    lse = torch.full((w.nq, w.q_rows), SENTINEL, device="cuda", dtype=torch.float32)
+    ra.merge_attn_states(o1, l1, o2, l2, out, lse, ra.make_dims(
+        case.d["q"], case.d["k_cur"], w.shard_cap, real_rows=w.real_rows, head_rows=w.head_rows))
+    torch.cuda.synchronize()
+    compare(case, out.cpu(), lse.cpu(), rows, TOL_BF16)
+    check_pads_untouched(case, out.cpu(), lse.cpu())
+
+
+def test_cache_only_without_cache_is_empty():
+    """cache_len = 0: the cache-only launch sees no key: out 0, lse -inf; the
+    merge then reduces to the current part."""
+    w = small("no-cache-partial", cache_len=0, P=1, real_rows=100, head_rows=50, tail_rows=50)
+    case = Case(w).to_device()
+    o1, l1, _ = run_partial(case, ra.RA_REGION_CACHE)
+    r = w.real_rows
+    assert (o1[:r] == 0).all() and torch.isneginf(l1[:, :r]).all()
+    o2, l2, _ = run_partial(case, ra.RA_REGION_CURRENT)
+    out = torch.empty(w.q_rows, w.nq, w.hd, device="cuda", dtype=torch.float32)
+    lse = torch.empty(w.nq, w.q_rows, device="cuda", dtype=torch.float32)
+    ra.merge_attn_states(o1, l1, o2, l2, out, lse, ra.make_dims(
+        case.d["q"], case.d["k_cur"], w.shard_cap, real_rows=r, out_fp32=True))
+    torch.cuda.synchronize()
+    assert torch.equal(out[:r], o2[:r]) and torch.equal(lse[:, :r], l2[:, :r])
+
+
+def test_two_launch_matches_fused_at_32k():
+    """The two-launch comparator computes the fused launch's result."""
+    w = workloads.CONFIGS["32k"]
+    case = Case(w).to_device()
+    d = case.d
+    fused, flse = run(case)
+    out = torch.empty(w.q_rows, w.nq, w.hd, device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty(w.nq, w.q_rows, device="cuda", dtype=torch.float32)
+    bf = torch.bfloat16
+    parts = (torch.empty(w.q_rows, w.nq, w.hd, device="cuda", dtype=bf),
+             torch.empty(w.nq, w.q_rows, device="cuda"),
+             torch.empty(w.q_rows, w.nq, w.hd, device="cuda", dtype=bf),
+             torch.empty(w.nq, w.q_rows, device="cuda"))
+    dims = ra.make_dims(d["q"], d["k_cur"], w.shard_cap, real_rows=w.real_rows,
+                        head_rows=w.head_rows, scale=w.scale)
+    print("[gpu] two-launch 32k", flush=True)
+    ra.two_launch_prefill(d["q"], d["k_cache"], d["v_cache"], d["k_cur"], d["v_cur"], w.cache_len,
+                          w.P, ra.StripeLayout(1, 0), out, lse, dims, parts)
+    torch.cuda.synchronize()
+    assert (out.cpu().float() - fused.float()).abs().max().item() <= TOL_BF16
+    assert (lse.cpu() - flse).abs().max().item() <= TOL_LSE
+    compare(case, out.cpu(), lse.cpu(), sample_rows(w, 16, seed=3), TOL_BF16)
