@@ -138,6 +138,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="32k", help="workload name (default: 32k)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="cut each row's key walk into this many segments (partials merged by "
+                         "LSE); 0 (default): the library's suggestion for this GPU")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-two-launch", action="store_true",
                     help="skip timing the two-launch comparator (cache-only + current-only + merge)")
@@ -175,14 +178,20 @@ def main():
     with_write = True
     t, d, layout, dims = setup(w, dev)
     stream = torch.cuda.current_stream()
+    if args.splits == 0:
+        args.splits = ra.ra_split_suggest(dims, torch.cuda.get_device_properties(dev)
+                                          .multi_processor_count)
+    ws_bytes = ra.ra_split_workspace_bytes(dims, args.splits)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
 
     def step(ev=None):
         ra.kv_cache_write(d["k_cur"], d["v_cur"], w.n_cur_real, d["k_cache"], d["v_cache"],
                           w.cache_len, w.P, layout, dims)
         if ev is not None:
             ev[0].record(stream)
-        ra.ring_attn_prefill(d["q"], d["k_cache"], d["v_cache"], d["k_cur"], d["v_cur"],
-                             w.cache_len, w.P, layout, d["out"], d["lse"], dims)
+        ra.ring_attn_prefill_split(d["q"], d["k_cache"], d["v_cache"], d["k_cur"], d["v_cur"],
+                                   w.cache_len, w.P, layout, args.splits, ws, d["out"], d["lse"],
+                                   dims)
         if ev is not None:
             ev[1].record(stream)
 
@@ -267,7 +276,7 @@ def main():
                                f"kv_cache_write of the chunk",
                    "cache_len": w.cache_len, "P": w.P, "q_rows": w.q_rows,
                    "real_rows": w.real_rows, "nq": w.nq, "nkv": w.nkv, "hd": w.hd,
-                   "flop_per_step": F},
+                   "splits": args.splits, "flop_per_step": F},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "ms_per_chunk": round(ms_per_step, 4),
         "ms_per_step_cold_median": round(sorted(cold)[len(cold) // 2], 4),

@@ -15,11 +15,15 @@ import os
 __all__ = ["StripeLayout", "Dims", "RingAttnError", "lib", "ring_attn_prefill",
            "ring_attn_partial", "merge_attn_states", "kv_cache_write", "ra_shard_len",
            "ra_version", "prefill", "two_launch_prefill", "LIB_PATH", "EXPORTED_SYMBOLS",
-           "RA_REGION_CACHE", "RA_REGION_CURRENT"]
+           "RA_REGION_CACHE", "RA_REGION_CURRENT", "ring_attn_prefill_split",
+           "ra_split_workspace_bytes", "ra_split_suggest", "RA_MAX_SPLITS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn.so")
-EXPORTED_SYMBOLS = ("ring_attn_prefill", "ring_attn_partial", "merge_attn_states",
-                    "kv_cache_write", "ra_shard_len", "ra_last_error", "ra_version")
+EXPORTED_SYMBOLS = ("ring_attn_prefill", "ring_attn_prefill_split", "ra_split_workspace_bytes",
+                    "ra_split_suggest",
+                    "ring_attn_partial", "merge_attn_states", "kv_cache_write", "ra_shard_len",
+                    "ra_last_error", "ra_version")
+RA_MAX_SPLITS = 64
 
 RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP = 0, 1, 2, 3
 RA_DTYPE_BF16, RA_DTYPE_FP32 = 0, 1
@@ -61,6 +65,13 @@ def lib():
         L.ring_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i32, StripeLayout, vp, vp,
                                         ctypes.POINTER(Dims), vp]
         L.ring_attn_prefill.restype = ctypes.c_int
+        L.ring_attn_prefill_split.argtypes = [vp, vp, vp, vp, vp, i64, i32, StripeLayout, i32,
+                                              vp, i64, vp, vp, ctypes.POINTER(Dims), vp]
+        L.ring_attn_prefill_split.restype = ctypes.c_int
+        L.ra_split_workspace_bytes.argtypes = [ctypes.POINTER(Dims), i32, ctypes.POINTER(i64)]
+        L.ra_split_workspace_bytes.restype = ctypes.c_int
+        L.ra_split_suggest.argtypes = [ctypes.POINTER(Dims), i32, ctypes.POINTER(i32)]
+        L.ra_split_suggest.restype = ctypes.c_int
         L.ring_attn_partial.argtypes = [vp, vp, vp, vp, vp, i64, i32, StripeLayout, i32, vp, vp,
                                         ctypes.POINTER(Dims), vp]
         L.ring_attn_partial.restype = ctypes.c_int
@@ -117,6 +128,30 @@ def ring_attn_prefill(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_la
     _check(lib().ring_attn_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_cur),
                                    _ptr(v_cur), cache_len, P, stripe_layout, _ptr(out),
                                    _ptr(lse), ctypes.byref(dims), _stream(stream)))
+
+
+def ra_split_suggest(dims, num_cus):
+    s = ctypes.c_int32()
+    _check(lib().ra_split_suggest(ctypes.byref(dims), num_cus, ctypes.byref(s)))
+    return s.value
+
+
+def ra_split_workspace_bytes(dims, splits):
+    n = ctypes.c_int64()
+    _check(lib().ra_split_workspace_bytes(ctypes.byref(dims), splits, ctypes.byref(n)))
+    return n.value
+
+
+def ring_attn_prefill_split(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
+                            splits, workspace, out, lse, dims, stream=None):
+    """Same arguments as the C entry point, with torch tensors for buffers
+    (``workspace`` a device tensor of at least ra_split_workspace_bytes
+    bytes, or None when splits == 1)."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().ring_attn_prefill_split(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_cur),
+                                         _ptr(v_cur), cache_len, P, stripe_layout, splits,
+                                         _ptr(workspace), nbytes, _ptr(out), _ptr(lse),
+                                         ctypes.byref(dims), _stream(stream)))
 
 
 def ring_attn_partial(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout, regions,

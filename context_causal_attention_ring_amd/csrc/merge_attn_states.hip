@@ -64,7 +64,63 @@ __global__ __launch_bounds__(256) void merge_attn_states_kernel(MergeParams p) {
   }
 }
 
+// The same merge over the S partials of a split launch (segments of one
+// row's key walk): lse = log sum_s exp(lse_s), out = sum_s exp(lse_s - lse) o_s.
+__global__ __launch_bounds__(256) void merge_splits_kernel(MergeSplitsParams p) {
+  const int quads = p.hd / 4;
+  const int64_t total = (int64_t)p.real_rows * p.nq * quads;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t part_stride = (int64_t)p.q_rows * p.nq * p.hd;      // elements per partial
+  const int64_t lse_stride = (int64_t)p.nq * p.q_rows;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
+    const int64_t rh = idx / quads;
+    const int row = (int)(rh / p.nq), h = (int)(rh - (int64_t)row * p.nq);
+    const int64_t li = (int64_t)h * p.q_rows + row;
+    float m = -__builtin_inff();
+    for (int s = 0; s < p.splits; ++s) m = fmaxf(m, p.part_lse[s * lse_stride + li]);
+    const int64_t e = idx * 4;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    float lse = m;
+    if (m != -__builtin_inff()) {
+      float sum = 0.f;
+      for (int s = 0; s < p.splits; ++s) {
+        const float w = __expf(p.part_lse[s * lse_stride + li] - m);  // exp(-inf) = 0
+        sum += w;
+        f32x4 a;
+        if (p.parts_f32) {
+          a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.part_o) +
+                                              s * part_stride + e);
+        } else {
+          const bf16x4 x = *reinterpret_cast<const bf16x4*>(
+              static_cast<const uint16_t*>(p.part_o) + s * part_stride + e);
+          a = f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+        }
+        o = f32x4{o[0] + w * a[0], o[1] + w * a[1], o[2] + w * a[2], o[3] + w * a[3]};
+      }
+      const float inv = 1.f / sum;
+      o = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+      lse = m + __logf(sum);
+    }
+    if (p.out_f32) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + e) = o;
+    } else {
+      const bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+      *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.out) + e) = ob;
+    }
+    if (p.lse != nullptr && idx % quads == 0) p.lse[li] = lse;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_merge_splits(const MergeSplitsParams& p, hipStream_t stream) {
+  const int64_t total = (int64_t)p.real_rows * p.nq * (p.hd / 4);
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  const int grid = (int)(blocks < 16384 ? blocks : 16384);
+  hipLaunchKernelGGL(merge_splits_kernel, dim3(grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   const int64_t total = (int64_t)p.real_rows * p.nq * (p.hd / 4);

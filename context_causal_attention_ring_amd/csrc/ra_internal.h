@@ -24,8 +24,11 @@ struct FusedParams {
   int32_t q_rows, real_rows;
   int32_t head_rows;        // rows of the head piece; the rest is the tail piece
   int32_t head_pos, tail_pos;  // chunk positions of the first head / tail row
-  int32_t row_tiles;        // workgroups per KV head
-  int32_t grid_real;        // row_tiles * NKV
+  int32_t row_tiles;        // row tiles per KV head
+  int32_t splits;           // segments the tile walk of a row tile is cut into
+  int32_t seg_tiles;        // tiles per segment (the last one of a row tile may be shorter)
+  int64_t seg_out_stride;   // elements between the segments' partial outputs
+  int32_t grid_real;        // row_tiles * splits * NKV
   int32_t out_f32;
   int32_t regions;          // 1: cache (ring) only, 2: current only, 3: both
   float scale_log2e;        // softmax scale * log2(e)
@@ -63,5 +66,16 @@ constexpr int kBKV = 32;            // keys per KV tile
 hipError_t launch_fused(const FusedParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_kv_cache_write(const WriteParams& p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+
+// Arguments of the S-way merge of a split launch's partials.
+struct MergeSplitsParams {
+  const void* part_o;       // [S, C, NQ, HD] bf16 | fp32 (parts_f32)
+  const float* part_lse;    // [S, NQ, C]
+  void* out;                // [C, NQ, HD] bf16 | fp32
+  float* lse;               // [NQ, C] or nullptr
+  int32_t splits, q_rows, real_rows, nq, hd;
+  int32_t parts_f32, out_f32;
+};
+hipError_t launch_merge_splits(const MergeSplitsParams& p, hipStream_t stream);
 
 }  // namespace ra

@@ -259,8 +259,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   const int bid = blockIdx.x;
   const int logical = (bid & 7) * (nwg >> 3) + (bid >> 3);
   if (logical >= p.grid_real) return;
-  const int g = logical / p.row_tiles;
-  const int rt = p.row_tiles - 1 - (logical - g * p.row_tiles);  // long causal rows first
+  // (KV head, segment, row tile), row tiles innermost: the workgroups that
+  // share an XCD walk the same stretch of the same KV head.
+  const int per_g = p.splits * p.row_tiles;
+  const int g = logical / per_g;
+  const int seg = (logical - g * per_g) / p.row_tiles;
+  const int rt = p.row_tiles - 1 - (logical - g * per_g - seg * p.row_tiles);  // long rows first
   const int row0 = rt * kRowsPerWG;
 
   // This lane's rows, one per row block: query row `token` (head or tail
@@ -312,7 +316,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // A partial launch walks one region only (its result is merged later).
   const int n_ring = (p.regions & 1) ? p.P * p.nb : 0;
   const int n_cur = (p.regions & 2) ? wg_max_pos / kBKV + 1 : 0;
-  const int T = n_ring + n_cur;
+  // This workgroup's segment of the walk: virtual tiles [v0, v0 + T).
+  const int v0 = seg * p.seg_tiles;
+  const int T = max(0, min(n_ring + n_cur - v0, p.seg_tiles));
   const uint32_t rowstride = (uint32_t)p.nkv * D * 2;  // bytes between tokens
   const uint32_t tile_stride = kBKV * rowstride;       // bytes between tiles
   // current tokens past the last position any row here sees load as zeros
@@ -328,24 +334,35 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     int key0;         // current: chunk position of the tile's first key
     bool in_ring;
   };
-  // The walk, one tile per call: shard visit k (ring order), tile b within
-  // it, then the current tiles c; past the end, zero-size fetches (the
-  // slot fills with zeros).  Everything here is wave-uniform.
-  int wk = n_ring > 0 ? 0 : p.P, wb = 0, wc = 0;
+  // The walk, one tile per call, from virtual tile v0: shard visit k (ring
+  // order), tile b within it, then the current tiles c; past the end,
+  // zero-size fetches (the slot fills with zeros).  Everything here is
+  // wave-uniform.
+  int wk, wb = 0, wc = 0;
+  if (v0 < n_ring) {
+    wk = v0 / p.nb;
+    wb = v0 - wk * p.nb;
+  } else {
+    wk = p.P;
+    wc = v0 - n_ring;
+  }
   i32x4 vis_k, vis_v;
   int vis_len = 0;
+  auto load_visit = [&]() RA_INLINE {  // shard visit wk: its descriptors and length
+    if (wk < p.P) {
+      int sh = p.ring_start - wk;
+      sh += (sh < 0) ? p.P : 0;
+      vis_len = full_i + min(max((int)p.rem - sh * p.interleave, 0), p.interleave);
+      const int64_t base = ((int64_t)sh * p.shard_cap * p.nkv + g) * D;
+      const uint32_t bytes = (uint32_t)vis_len * rowstride;
+      vis_k = make_desc(p.k_cache + base, bytes);
+      vis_v = make_desc(p.v_cache + base, bytes);
+    }
+  };
+  load_visit();
   auto next_src = [&]() RA_INLINE {
     Src s;
     if (wk < p.P) {
-      if (wb == 0) {  // a new shard visit: its descriptors and length
-        int sh = p.ring_start - wk;
-        sh += (sh < 0) ? p.P : 0;
-        vis_len = full_i + min(max((int)p.rem - sh * p.interleave, 0), p.interleave);
-        const int64_t base = ((int64_t)sh * p.shard_cap * p.nkv + g) * D;
-        const uint32_t bytes = (uint32_t)vis_len * rowstride;
-        vis_k = make_desc(p.k_cache + base, bytes);
-        vis_v = make_desc(p.v_cache + base, bytes);
-      }
       s.kr = vis_k;
       s.vr = vis_v;
       s.off = (uint32_t)wb * tile_stride;
@@ -355,6 +372,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       if (++wb == p.nb) {
         wb = 0;
         ++wk;
+        load_visit();
       }
     } else {
       const bool live = wc < n_cur;
@@ -777,7 +795,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     // a row that saw no key (possible in a one-region launch) gets out = 0
     // and lse = -inf (m = -inf, log2 0 = -inf)
     const float inv = l_norm > 0.f ? 1.f / l_norm : 0.f;
-    const int64_t obase = ((int64_t)token[rb] * p.nq + head[rb]) * D;
+    // a split launch writes its segment's partial (out, lse)
+    const int64_t obase = seg * p.seg_out_stride + ((int64_t)token[rb] * p.nq + head[rb]) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -794,7 +813,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       }
     }
     if (h == 0 && p.lse != nullptr)
-      p.lse[(int64_t)head[rb] * p.q_rows + token[rb]] = (mlog[rb] + __log2f(l_tot)) * kLn2;
+      p.lse[((int64_t)seg * p.nq + head[rb]) * p.q_rows + token[rb]] =
+          (mlog[rb] + __log2f(l_tot)) * kLn2;
   }
 }
 

@@ -96,12 +96,27 @@ int ra_shard_len(int64_t cache_len, int32_t P, ra_stripe_layout_t stripe_layout,
 
 namespace {
 
+// Bytes of a split launch's workspace: the partial outputs [S, C, NQ, HD]
+// (in the output dtype) then the partial LSEs [S, NQ, C] fp32, both 256-byte
+// aligned.
+int64_t split_part_bytes(const ra_dims_t& d, int32_t splits) {
+  const int64_t o = (int64_t)splits * d.q_rows * d.num_q_heads * d.head_dim *
+                    (d.out_dtype == RA_DTYPE_FP32 ? 4 : 2);
+  return (o + 255) / 256 * 256;
+}
+int64_t split_workspace_bytes(const ra_dims_t& d, int32_t splits) {
+  const int64_t l = (int64_t)splits * d.num_q_heads * d.q_rows * 4;
+  return split_part_bytes(d, splits) + (l + 255) / 256 * 256;
+}
+
 // ring_attn_prefill over the regions selected by `regions` (1: cache, 2:
-// current, 3: both).
+// current, 3: both), with the walk of every row tile cut into `splits`
+// segments.  With splits > 1, out and lse receive the segments' partials
+// ([splits, C, NQ, HD] and [splits, NQ, C]).
 int prefill_regions(const void* q, const void* k_cache, const void* v_cache, const void* k_cur,
                     const void* v_cur, int64_t cache_len, int32_t P,
                     ra_stripe_layout_t stripe_layout, int32_t regions, void* out, float* lse,
-                    const ra_dims_t* dims, void* stream) {
+                    const ra_dims_t* dims, void* stream, int32_t splits = 1) {
   if (int rc = check_heads(dims)) return rc;
   if (int rc = check_layout(P, stripe_layout, cache_len)) return rc;
   const ra_dims_t& d = *dims;
@@ -175,8 +190,9 @@ int prefill_regions(const void* q, const void* k_cache, const void* v_cache, con
   const int64_t q_bytes = (int64_t)C * NQ * HD * 2;
   const int64_t cur_bytes = (int64_t)d.cur_len * NKV * HD * 2;
   const int64_t cache_bytes = (int64_t)P * d.shard_cap * NKV * HD * 2;
-  const int64_t out_bytes = (int64_t)C * NQ * HD * (d.out_dtype == RA_DTYPE_FP32 ? 4 : 2);
-  const int64_t lse_bytes = (int64_t)NQ * C * 4;
+  const int64_t out_bytes =
+      (int64_t)splits * C * NQ * HD * (d.out_dtype == RA_DTYPE_FP32 ? 4 : 2);
+  const int64_t lse_bytes = (int64_t)splits * NQ * C * 4;
   struct R { const void* p; int64_t n; };
   const R ins[] = {{q, q_bytes}, {k_cache, cache_len > 0 ? cache_bytes : 0},
                    {v_cache, cache_len > 0 ? cache_bytes : 0}, {k_cur, cur_bytes},
@@ -215,7 +231,17 @@ int prefill_regions(const void* q, const void* k_cache, const void* v_cache, con
   p.head_pos = d.head_pos;
   p.tail_pos = d.tail_pos;
   p.row_tiles = (int32_t)((rows_total + ra::kRowsPerWG - 1) / ra::kRowsPerWG);
-  p.grid_real = p.row_tiles * NKV;
+  p.splits = splits;
+  {
+    const int64_t t_max = ((regions & RA_REGION_CACHE) ? (int64_t)P * p.nb : 0) +
+                          ((regions & RA_REGION_CURRENT) ? max_pos / ra::kBKV + 1 : 0);
+    p.seg_tiles = splits == 1 ? (int32_t)(lim31 / 4) : (int32_t)((t_max + splits - 1) / splits);
+    if (p.seg_tiles < 1) p.seg_tiles = 1;
+  }
+  p.seg_out_stride = (int64_t)C * NQ * HD;
+  if ((int64_t)p.row_tiles * splits * NKV >= lim31 / 2)
+    return fail(RA_ERR_UNSUPPORTED, "too many workgroups");
+  p.grid_real = p.row_tiles * splits * NKV;
   p.out_f32 = d.out_dtype == RA_DTYPE_FP32;
   p.regions = regions;
   const float scale = d.scale == 0.f ? 1.f / std::sqrt((float)HD) : d.scale;
@@ -251,6 +277,97 @@ int ring_attn_partial(const void* q, const void* k_cache, const void* v_cache, c
                 "got %d", regions);
   return prefill_regions(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout, regions,
                          out, lse, dims, stream);
+}
+
+int ra_split_suggest(const ra_dims_t* dims, int32_t num_cus, int32_t* splits) {
+  if (int rc = check_heads(dims)) return rc;
+  if (num_cus < 1) return fail(RA_ERR_INVALID_ARG, "num_cus must be >= 1; got %d", num_cus);
+  if (!splits) return fail(RA_ERR_INVALID_ARG, "splits must not be NULL");
+  const ra_dims_t& d = *dims;
+  if (d.real_rows < 0 || d.real_rows > d.q_rows)
+    return fail(RA_ERR_INVALID_ARG, "real_rows must be in [0, q_rows=%d]; got %d", d.q_rows,
+                d.real_rows);
+  // One workgroup per CU at a time.  A launch of W workgroups takes
+  // ceil(W / CUs) waves; splitting multiplies W by S at a small cost per
+  // segment (its own Q load and partial output), so pick the S that best
+  // fills the last wave.
+  const int64_t group = d.num_q_heads / d.num_kv_heads;
+  const int64_t wgs = ((int64_t)d.real_rows * group + ra::kRowsPerWG - 1) / ra::kRowsPerWG *
+                      d.num_kv_heads;
+  int32_t best = 1;
+  double best_cost = 1e300;
+  for (int32_t s = 1; s <= 16 && wgs > 0; ++s) {
+    const double waves = (double)(wgs * s) / num_cus;
+    const double cost = std::ceil(waves) / waves * (1.0 + 0.02 * (s - 1));
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  *splits = best;
+  return RA_OK;
+}
+
+int ra_split_workspace_bytes(const ra_dims_t* dims, int32_t splits, int64_t* bytes) {
+  if (int rc = check_heads(dims)) return rc;
+  if (splits < 1 || splits > RA_MAX_SPLITS)
+    return fail(RA_ERR_INVALID_ARG, "splits must be in [1, %d]; got %d", RA_MAX_SPLITS, splits);
+  if (dims->q_rows < 0) return fail(RA_ERR_INVALID_ARG, "q_rows must be >= 0");
+  if (!bytes) return fail(RA_ERR_INVALID_ARG, "bytes must not be NULL");
+  *bytes = splits == 1 ? 0 : split_workspace_bytes(*dims, splits);
+  return RA_OK;
+}
+
+int ring_attn_prefill_split(const void* q, const void* k_cache, const void* v_cache,
+                            const void* k_cur, const void* v_cur, int64_t cache_len, int32_t P,
+                            ra_stripe_layout_t stripe_layout, int32_t splits, void* workspace,
+                            int64_t workspace_bytes, void* out, float* lse,
+                            const ra_dims_t* dims, void* stream) {
+  int64_t need = 0;
+  if (int rc = ra_split_workspace_bytes(dims, splits, &need)) return rc;
+  if (splits == 1)
+    return ring_attn_prefill(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
+                             out, lse, dims, stream);
+  const ra_dims_t& d = *dims;
+  if (!workspace) return fail(RA_ERR_INVALID_ARG, "workspace must not be NULL when splits > 1");
+  if (!aligned16(workspace))
+    return fail(RA_ERR_INVALID_ARG, "every tensor pointer must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(RA_ERR_INVALID_ARG, "workspace_bytes %lld is below the %lld bytes splits=%d needs",
+                (long long)workspace_bytes, (long long)need, splits);
+  // the workspace must not overlap the caller's tensors
+  const int64_t C = d.q_rows, NQ = d.num_q_heads, HD = d.head_dim, NKV = d.num_kv_heads;
+  struct R { const void* p; int64_t n; };
+  const R others[] = {{q, C * NQ * HD * 2}, {k_cache, cache_len > 0 ? (int64_t)P * d.shard_cap * NKV * HD * 2 : 0},
+                      {v_cache, cache_len > 0 ? (int64_t)P * d.shard_cap * NKV * HD * 2 : 0},
+                      {k_cur, (int64_t)d.cur_len * NKV * HD * 2}, {v_cur, (int64_t)d.cur_len * NKV * HD * 2},
+                      {out, C * NQ * HD * (d.out_dtype == RA_DTYPE_FP32 ? 4 : 2)}, {lse, NQ * C * 4}};
+  for (const R& r : others)
+    if (overlaps(workspace, need, r.p, r.n))
+      return fail(RA_ERR_INVALID_ARG, "workspace overlaps another tensor");
+  char* ws = static_cast<char*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(ws + split_part_bytes(d, splits));
+  if (int rc = prefill_regions(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
+                               RA_REGION_CACHE | RA_REGION_CURRENT, ws, part_lse, dims, stream,
+                               splits))
+    return rc;
+  if (d.real_rows == 0) return RA_OK;
+  if (!out) return fail(RA_ERR_INVALID_ARG, "out must not be NULL");
+  ra::MergeSplitsParams m{};
+  m.part_o = ws;
+  m.part_lse = part_lse;
+  m.out = out;
+  m.lse = lse;
+  m.splits = splits;
+  m.q_rows = d.q_rows;
+  m.real_rows = d.real_rows;
+  m.nq = d.num_q_heads;
+  m.hd = d.head_dim;
+  m.parts_f32 = m.out_f32 = d.out_dtype == RA_DTYPE_FP32;
+  hipError_t e = ra::launch_merge_splits(m, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(RA_ERR_HIP, "split merge launch failed: %s", hipGetErrorString(e));
+  return RA_OK;
 }
 
 int merge_attn_states(const void* o1, const float* lse1, const void* o2, const float* lse2,

@@ -129,6 +129,44 @@ int ring_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
                       int32_t P, ra_stripe_layout_t stripe_layout, void* out,
                       float* lse, const ra_dims_t* dims, void* stream);
 
+/* Largest number of segments a split launch may cut each row's walk into. */
+#define RA_MAX_SPLITS 64
+
+/*
+ * ring_attn_prefill_split -- ring_attn_prefill with the key walk of every
+ * row cut into `splits` consecutive segments (in walk order: shard visits,
+ * then current blocks) run by separate workgroups.  Each segment's
+ * (m, l, acc) is spilled to `workspace` as a normalised partial output and
+ * its LSE, and one log-sum-exp merge forms out and lse.  The pages name an
+ * HBM-spilled (m, l, acc) as the follow-up for long contexts (Performance
+ * section); on one GPU the split serves parallelism: a rank's share of a few
+ * hundred rows fills only a fraction of the chip unless its walk is split.
+ * Same arguments and result as ring_attn_prefill, plus
+ *   splits           1 .. RA_MAX_SPLITS (1: ring_attn_prefill itself)
+ *   workspace        caller-owned device scratch, 16-byte aligned, at least
+ *                    ra_split_workspace_bytes() bytes; overwritten; must not
+ *                    overlap any tensor argument; unused when splits == 1
+ *   workspace_bytes  its size
+ * The partials are in the output dtype, so a bf16 result is merged from
+ * bf16 partials (within the bf16 tolerance of the unsplit launch).
+ */
+int ring_attn_prefill_split(const void* q, const void* k_cache, const void* v_cache,
+                            const void* k_cur, const void* v_cur, int64_t cache_len,
+                            int32_t P, ra_stripe_layout_t stripe_layout, int32_t splits,
+                            void* workspace, int64_t workspace_bytes, void* out, float* lse,
+                            const ra_dims_t* dims, void* stream);
+
+/* Host-only: a split count for these dims on a GPU with num_cus compute
+ * units.  One workgroup (256 query rows of one KV head) runs per CU at a
+ * time; the count is chosen so that the workgroups of all segments fill the
+ * last wave best, charging each extra segment a small cost (1: no split).
+ * Writes *splits; no GPU involved. */
+int ra_split_suggest(const ra_dims_t* dims, int32_t num_cus, int32_t* splits);
+
+/* Host-only: workspace bytes ring_attn_prefill_split needs for these dims and
+ * splits (0 when splits == 1).  Writes *bytes; no GPU involved. */
+int ra_split_workspace_bytes(const ra_dims_t* dims, int32_t splits, int64_t* bytes);
+
 /*
  * ring_attn_partial -- the same launch restricted to some key regions:
  * regions = RA_REGION_CACHE (the cache-only ring launch), RA_REGION_CURRENT

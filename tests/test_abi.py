@@ -127,6 +127,44 @@ def test_partial_validates_like_prefill():
     assert rc == 1 and "P must" in ra.lib().ra_last_error().decode()
 
 
+def call_split(d, splits=4, ws=FAKE + 0x20000000, ws_bytes=1 << 30):
+    q, kc, vc, kcur, vcur = FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000, FAKE + 0x4000000
+    return ra.lib().ring_attn_prefill_split(q, kc, vc, kcur, vcur, 512, 2, ra.StripeLayout(1, 0),
+                                            splits, ws, ws_bytes, FAKE + 0x8000000, None,
+                                            ctypes.byref(d), None)
+
+
+def test_split_workspace_bytes():
+    d = dims()
+    assert ra.ra_split_workspace_bytes(d, 1) == 0
+    # partial outputs [S, C, NQ, HD] bf16 then LSEs [S, NQ, C] fp32, 256-byte aligned
+    assert ra.ra_split_workspace_bytes(d, 3) == 3 * 128 * 4 * 64 * 2 + 3 * 4 * 128 * 4
+    d32 = dims(out_dtype=1, q_rows=5, head_rows=5, real_rows=5, tail_pos=5)
+    assert ra.ra_split_workspace_bytes(d32, 2) == 2 * 5 * 4 * 64 * 4 + 256  # 160 B of LSE rounds up
+
+
+@pytest.mark.parametrize("rows,group,nkv,cus,expect", [
+    (4096, 16, 2, 256, 1),    # 512 workgroups: two full waves
+    (3548, 16, 2, 256, 4),    # 444 workgroups: 1.73 waves; x4 gives 6.94 waves
+    (512, 16, 2, 256, 4),     # a rank's 2 x 256 rows: 64 workgroups
+    (0, 16, 2, 256, 1),
+])
+def test_split_suggest(rows, group, nkv, cus, expect):
+    d = dims(num_q_heads=group * nkv, num_kv_heads=nkv, head_dim=256, q_rows=max(rows, 1),
+             head_rows=max(rows, 1), real_rows=rows, tail_pos=max(rows, 1), cur_len=max(rows, 1))
+    assert ra.ra_split_suggest(d, cus) == expect
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(splits=0), "splits"), (dict(splits=65), "splits"),
+    (dict(ws=None), "workspace must not be NULL"), (dict(ws=FAKE + 0x20000008), "aligned"),
+    (dict(ws_bytes=1000), "workspace_bytes"), (dict(ws=FAKE + 0x3000000), "overlaps"),
+])
+def test_split_rejects_bad_arguments(kw, msg):
+    assert call_split(dims(), **kw) == 1
+    assert msg in ra.lib().ra_last_error().decode()
+
+
 def call_merge(d, ptrs=None, out=FAKE + 0x8000000, lse=None, parts=1):
     o1, l1, o2, l2 = ptrs or (FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000)
     return ra.lib().merge_attn_states(o1, l1, o2, l2, parts, out, lse, ctypes.byref(d), None)

@@ -397,3 +397,57 @@ def test_two_launch_matches_fused_at_32k():
     assert (out.cpu().float() - fused.float()).abs().max().item() <= TOL_BF16
     assert (lse.cpu() - flse).abs().max().item() <= TOL_LSE
     compare(case, out.cpu(), lse.cpu(), sample_rows(w, 16, seed=3), TOL_BF16)
+
+
+# ---------------------------------------------------------------- split walk (partials in HBM)
+
+def run_split(case, splits, out_fp32=False):
+    w, d = case.w, case.d
+    C, NQ, HD = w.q_rows, w.nq, w.hd
+    out = torch.full((C, NQ, HD), SENTINEL, device="cuda",
+                     dtype=torch.float32 if out_fp32 else torch.bfloat16)
+    lse = torch.full((NQ, C), SENTINEL, device="cuda", dtype=torch.float32)
+    dims = ra.make_dims(d["q"], d["k_cur"], w.shard_cap, real_rows=w.real_rows,
+                        head_rows=w.head_rows, scale=w.scale, out_fp32=out_fp32,
+                        head_pos=w.head_pos, tail_pos=w.tail_start)
+    nbytes = ra.ra_split_workspace_bytes(dims, splits)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda") if nbytes else None
+    print(f"[gpu] ring_attn_prefill_split {w.name} splits={splits} C={C} L={w.cache_len}",
+          flush=True)
+    ra.ring_attn_prefill_split(d["q"], d["k_cache"], d["v_cache"], d["k_cur"], d["v_cur"],
+                               w.cache_len, w.P, ra.StripeLayout(w.interleave, 0), splits, ws,
+                               out, lse, dims)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+SPLIT_CASES = [(workloads.CONFIGS["tiny"], 3), (FULL_CASES[1], 2), (FULL_CASES[2], 7),
+               (RANK_CASES[2], 5), (small("split-nocache", cache_len=0, P=1), 4),
+               (small("split-many", cache_len=1000, P=3), 64)]
+
+
+@pytest.mark.parametrize("w,splits", SPLIT_CASES, ids=lambda x: getattr(x, "name", str(x)))
+def test_split_parity(w, splits):
+    """Segments of the walk (some empty for short rows) merged by LSE equal
+    the definition."""
+    case = Case(w).to_device()
+    out, lse = run_split(case, splits)
+    compare(case, out, lse, list(range(w.real_rows)), TOL_BF16)
+    check_pads_untouched(case, out, lse)
+
+
+def test_split_fp32_output():
+    w = FULL_CASES[1]
+    case = Case(w).to_device()
+    out, lse = run_split(case, 3, out_fp32=True)
+    compare(case, out, lse, list(range(w.real_rows)), TOL_F32)
+
+
+@pytest.mark.parametrize("name,splits", [("32k_rank3of8", 8), ("128k", 2)])
+def test_split_full_size(name, splits):
+    w = workloads.CONFIGS[name]
+    case = Case(w).to_device()
+    out, lse = run_split(case, splits)
+    rows = list(range(w.real_rows)) if w.q_rows <= 512 else sample_rows(w, 24, seed=w.seed)
+    compare(case, out, lse, rows, TOL_BF16)
+    check_pads_untouched(case, out, lse)
