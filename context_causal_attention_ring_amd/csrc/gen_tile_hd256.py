@@ -5,7 +5,10 @@ blocks; the accumulator O^T is 2 x 8 tiles of 32 x 32 fp32 in AGPRs).
 
 One block, in order:
   1. S^T = K Q^T of tile v: 32 MFMAs, K operands read from LDS two k-steps
-     ahead; the first two V operands of step 3 are read at the end.
+     ahead; the first two V operands of step 3 are read at the end.  Every
+     two k-steps one LDS-DMA copy of the next tiles is issued (8 per block:
+     the wave's rows of one K tile and one V tile), so the vector memory
+     pipe drains them in the MFMAs' shadow rather than stalling the wave.
   2. Only when the tile is cut by a key bound (a uniform flag): the scores
      of keys at or past each row's bound become -inf.
   3. O^T += V^T P^T of tile v-1: 32 MFMAs.  After each MFMA an even share
@@ -99,6 +102,17 @@ def vreads(t):
             for h in (0, 1)]
 
 
+def dma(i):
+    """One 16-byte-per-lane LDS-DMA copy of this block's share of the next
+    tiles: i < 4 copies rows of a K tile, i >= 4 rows of a V tile.  The lane
+    offset (swizzled chunk + the instruction's rows) is precomputed, the
+    scalar offset is the tile's first byte, M0 the LDS destination."""
+    kind, j = ("k", i) if i < 4 else ("v", i - 4)
+    return [f"s_add_u32 m0, %[m0b], %[m{kind}{j}]",
+            "s_nop 0",
+            f"buffer_load_dwordx4 %[d{kind}{j}], %[desc{kind}], %[off{kind}] offen lds"]
+
+
 def qk_part():
     out = ["s_nop 1", kread(0), kread(1)]
     for k in range(NKS):
@@ -116,6 +130,8 @@ def qk_part():
             c = "0" if k == 0 else stile(rb)
             out.append(f"v_mfma_f32_32x32x16_bf16 {stile(rb)}, {grp(kgroup(k))}, "
                        f"{qop(rb, k)}, {c}")
+        if k % 2 == 1:  # one copy of the next tiles per two k-steps
+            out += dma(k // 2)
     return out
 
 

@@ -179,6 +179,10 @@ __device__ __forceinline__ float wave_max_pair(float x) {
 // Q and the two probability buffers are pinned to v[52:211] (buffer PIN is
 // read, 1 - PIN written); scores live in v[212:243] and the operand ring in
 // v[244:255] (clobbered).
+// The block also issues this wave's LDS-DMA copies of one K tile (source
+// desck at tile offset offk, to LDS m0b + MK + 1024 j) and one V tile (descv,
+// offv, m0b + MV + 1024 j), j = 0..3, lane offsets dk[j] / dv[j]; the caller
+// waits for them (vmcnt) and synchronises before the slots are read.
 #include "tile_hd256.inc"
 #define RA_TILE_STATE_OPERANDS                                                                  \
   [acc00] "+a"(acc[0][0]), [acc01] "+a"(acc[0][1]), [acc02] "+a"(acc[0][2]),                   \
@@ -198,14 +202,22 @@ __device__ __forceinline__ float wave_max_pair(float x) {
       [ko1] "i"(KOFF + 256), [vo000] "i"(VOFF), [vo001] "i"(VOFF + 4096),                       \
       [vo010] "i"(VOFF + 256), [vo011] "i"(VOFF + 256 + 4096), [vo100] "i"(VOFF + 8192),        \
       [vo101] "i"(VOFF + 8192 + 4096), [vo110] "i"(VOFF + 8192 + 256),                          \
-      [vo111] "i"(VOFF + 8192 + 256 + 4096)
-template <uint32_t KOFF, uint32_t VOFF, int PIN>
+      [vo111] "i"(VOFF + 8192 + 256 + 4096), [desck] "s"(desck), [descv] "s"(descv),            \
+      [offk] "s"(offk), [offv] "s"(offv), [m0b] "s"(m0b), [dk0] "v"(dk[0]), [dk1] "v"(dk[1]),   \
+      [dk2] "v"(dk[2]), [dk3] "v"(dk[3]), [dv0] "v"(dv[0]), [dv1] "v"(dv[1]), [dv2] "v"(dv[2]), \
+      [dv3] "v"(dv[3]), [mk0] "i"(MK), [mk1] "i"(MK + 1024), [mk2] "i"(MK + 2048),              \
+      [mk3] "i"(MK + 3072), [mv0] "i"(MV), [mv1] "i"(MV + 1024), [mv2] "i"(MV + 2048),          \
+      [mv3] "i"(MV + 3072)
+template <uint32_t KOFF, uint32_t VOFF, int PIN, uint32_t MK, uint32_t MV>
 __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], const bf16x8 (&pin)[2][2],
                                            bf16x8 (&pout)[2][2], const bf16x8 (&q)[2][16],
                                            const uint32_t (&ka)[8], const uint32_t (&va)[4],
                                            float (&ml)[2], float (&l)[2], float (&al)[2],
                                            uint64_t& any, float c2, float tau, uint32_t mflag,
-                                           const int (&lim)[2]) {
+                                           const int (&lim)[2], const i32x4& desck,
+                                           const i32x4& descv, uint32_t offk, uint32_t offv,
+                                           uint32_t m0b, const uint32_t (&dk)[4],
+                                           const uint32_t (&dv)[4]) {
 #if defined(__HIP_DEVICE_COMPILE__)
   float a0, b0, a1, b1, th0, th1, r0, r1;
   uint64_t c0, c1;
@@ -214,12 +226,12 @@ __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], const bf16x8 (&p
     asm volatile(RA_TILE_HD256_ASM_P0
                  : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_PB_OUT1
                  : RA_TILE_HD256_Q_OPERANDS, RA_TILE_HD256_PB_IN0, RA_TILE_INPUT_OPERANDS
-                 : RA_TILE_HD256_CLOBBERS, "memory", "scc");
+                 : RA_TILE_HD256_CLOBBERS, "memory", "scc", "m0");
   } else {
     asm volatile(RA_TILE_HD256_ASM_P1
                  : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_PB_OUT0
                  : RA_TILE_HD256_Q_OPERANDS, RA_TILE_HD256_PB_IN1, RA_TILE_INPUT_OPERANDS
-                 : RA_TILE_HD256_CLOBBERS, "memory", "scc");
+                 : RA_TILE_HD256_CLOBBERS, "memory", "scc", "m0");
   }
 #endif
 }
@@ -240,9 +252,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   constexpr int DPW = kBKV * CPR / (64 * kWaves);  // DMA instructions per wave per tile
   static_assert(DPW >= 1 && DPW * 64 * kWaves == kBKV * CPR, "tile must split over the waves");
   constexpr bool ASM256 = D == 256 && NRB == 2 && NKB == 1;  // hand-scheduled tile body
-  // LDS: K slots 0, 1 then V slots 0, 1.  Slot offsets are compile-time
-  // constants because the tile loop is unrolled over the two slots.
-  constexpr int NSLOT = 2;
+  // LDS: K slots 0..3 then V slots 0..3 (tile t in slot t mod 4).  Slot
+  // offsets are compile-time constants because the tile loop is unrolled
+  // over the four slots.
+  constexpr int NSLOT = 4;
+  constexpr uint32_t VBASE = NSLOT * TILE_B;  // byte offset of the V slots
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * NSLOT * TILE];
   auto kslot = [&](int s) RA_INLINE { return lds + s * TILE; };
   auto vslot = [&](int s) RA_INLINE { return lds + (NSLOT + s) * TILE; };
@@ -417,6 +431,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
             s.off + (uint32_t)R * rowstride);
     }
   };
+  // The same copies as issued from the HD = 256 tile block: instruction i's
+  // rows move from the scalar into the lane offset (their sum, which the
+  // descriptor bounds, is unchanged), so only M0 and the tile offset vary.
+  uint32_t dk[DPW], dv[DPW];
+#pragma unroll
+  for (int i = 0; i < DPW; ++i) {
+    const int R = (wave * DPW + i) * RPI;
+    dk[i] = (dma_kbase ^ (uint32_t)(swz_k(R, CPR) << 4)) + (uint32_t)R * rowstride;
+    dv[i] = (dma_vbase ^ (uint32_t)(swz_v(R, CPR) << 4)) + (uint32_t)R * rowstride;
+  }
+  const uint32_t m0b = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(wave * DPW) * 1024u);
 
   // K operand reads: lane reads row 32 kb + lr, chunk 2s + h.  (2s + h) ^ swz
   // = 2s ^ x with x = h ^ swz < 16, so steps s and s + 8 differ by 256 bytes
@@ -440,12 +465,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     vbase = (uint32_t)(r * D * 2 + ((c0 ^ swz_v(r, CPR)) << 4) + 8 * (i16 & 1));
   }
   // Absolute LDS addresses for the hand-scheduled body: K reads ka[j] + slot,
-  // V reads va[db % 4] + slot (d blocks 4..7 add 256: bit 8 of vbase is 0).
+  // V reads va[db % 4] + slot, the V slots counted from VBASE (d blocks 4..7
+  // add 256: bit 8 of vbase is 0), so every offset stays below 64 KiB.
   uint32_t ka[8], va[4];
 #pragma unroll
   for (int j = 0; j < 8; ++j) ka[j] = lds0 + kx[j % NKX];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) va[d] = lds0 + (vbase ^ (uint32_t)(d << 6));
+  for (int d = 0; d < 4; ++d) va[d] = lds0 + VBASE + (vbase ^ (uint32_t)(d << 6));
 
   f32x16 acc[NRB][NDB];
 #pragma unroll
@@ -485,25 +511,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     for (int s = 0; s < NKS; ++s) {
       if (s + 2 < NKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, NRB, 0);                 // NRB MFMAs
-    }
-  };
-
-  // O^T += V^T P^T for one tile: every V operand feeds all row blocks.
-  auto pv = [&](const uint16_t* vt, const bf16x8 (&pb)[NRB][NPS]) RA_INLINE {
-#pragma unroll
-    for (int ks = 0; ks < NPS; ++ks) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const uint32_t o = (vbase ^ (uint32_t)(db << 6)) + ks * 16 * D * 2;
-        const i16x4 x1 = lds_read_tr(vt, o);
-        const i16x4 x2 = lds_read_tr(vt, o + 8 * D * 2);
-        const i16x8 x = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
-        const bf16x8 a = __builtin_bit_cast(bf16x8, x);
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-          acc[rb][db] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[rb][ks], acc[rb][db], 0, 0, 0);
-      }
     }
   };
 
@@ -665,21 +672,28 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     return any;
   };
 
-  // Iteration v reads K(v) and V(v-1) and fetches K(v+1) and V(v) into the
-  // slots that K(v-1) and V(v-2) left; tile v lives in slot v & 1.  The
-  // scores of tile v are computed, then its softmax is issued between the
-  // P.V MFMAs of tile v-1, which do not depend on it, then tile v's bf16
-  // packing; the rare rescale for tile v's max is applied at the top of the
-  // next iteration, between P.V(v-1) and P.V(v).  The accumulator is touched
-  // by no branch but the rescale.  Tile 0 runs the same body: its "previous"
-  // V slot is filled with zeros and the probabilities start at zero.
-  Src s0 = next_src(), s1 = next_src();  // tiles v, v+1
+  // Tiles run in pairs (2j, 2j+1); tile t's K and V live in slot t mod 4.
+  // Tile t computes its scores from K(t), then issues its softmax between the
+  // P.V MFMAs of tile t-1 (which read V(t-1)), then packs its probabilities;
+  // the rare rescale for tile t's max is applied before the P.V of tile t.
+  // At the start of pair j the copies for pair j+1 go out: K(2j+2), K(2j+3)
+  // and, one tile behind, V(2j+1), V(2j+2); the slots they fill were last
+  // read during pair j-1.  One wait and one barrier at the end of the pair
+  // make them visible, so copies are in flight for a whole pair and the
+  // workgroup synchronises every other tile.  Tiles at or past the end of
+  // this workgroup's walk (t >= T) are fully masked: pass T carries the P.V
+  // of the last tile.  Tile 0 runs the same body: its "previous" V slot is
+  // filled with zeros and the probabilities start at zero.
+  Src c0 = next_src(), c1 = next_src();  // tiles 2j, 2j+1
+  Src n0 = next_src(), n1 = next_src();  // tiles 2j+2, 2j+3
   {
-    Src zero = s0;
+    Src zero = c0;
     zero.vr = make_desc(p.v_cur, 0);  // a zero-size fetch: the slot fills with zeros
     zero.off = 0;
-    issue_k(s0, kslot(0));
-    issue_v(zero, vslot(1));
+    issue_k(c0, kslot(0));
+    issue_k(c1, kslot(1));
+    issue_v(zero, vslot(3));
+    issue_v(c0, vslot(0));
   }
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
@@ -720,18 +734,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       }
     }
   };
-  // One tile.  `last` runs the block once more after the walk: its score
-  // tile is fully masked, so only the P.V of the final tile has an effect.
-  auto body = [&](auto slot, bool last) RA_INLINE {
-    constexpr int SL = decltype(slot)::value;  // slot of tile v
+  // Tile v, in slot SL = v mod 4.
+  auto body = [&](auto slot, int v) RA_INLINE {
+    constexpr int SL = decltype(slot)::value;
     rescale();
-    if (!last) {
-      issue_k(s1, kslot(SL ^ 1));
-      issue_v(s0, vslot(SL));
+    if constexpr (SL % 2 == 0 && !ASM256) {  // start of a pair: the copies of the next pair
+      if (v + 2 <= T) {
+        issue_k(n0, kslot((SL + 2) % 4));
+        issue_k(n1, kslot((SL + 3) % 4));
+        issue_v(c1, vslot((SL + 1) % 4));
+        issue_v(n0, vslot((SL + 2) % 4));
+      }
     }
     int lim[NRB];
-    bool cut = bounds(s0, lim);
-    if (last) {
+    bool cut = bounds(SL % 2 == 0 ? c0 : c1, lim);
+    if (v >= T) {  // past the walk: every key masked
       cut = true;
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) lim[rb] = -kBKV;
@@ -740,50 +757,53 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) lim[rb] -= 4 * h;
       uint64_t anyf;
-      // tile v's probabilities go to buffer v & 1 = SL; tile v-1's are read
-      tile_hd256<SL * TILE_B, (NSLOT + (SL ^ 1)) * TILE_B, SL ^ 1>(
-          acc, pbuf[SL ^ 1], pbuf[SL], qreg, ka, va, mlog, lsum, alpha, anyf, c2, kTau<F32OUT>,
-          __builtin_amdgcn_readfirstlane(cut ? 1u : 0u), lim);
+      // tile v's probabilities go to buffer v & 1; tile v-1's are read
+      constexpr int PB = SL & 1;
+      // this block's copies: K of tile v + 2 and V of tile v + 1 (for an
+      // even v the sources are n0 and c1, for an odd v n1 and n0)
+      const Src& ks = SL % 2 == 0 ? n0 : n1;
+      const Src& vs = SL % 2 == 0 ? c1 : n0;
+      const i32x4 dkr = {__builtin_amdgcn_readfirstlane(ks.kr[0]),
+                         __builtin_amdgcn_readfirstlane(ks.kr[1]),
+                         __builtin_amdgcn_readfirstlane(ks.kr[2]),
+                         __builtin_amdgcn_readfirstlane(ks.kr[3])};
+      const i32x4 dvr = {__builtin_amdgcn_readfirstlane(vs.vr[0]),
+                         __builtin_amdgcn_readfirstlane(vs.vr[1]),
+                         __builtin_amdgcn_readfirstlane(vs.vr[2]),
+                         __builtin_amdgcn_readfirstlane(vs.vr[3])};
+      tile_hd256<SL * TILE_B, ((SL + 3) % 4) * TILE_B, PB ^ 1, ((SL + 2) % 4) * TILE_B,
+                 VBASE + ((SL + 1) % 4) * TILE_B>(
+          acc, pbuf[PB ^ 1], pbuf[PB], qreg, ka, va, mlog, lsum, alpha, anyf, c2, kTau<F32OUT>,
+          __builtin_amdgcn_readfirstlane(cut ? 1u : 0u), lim, dkr, dvr,
+          __builtin_amdgcn_readfirstlane(ks.off), __builtin_amdgcn_readfirstlane(vs.off), m0b,
+          dk, dv);
       any = anyf != 0;
-      sum_rounded(pbuf[SL]);
+      sum_rounded(pbuf[PB]);
     } else {
       f32x16 S[NRB][NKB];
       qk(kslot(SL), S);
       if (cut) mask(S, lim);
-      any = pv_softmax(vslot(SL ^ 1), S, alpha);
+      any = pv_softmax(vslot((SL + 3) % 4), S, alpha);
       pack(S, pb, alpha);
     }
-    if (!last) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(v+1), V(v) have landed
+    if constexpr (SL % 2 == 1) {  // end of a pair
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
       __syncthreads();
-      s0 = s1;
-      s1 = next_src();
+      c0 = n0;
+      c1 = n1;
+      n0 = next_src();
+      n1 = next_src();
     }
   };
-  if constexpr (ASM256) {
-    // Tiles 0 .. T-1, two per trip so that slot offsets are constants, and
-    // one more pass of the block, v = T, for the P.V of the last tile: its
-    // score tile is fully masked and the K slot holds the zero tile fetched
-    // past the walk.
-    for (int v = 0;;) {
-      body(std::integral_constant<int, 0>{}, v == T);
-      if (v++ == T) break;
-      body(std::integral_constant<int, 1>{}, v == T);
-      if (v++ == T) break;
-    }
-  } else {
-    for (int v = 0; v < T;) {
-      body(std::integral_constant<int, 0>{}, false);
-      if (++v == T) break;
-      body(std::integral_constant<int, 1>{}, false);
-      ++v;
-    }
-    // P.V of the last tile, T - 1, whose V is in slot (T - 1) & 1.
-    rescale();
-    if (T & 1)
-      pv(vslot(0), pb);
-    else
-      pv(vslot(1), pb);
+  // Tiles 0 .. T (pass T is the P.V of the last tile), four per trip so that
+  // the slot offsets are constants.
+  for (int v = 0;;) {
+    body(std::integral_constant<int, 0>{}, v);
+    body(std::integral_constant<int, 1>{}, v + 1);
+    if ((v += 2) > T) break;
+    body(std::integral_constant<int, 2>{}, v);
+    body(std::integral_constant<int, 3>{}, v + 1);
+    if ((v += 2) > T) break;
   }
 
   // Epilogue: out = acc / l, lse = ln 2 * (m + log2 l).
