@@ -806,6 +806,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     if ((v += 2) > T) break;
   }
 
+#if defined(__HIP_DEVICE_COMPILE__)
+  // the last P.V MFMAs (inline asm, unseen by the compiler's hazard checks)
+  // may still be writing acc, which is read below
+  if constexpr (ASM256) asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+#endif
+
   // Epilogue: out = acc / l, lse = ln 2 * (m + log2 l).
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {

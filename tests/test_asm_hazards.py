@@ -1,0 +1,89 @@
+"""Static checks of the compiled fused kernel around its hand-scheduled blocks.
+
+The HD = 256 tile block is one inline-asm statement, so the compiler's
+hazard checks do not see the MFMAs inside it.  An MFMA reads its A and B
+operands while it runs and writes its result at the end, so compiler code
+that follows a block must not, before those MFMAs are done, write a
+register the block's last two MFMAs read or touch a register they write.
+Inside the block this holds by construction; this test checks the
+compiler's side on the device assembly of the kernel as it is built: the
+first WINDOW instructions after every tile block do none of that unless two
+s_nop 15 (32 wait states) come first.
+"""
+import os
+import re
+import shutil
+import tempfile
+
+import pytest
+
+from context_causal_attention_ring_amd import build
+
+WINDOW = 40  # instructions; each takes at least a cycle, an MFMA's operands are read well within
+HAS_HIPCC = any(p and os.path.exists(p) for p in
+                (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"))
+
+
+def regs(text):
+    out = set()
+    for kind, a, b in re.findall(r"\b([va])\[(\d+):(\d+)\]", text):
+        out |= {(kind, r) for r in range(int(a), int(b) + 1)}
+    for kind, a in re.findall(r"\b([va])(\d+)\b", text):
+        out.add((kind, int(a)))
+    return out
+
+
+def tile_blocks(lines):
+    """(index after the block, last two MFMAs) for every big inline-asm block."""
+    start = None
+    for i, line in enumerate(lines):
+        if ";;#ASMSTART" in line:
+            start = i
+        elif ";;#ASMEND" in line and start is not None and i - start > 300:
+            mfma = [x.strip() for x in lines[start:i] if x.strip().startswith("v_mfma")]
+            yield i + 1, mfma[-2:]
+
+
+def hazards_after(lines, at, mfmas):
+    src, dst = set(), set()
+    for m in mfmas:
+        ops = m.split(None, 1)[1].split(", ")
+        dst |= regs(ops[0])
+        src |= regs(ops[1]) | regs(ops[2])
+    found, n, nops = [], 0, 0
+    for line in lines[at:at + 10 * WINDOW]:
+        ins = line.split(";")[0].strip()
+        if not ins or ins.startswith("."):
+            continue
+        n += 1
+        if n > WINDOW:
+            break
+        if ins.startswith("s_nop 15"):
+            nops += 1
+            if nops >= 2:
+                break
+        parts = ins.split(None, 1)
+        if len(parts) < 2:
+            continue
+        writes = regs(parts[1].split(",")[0]) if parts[0].startswith(
+            ("v_", "ds_read", "scratch_load", "global_load", "buffer_load")) else set()
+        if writes & (src | dst) or regs(parts[1]) & dst:
+            found.append(ins)
+    return found
+
+
+@pytest.mark.skipif(not HAS_HIPCC, reason="needs hipcc to assemble the kernel")
+def test_no_compiler_code_races_the_last_mfmas_of_a_tile_block():
+    with tempfile.TemporaryDirectory() as tmp:
+        asm = open(build.assemble(out=os.path.join(tmp, "fused.s"))).read()
+    kernels = re.findall(r"^(_ZN2ra\S*fused_kernelILi256\S*):", asm, re.M)
+    assert len(kernels) == 2  # bf16 and fp32 output
+    for name in kernels:
+        body = asm[asm.index(name + ":"):asm.index(".Lfunc_end", asm.index(name + ":"))]
+        lines = body.splitlines()
+        blocks = list(tile_blocks(lines))
+        assert len(blocks) == 4, name  # the loop is unrolled over the four slots
+        for at, mfmas in blocks:
+            assert len(mfmas) == 2
+            bad = hazards_after(lines, at, mfmas)
+            assert not bad, f"{name}: compiler code after a tile block: {bad}"
