@@ -3,28 +3,37 @@
 fused ring + current attention kernel at HD = 256 (a wave owns two 32-row
 blocks; the accumulator O^T is 2 x 8 tiles of 32 x 32 fp32 in AGPRs).
 
-One block, in order:
-  1. S^T = K Q^T of tile v: 32 MFMAs, K operands read from LDS two k-steps
-     ahead; the first two V operands of step 3 are read at the end.  Every
-     two k-steps one LDS-DMA copy of the next tiles is issued (8 per block:
-     the wave's rows of one K tile and one V tile), so the vector memory
-     pipe drains them in the MFMAs' shadow rather than stalling the wave.
+Tiles run in pairs (K and V slots t mod 4).  One block, in order:
+  1. S^T = K Q^T of tile v: 32 MFMAs.  The operands of the first two
+     k-steps were read into KPRE ahead (by the block before, or before the
+     loop), so the MFMAs start at once; the others are read from LDS two
+     k-steps ahead; the first two V operands of the P.V below are read at
+     the end.  Every two k-steps one LDS-DMA copy of the next tiles is
+     issued (8 per block: the wave's rows of one K tile and one V tile), so
+     the vector memory pipe drains them in the MFMAs' shadow rather than
+     stalling the wave.
   2. Only when the tile is cut by a key bound (a uniform flag): the scores
      of keys at or past each row's bound become -inf.
   3. O^T += V^T P^T of tile v-1: 32 MFMAs.  After each MFMA an even share
      (by issue cost) of tile v's online softmax is issued: the row max (two
      in-lane max3 chains, one v_permlane32_swap exchange with lane ^ 32),
      the lazy running-max vote, one FMA + exp2 per score, the row sums, and
-     the bf16 packing of the probabilities into the next P.V operands.
+     the bf16 packing of the probabilities into the next P.V operands.  The
+     even tile of a pair reads the odd tile's KPRE here.
+  4. Odd tile only (the end of the pair): wait for this wave's copies, meet
+     the other waves at the pair's barrier, and read the next pair's first
+     KPRE, left in flight: the scalar code between blocks hides its latency.
 The block is a single asm statement so that the softmax stays in the MFMAs'
 shadow (as separate C++ it was sunk past the tile's barrier).  The scores
-live in clobbered VGPRs v[212:243] and the operand ring in v[244:255]; both
+live in clobbered VGPRs v[204:235] and the operand ring in v[244:255]; both
 are dead outside the block.
 
 Hazards respected inside the block (gfx950): a VALU op never reads the
 result of a transcendental in the next slot; two wait states between a VALU
 write and v_permlane32_swap, and between an SGPR write and its use as a lane
 mask; MFMA results are read by VALU only after a later MFMA and an s_nop.
+Code after the block must leave the last MFMAs' operands alone for a while
+(the compiler cannot see them); a CPU test checks the compiled kernel.
 
 Usage: python gen_tile_hd256.py            (rewrites the .inc)
        python gen_tile_hd256.py --check    (exit 1 if the .inc is stale)
@@ -40,10 +49,12 @@ NDB = 8            # 32-wide d blocks of the output (HD / 32)
 NPS = 2            # 16-key steps of P.V per 32-key tile
 NT = NPS * NDB     # P.V steps; each issues one MFMA per row block
 NRB = 2            # 32-row blocks per wave
-Q0 = 52            # Q^T operands (pinned): row block rb, k-step k -> v[Q0 + 64 rb + 4 k : +3]
-PB = (180, 196)    # bf16 probabilities (pinned), two buffers: [rb][ks] -> v[PB + 8 rb + 4 ks : +3]
-S0 = 212           # scores (clobbered): row block rb, key slot i -> v[S0 + 16 rb + i]
+Q0 = 44            # Q^T operands (pinned): row block rb, k-step k -> v[Q0 + 64 rb + 4 k : +3]
+PB = (172, 188)    # bf16 probabilities (pinned), two buffers: [rb][ks] -> v[PB + 8 rb + 4 ks : +3]
+S0 = 204           # scores (clobbered): row block rb, key slot i -> v[S0 + 16 rb + i]
+KPRE = 236         # K operands of k-steps 0 and 1 (pinned), read ahead: v[KPRE + 4 k : +3]
 RING0 = 244        # operand ring (clobbered): group j -> v[RING0 + 4j : RING0 + 4j + 3]
+KPRE_STEP = 2      # P.V step of an even tile after which the odd tile's KPRE is read
 
 # Issue cost of one instruction, in units of one full-rate VALU op (measured
 # on gfx950: v_exp_f32 is half rate; SALU and s_nop issue in about a cycle).
@@ -102,34 +113,56 @@ def vreads(t):
             for h in (0, 1)]
 
 
+def kop(k):
+    """K operand of k-step k: the first two were read ahead into KPRE."""
+    return f"%[kp{k}]" if k < 2 else grp(kgroup(k))
+
+
+def kpre_reads():
+    """The first two K operands of the next tile, into KPRE (slot at kpo)."""
+    return [f"ds_read_b128 %[kp{k}], %[ka{k}] offset:%[kpo]" for k in range(2)]
+
+
 def dma(i):
     """One 16-byte-per-lane LDS-DMA copy of this block's share of the next
-    tiles: i < 4 copies rows of a K tile, i >= 4 rows of a V tile.  The lane
-    offset (swizzled chunk + the instruction's rows) is precomputed, the
-    scalar offset is the tile's first byte, M0 the LDS destination."""
+    tiles: i < 4 copies rows of a K tile, i >= 4 rows of a V tile.
+    Instruction j = 2 a + b of wave w moves rows 2 w + 8 a + 16 b and the
+    next one.  Rows 16 apart share their swizzle, so lane offset a
+    (precomputed, %[d<kind>a] / %[d<kind>b]) serves both b; the 16 rows of
+    b = 1 go into the scalar offset next to the tile's first byte.  M0
+    holds the LDS destination."""
     kind, j = ("k", i) if i < 4 else ("v", i - 4)
-    return [f"s_add_u32 m0, %[m0b], %[m{kind}{j}]",
-            "s_nop 0",
-            f"buffer_load_dwordx4 %[d{kind}{j}], %[desc{kind}], %[off{kind}] offen lds"]
+    a, b = j >> 1, j & 1
+    out = [f"s_add_u32 m0, %[m0b], %[m{kind}{j}]"]
+    soff = f"%[off{kind}]"
+    if b:
+        out.append(f"s_add_u32 %[st], {soff}, %[rs16]")
+        soff = "%[st]"
+    return out + ["s_nop 0",
+                  f"buffer_load_dwordx4 %[d{kind}{'b' if a else 'a'}], %[desc{kind}], {soff} "
+                  "offen lds"]
 
 
 def qk_part():
-    out = ["s_nop 1", kread(0), kread(1)]
+    # KPRE was read by the block before (or before the loop): wait for it.
+    out = ["s_nop 1", "s_waitcnt lgkmcnt(0)"]
     for k in range(NKS):
+        wait = None
         if k + 2 < NKS:
             out.append(kread(k + 2))
-            wait = 2
+            if k >= 2:
+                wait = 2
         elif k == NKS - 2:
             out += vreads(0)
             wait = 3
         else:
             out += vreads(1)
             wait = 4
-        out.append(f"s_waitcnt lgkmcnt({wait})")
+        if wait is not None:
+            out.append(f"s_waitcnt lgkmcnt({wait})")
         for rb in range(NRB):
             c = "0" if k == 0 else stile(rb)
-            out.append(f"v_mfma_f32_32x32x16_bf16 {stile(rb)}, {grp(kgroup(k))}, "
-                       f"{qop(rb, k)}, {c}")
+            out.append(f"v_mfma_f32_32x32x16_bf16 {stile(rb)}, {kop(k)}, {qop(rb, k)}, {c}")
         if k % 2 == 1:  # one copy of the next tiles per two k-steps
             out += dma(k // 2)
     return out
@@ -251,17 +284,32 @@ def assign(ops, ngaps):
 
 
 def pv_part(pin):
+    """P.V of the previous tile with this tile's softmax.  Variant P1 is the
+    even tile of a pair: it reads the odd tile's KPRE at step KPRE_STEP
+    (that K landed before the previous pair's barrier).  Variant P0, the odd
+    tile, ends the pair: wait for this wave's copies, meet the other waves
+    at the barrier, then read the next pair's first KPRE, left in flight
+    for the next block to wait on."""
+    even = pin == 1
     gaps, per = assign(softmax_ops(1 - pin), NRB * NT)
     out = []
     for t in range(NT):
         ks, db = divmod(t, NDB)
-        out.append(f"s_waitcnt lgkmcnt({2 if t + 1 < NT else 0})")
+        wait = 2 if t + 1 < NT else 0
+        if even and t == KPRE_STEP + 1:  # the KPRE reads went out before step t+1's V reads
+            wait = 4
+        out.append(f"s_waitcnt lgkmcnt({wait})")
         for rb in range(NRB):
             out.append(f"v_mfma_f32_32x32x16_bf16 %[acc{rb}{db}], {grp(vgroup(t))}, "
                        f"{pbop(pin, rb, ks)}, %[acc{rb}{db}]")
-            if rb == NRB - 1 and t + 2 < NT:
-                out += vreads(t + 2)
+            if rb == NRB - 1:
+                if even and t == KPRE_STEP:
+                    out += kpre_reads()
+                if t + 2 < NT:
+                    out += vreads(t + 2)
             out += gaps[NRB * t + rb]
+    if not even:
+        out += ["s_waitcnt vmcnt(0)", "s_barrier"] + kpre_reads()
     return out, per
 
 
@@ -296,6 +344,8 @@ def render():
         out += macro(f"RA_TILE_HD256_ASM_P{pin}", qk_part() + mask_part() + pv)
     q = [f'[q{rb}_{k}] "{{{qop(rb, k)}}}"(q[{rb}][{k}])' for rb in range(NRB) for k in range(NKS)]
     out += operand_list("RA_TILE_HD256_Q_OPERANDS", q)
+    kp = [f'[kp{k}] "+{{v[{KPRE + 4 * k}:{KPRE + 4 * k + 3}]}}"(kpre[{k}])' for k in range(2)]
+    out += operand_list("RA_TILE_HD256_KPRE_OPERANDS", kp)
     for buf in (0, 1):
         ins = [f'"{{{pbop(buf, rb, ks)}}}"(pin[{rb}][{ks}])' for rb in range(NRB)
                for ks in range(NPS)]
@@ -303,7 +353,7 @@ def render():
                 for ks in range(NPS)]
         out += operand_list(f"RA_TILE_HD256_PB_IN{buf}", ins)
         out += operand_list(f"RA_TILE_HD256_PB_OUT{buf}", outs)
-    clob = [f'"v{r}"' for r in range(S0, RING0 + 12)]
+    clob = [f'"v{r}"' for r in list(range(S0, S0 + 32)) + list(range(RING0, RING0 + 12))]
     out += operand_list("RA_TILE_HD256_CLOBBERS", clob)
     return "\n".join(out) + "\n"
 

@@ -164,25 +164,33 @@ __device__ __forceinline__ float wave_max_pair(float x) {
 
 // One 32-key tile at HD = 256 as a single instruction block (generated:
 // tile_hd256.inc; this binds its operands).  In order: S^T = K Q^T of tile
-// v from the K slot at KOFF; if mflag, scores of keys at or past each row's
-// bound (lim = bound - 4 h) become -inf; then O^T += V^T P^T of tile v-1
-// (V slot at VOFF, bf16 probabilities pin) with tile v's online softmax in
-// the MFMAs' shadow.  On return pout holds tile v's bf16 probabilities, ml
-// and l the updated running max (log2 units) and row sums, al the factor the
-// accumulator must be scaled by, and `any` is non-zero when some row of the
-// wave asked for that rescale (al == 1 for every row otherwise).
+// v from the K slot at KOFF, its first two operands already in kpre; if
+// mflag, scores of keys at or past each row's bound (lim = bound - 4 h)
+// become -inf; then O^T += V^T P^T of tile v-1 (V slot at VOFF, bf16
+// probabilities pin) with tile v's online softmax in the MFMAs' shadow.  The
+// even tile of a pair (PIN = 1) reads the odd tile's kpre from the K slot at
+// KPO during its P.V; the odd tile (PIN = 0) ends with the pair's wait for
+// this wave's copies and barrier, then reads the next pair's kpre (slot KPO)
+// and leaves it in flight (the next block waits for it).  On return pout
+// holds tile v's bf16 probabilities, ml and l the updated running max (log2
+// units) and row sums, al the factor the accumulator must be scaled by, and
+// `any` is non-zero when some row of the wave asked for that rescale (al ==
+// 1 for every row otherwise).
 //   ka[j]  LDS address of this lane's K row at chunk (2j + h) ^ swizzle;
 //          k-step s reads ka[s % 8] + KOFF + 256 (s / 8)
 //   va[d]  LDS address of this lane's transposed V read for d blocks d and
 //          d + 4; step (ks, db) reads va[db % 4] + VOFF + 8192 ks + 256
 //          (db / 4), and + 4096 for keys 8..15
-// Q and the two probability buffers are pinned to v[52:211] (buffer PIN is
-// read, 1 - PIN written); scores live in v[212:243] and the operand ring in
-// v[244:255] (clobbered).
+// Q and the two probability buffers are pinned to v[44:203] (buffer PIN is
+// read, 1 - PIN written) and kpre to v[236:243]; scores live in v[204:235]
+// and the operand ring in v[244:255] (clobbered).
 // The block also issues this wave's LDS-DMA copies of one K tile (source
-// desck at tile offset offk, to LDS m0b + MK + 1024 j) and one V tile (descv,
-// offv, m0b + MV + 1024 j), j = 0..3, lane offsets dk[j] / dv[j]; the caller
-// waits for them (vmcnt) and synchronises before the slots are read.
+// desck at tile offset offk, to the slot at MK) and one V tile (descv, offv,
+// to MV), four instructions each.  Instruction j = 2 a + b of wave w moves
+// rows 2 w + 8 a + 16 b and the next (to LDS m0b + 512 (8 a + 16 b) past the
+// slot); its lane offset is dl.ka / dl.kb (dl.va / dl.vb) for a = 0 / 1, and
+// b adds dl.rs16, 16 rows' stride, to the scalar offset.  The caller waits
+// for them (vmcnt) and synchronises before the slots are read.
 #include "tile_hd256.inc"
 #define RA_TILE_STATE_OPERANDS                                                                  \
   [acc00] "+a"(acc[0][0]), [acc01] "+a"(acc[0][1]), [acc02] "+a"(acc[0][2]),                   \
@@ -193,7 +201,8 @@ __device__ __forceinline__ float wave_max_pair(float x) {
       [acc17] "+a"(acc[1][7]), [ml0] "+v"(ml[0]), [ml1] "+v"(ml[1]), [l0] "+v"(l[0]),          \
       [l1] "+v"(l[1]), [al0] "=&v"(al[0]), [al1] "=&v"(al[1]), [any] "=&s"(any),              \
       [a0] "=&v"(a0), [b0] "=&v"(b0), [a1] "=&v"(a1), [b1] "=&v"(b1), [th0] "=&v"(th0),       \
-      [th1] "=&v"(th1), [r0] "=&v"(r0), [r1] "=&v"(r1), [c0] "=&s"(c0), [c1] "=&s"(c1)
+      [th1] "=&v"(th1), [r0] "=&v"(r0), [r1] "=&v"(r1), [c0] "=&s"(c0), [c1] "=&s"(c1),        \
+      [st] "=&s"(st), RA_TILE_HD256_KPRE_OPERANDS
 #define RA_TILE_INPUT_OPERANDS                                                                  \
   [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [ka2] "v"(ka[2]), [ka3] "v"(ka[3]), [ka4] "v"(ka[4]),    \
       [ka5] "v"(ka[5]), [ka6] "v"(ka[6]), [ka7] "v"(ka[7]), [va0] "v"(va[0]), [va1] "v"(va[1]), \
@@ -202,24 +211,29 @@ __device__ __forceinline__ float wave_max_pair(float x) {
       [ko1] "i"(KOFF + 256), [vo000] "i"(VOFF), [vo001] "i"(VOFF + 4096),                       \
       [vo010] "i"(VOFF + 256), [vo011] "i"(VOFF + 256 + 4096), [vo100] "i"(VOFF + 8192),        \
       [vo101] "i"(VOFF + 8192 + 4096), [vo110] "i"(VOFF + 8192 + 256),                          \
-      [vo111] "i"(VOFF + 8192 + 256 + 4096), [desck] "s"(desck), [descv] "s"(descv),            \
-      [offk] "s"(offk), [offv] "s"(offv), [m0b] "s"(m0b), [dk0] "v"(dk[0]), [dk1] "v"(dk[1]),   \
-      [dk2] "v"(dk[2]), [dk3] "v"(dk[3]), [dv0] "v"(dv[0]), [dv1] "v"(dv[1]), [dv2] "v"(dv[2]), \
-      [dv3] "v"(dv[3]), [mk0] "i"(MK), [mk1] "i"(MK + 1024), [mk2] "i"(MK + 2048),              \
-      [mk3] "i"(MK + 3072), [mv0] "i"(MV), [mv1] "i"(MV + 1024), [mv2] "i"(MV + 2048),          \
-      [mv3] "i"(MV + 3072)
-template <uint32_t KOFF, uint32_t VOFF, int PIN, uint32_t MK, uint32_t MV>
+      [vo111] "i"(VOFF + 8192 + 256 + 4096), [kpo] "i"(KPO), [desck] "s"(desck),                \
+      [descv] "s"(descv), [offk] "s"(offk), [offv] "s"(offv), [m0b] "s"(m0b),                   \
+      [rs16] "s"(dl.rs16), [dka] "v"(dl.ka), [dkb] "v"(dl.kb), [dva] "v"(dl.va),                \
+      [dvb] "v"(dl.vb), [mk0] "i"(MK), [mk1] "i"(MK + 8192), [mk2] "i"(MK + 4096),              \
+      [mk3] "i"(MK + 12288), [mv0] "i"(MV), [mv1] "i"(MV + 8192), [mv2] "i"(MV + 4096),         \
+      [mv3] "i"(MV + 12288)
+struct CopyLanes {    // a lane's offsets for the block's LDS-DMA copies (see below)
+  uint32_t ka, kb, va, vb;
+  uint32_t rs16;      // 16 rows' stride in bytes (uniform)
+};
+template <uint32_t KOFF, uint32_t VOFF, int PIN, uint32_t MK, uint32_t MV, uint32_t KPO>
 __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], const bf16x8 (&pin)[2][2],
                                            bf16x8 (&pout)[2][2], const bf16x8 (&q)[2][16],
-                                           const uint32_t (&ka)[8], const uint32_t (&va)[4],
+                                           bf16x8 (&kpre)[2], const uint32_t (&ka)[8],
+                                           const uint32_t (&va)[4],
                                            float (&ml)[2], float (&l)[2], float (&al)[2],
                                            uint64_t& any, float c2, float tau, uint32_t mflag,
                                            const int (&lim)[2], const i32x4& desck,
                                            const i32x4& descv, uint32_t offk, uint32_t offv,
-                                           uint32_t m0b, const uint32_t (&dk)[4],
-                                           const uint32_t (&dv)[4]) {
+                                           uint32_t m0b, const CopyLanes& dl) {
 #if defined(__HIP_DEVICE_COMPILE__)
   float a0, b0, a1, b1, th0, th1, r0, r1;
+  uint32_t st;
   uint64_t c0, c1;
   const float ninf = kNegInf;
   if constexpr (PIN == 0) {
@@ -431,17 +445,22 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
             s.off + (uint32_t)R * rowstride);
     }
   };
-  // The same copies as issued from the HD = 256 tile block: instruction i's
-  // rows move from the scalar into the lane offset (their sum, which the
-  // descriptor bounds, is unchanged), so only M0 and the tile offset vary.
-  uint32_t dk[DPW], dv[DPW];
-#pragma unroll
-  for (int i = 0; i < DPW; ++i) {
-    const int R = (wave * DPW + i) * RPI;
-    dk[i] = (dma_kbase ^ (uint32_t)(swz_k(R, CPR) << 4)) + (uint32_t)R * rowstride;
-    dv[i] = (dma_vbase ^ (uint32_t)(swz_v(R, CPR) << 4)) + (uint32_t)R * rowstride;
+  // The copies issued from the HD = 256 tile block split the rows another
+  // way: instruction 2 a + b of wave w moves rows R = 2 w + 8 a + 16 b and
+  // R + 1.  Rows 16 apart share their swizzle, so two lane offsets per
+  // operand (a = 0, 1) carry the swizzle and R's rows for b = 0; the 16 more
+  // rows of b = 1 go into the scalar offset (the sum, which the descriptor
+  // bounds, is the same).
+  CopyLanes dl;
+  {
+    const int r0 = 2 * wave, r1 = 2 * wave + 8;
+    dl.ka = (dma_kbase ^ (uint32_t)(swz_k(r0, CPR) << 4)) + (uint32_t)r0 * rowstride;
+    dl.kb = (dma_kbase ^ (uint32_t)(swz_k(r1, CPR) << 4)) + (uint32_t)r1 * rowstride;
+    dl.va = (dma_vbase ^ (uint32_t)(swz_v(r0, CPR) << 4)) + (uint32_t)r0 * rowstride;
+    dl.vb = (dma_vbase ^ (uint32_t)(swz_v(r1, CPR) << 4)) + (uint32_t)r1 * rowstride;
+    dl.rs16 = 16 * rowstride;
   }
-  const uint32_t m0b = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(wave * DPW) * 1024u);
+  const uint32_t m0b = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)wave * 2u * D * 2u);
 
   // K operand reads: lane reads row 32 kb + lr, chunk 2s + h.  (2s + h) ^ swz
   // = 2s ^ x with x = h ^ swz < 16, so steps s and s + 8 differ by 256 bytes
@@ -701,6 +720,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     for (int ks = 0; ks < NPS; ++ks) pb[rb][ks] = pbuf[0][rb][ks] = pbuf[1][rb][ks] = bf16x8{};
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
   __syncthreads();
+  // HD = 256: the first two K operands of tile 0 (each block reads them for
+  // the tile after it).
+  bf16x8 kpre[2];
+#if defined(__HIP_DEVICE_COMPILE__)
+  if constexpr (ASM256)
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "={v[236:239]}"(kpre[0]), "={v[240:243]}"(kpre[1])
+                 : "v"(ka[0]), "v"(ka[1])
+                 : "memory");
+#endif
 
   bool any = false;       // the previous tile asked for a rescale ...
   float alpha[NRB];       // ... by these factors
@@ -772,11 +801,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
                          __builtin_amdgcn_readfirstlane(vs.vr[2]),
                          __builtin_amdgcn_readfirstlane(vs.vr[3])};
       tile_hd256<SL * TILE_B, ((SL + 3) % 4) * TILE_B, PB ^ 1, ((SL + 2) % 4) * TILE_B,
-                 VBASE + ((SL + 1) % 4) * TILE_B>(
-          acc, pbuf[PB ^ 1], pbuf[PB], qreg, ka, va, mlog, lsum, alpha, anyf, c2, kTau<F32OUT>,
-          __builtin_amdgcn_readfirstlane(cut ? 1u : 0u), lim, dkr, dvr,
+                 VBASE + ((SL + 1) % 4) * TILE_B, ((SL + 1) % 4) * TILE_B>(
+          acc, pbuf[PB ^ 1], pbuf[PB], qreg, kpre, ka, va, mlog, lsum, alpha, anyf, c2,
+          kTau<F32OUT>, __builtin_amdgcn_readfirstlane(cut ? 1u : 0u), lim, dkr, dvr,
           __builtin_amdgcn_readfirstlane(ks.off), __builtin_amdgcn_readfirstlane(vs.off), m0b,
-          dk, dv);
+          dl);
       any = anyf != 0;
       sum_rounded(pbuf[PB]);
     } else {
@@ -787,8 +816,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       pack(S, pb, alpha);
     }
     if constexpr (SL % 2 == 1) {  // end of a pair
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
-      __syncthreads();
+      if constexpr (!ASM256) {  // (the HD = 256 block waits and synchronises itself)
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+        __syncthreads();
+      }
       c0 = n0;
       c1 = n1;
       n0 = next_src();
@@ -809,7 +840,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
 #if defined(__HIP_DEVICE_COMPILE__)
   // the last P.V MFMAs (inline asm, unseen by the compiler's hazard checks)
   // may still be writing acc, which is read below
-  if constexpr (ASM256) asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+  // (and the last block's KPRE reads may still be landing)
+  if constexpr (ASM256) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15" ::: "memory");
 #endif
 
   // Epilogue: out = acc / l, lse = ln 2 * (m + log2 l).

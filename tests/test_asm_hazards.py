@@ -8,8 +8,11 @@ register the block's last two MFMAs read or touch a register they write.
 Inside the block this holds by construction; this test checks the
 compiler's side on the device assembly of the kernel as it is built: the
 first WINDOW instructions after every tile block do none of that unless two
-s_nop 15 (32 wait states) come first.
+s_nop 15 (32 wait states) come first.  A block may also leave LDS reads of
+the next tile's first K operands (KPRE) in flight, so no compiler
+instruction between two blocks may touch those registers.
 """
+import importlib.util
 import os
 import re
 import shutil
@@ -18,6 +21,12 @@ import tempfile
 import pytest
 
 from context_causal_attention_ring_amd import build
+
+_spec = importlib.util.spec_from_file_location("gen_tile_hd256",
+                                               os.path.join(build.CSRC, "gen_tile_hd256.py"))
+gen = importlib.util.module_from_spec(_spec)
+_spec.loader.exec_module(gen)
+KPRE = {("v", r) for r in range(gen.KPRE, gen.KPRE + 8)}
 
 WINDOW = 40  # instructions; each takes at least a cycle, an MFMA's operands are read well within
 HAS_HIPCC = any(p and os.path.exists(p) for p in
@@ -34,14 +43,28 @@ def regs(text):
 
 
 def tile_blocks(lines):
-    """(index after the block, last two MFMAs) for every big inline-asm block."""
+    """(start, index after the block, last two MFMAs) for every big inline-asm block."""
     start = None
     for i, line in enumerate(lines):
         if ";;#ASMSTART" in line:
             start = i
         elif ";;#ASMEND" in line and start is not None and i - start > 300:
             mfma = [x.strip() for x in lines[start:i] if x.strip().startswith("v_mfma")]
-            yield i + 1, mfma[-2:]
+            yield start, i + 1, mfma[-2:]
+
+
+def compiler_code(lines):
+    """Instructions outside inline asm (labels and comments dropped)."""
+    inside = False
+    for line in lines:
+        if ";;#ASMSTART" in line:
+            inside = True
+        elif ";;#ASMEND" in line:
+            inside = False
+        elif not inside:
+            ins = line.split(";")[0].strip()
+            if ins and not ins.startswith(".") and not ins.endswith(":"):
+                yield ins
 
 
 def hazards_after(lines, at, mfmas):
@@ -83,7 +106,11 @@ def test_no_compiler_code_races_the_last_mfmas_of_a_tile_block():
         lines = body.splitlines()
         blocks = list(tile_blocks(lines))
         assert len(blocks) == 4, name  # the loop is unrolled over the four slots
-        for at, mfmas in blocks:
+        for _, at, mfmas in blocks:
             assert len(mfmas) == 2
             bad = hazards_after(lines, at, mfmas)
             assert not bad, f"{name}: compiler code after a tile block: {bad}"
+        # from the first block to the last (the tile loop), KPRE is the blocks' own
+        first, last = blocks[0][0], blocks[-1][1]
+        touch = [ins for ins in compiler_code(lines[first:last]) if regs(ins) & KPRE]
+        assert not touch, f"{name}: compiler code touches the KPRE registers: {touch[:4]}"
