@@ -282,17 +282,28 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   const int h = lane >> 5;   // lane half: keys / d interleave of the MFMA layouts
   const int lr = lane & 31;  // this lane's row within each 32-row block
 
-  // XCD-aware workgroup order (grid is a multiple of 8).
+  // XCD-aware workgroup order (grid is a multiple of 8): workgroup bid runs
+  // on XCD bid % 8, so XCD x takes the logical items [x, x + 1) * nwg / 8.
   const int nwg = gridDim.x;
   const int bid = blockIdx.x;
-  const int logical = (bid & 7) * (nwg >> 3) + (bid >> 3);
+  const int per_xcd = nwg >> 3;
+  const int logical = (bid & 7) * per_xcd + (bid >> 3);
   if (logical >= p.grid_real) return;
-  // (KV head, segment, row tile), row tiles innermost: the workgroups that
-  // share an XCD walk the same stretch of the same KV head.
+  // Items are (KV head, segment, row tile), row tiles innermost and the
+  // longest causal rows first, so the XCDs of one KV head walk its K/V (L2
+  // reuse).  When a KV head spans n_x whole XCDs its items are dealt to them
+  // in turn (item i to XCD i mod n_x), so that every XCD gets long and short
+  // rows alike and runs its longest first: a contiguous share would give one
+  // XCD all the longest rows and end the launch late.
   const int per_g = p.splits * p.row_tiles;
   const int g = logical / per_g;
-  const int seg = (logical - g * per_g) / p.row_tiles;
-  const int rt = p.row_tiles - 1 - (logical - g * per_g - seg * p.row_tiles);  // long rows first
+  int r = logical - g * per_g;
+  if (per_g % per_xcd == 0) {
+    const int n_x = per_g / per_xcd;
+    r = (r % per_xcd) * n_x + r / per_xcd;
+  }
+  const int seg = r / p.row_tiles;
+  const int rt = p.row_tiles - 1 - (r - seg * p.row_tiles);  // long rows first
   const int row0 = rt * kRowsPerWG;
 
   // This lane's rows, one per row block: query row `token` (head or tail
