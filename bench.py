@@ -54,6 +54,26 @@ FUSED_SOURCES = [os.path.join(ROOT, "context_causal_attention_ring_amd", "csrc",
                  for f in ("ring_attn_fused.hip", "tile_hd256.inc")]
 
 
+def peak_sclk_mhz():
+    """The device's peak engine clock as HIP reports it (attribute 5, kHz), or
+    None if the runtime cannot be asked.  The clock under load is lower."""
+    import ctypes
+    import context_causal_attention_ring_amd as ra
+    try:  # the HIP runtime the library itself is linked against
+        get = ctypes.CDLL(ra.LIB_PATH).hipDeviceGetAttribute
+    except (OSError, AttributeError):
+        return None
+    val = ctypes.c_int(0)
+    if get(ctypes.byref(val), 5, torch_device_index()) == 0 and val.value > 0:
+        return round(val.value / 1000)
+    return None
+
+
+def torch_device_index():
+    import torch
+    return torch.cuda.current_device()
+
+
 def fused_source_sha():
     """sha256 over the fused kernel's sources (the kernel and its generated tile block)."""
     import hashlib
@@ -208,6 +228,8 @@ def main():
     total_s = time.perf_counter() - t0
     kern_ms = [a.elapsed_time(b) for a, b in evs]
     kern_ms_avg = sum(kern_ms) / len(kern_ms)
+    kern_sorted = sorted(kern_ms)
+    kern_ms_median = kern_sorted[len(kern_sorted) // 2]
     ms_per_step = total_s * 1e3 / args.steps
 
     # The removed two-launch variant as a comparator: cache-only launch,
@@ -283,8 +305,11 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": "ring_attn_fused_kernel<256>",
-                     "kernel_ms_avg": round(kern_ms_avg, 4)},
-        "device": {"name": props.name, "cus": props.multi_processor_count},
+                     "kernel_ms_avg": round(kern_ms_avg, 4),
+                     "kernel_ms_median": round(kern_ms_median, 4),
+                     "kernel_ms_min": round(kern_sorted[0], 4)},
+        "device": {"name": props.name, "arch": props.gcnArchName.split(":")[0],
+                   "cus": props.multi_processor_count, "peak_sclk_mhz": peak_sclk_mhz()},
     }
     if two is not None:
         two["fused_time_reduction"] = round(1 - ms_per_step / two["ms_per_step"], 4)
