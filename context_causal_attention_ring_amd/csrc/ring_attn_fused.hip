@@ -20,13 +20,13 @@
 //    probabilities are already laid out as the B operand of O^T = V^T P^T
 //    (the key order inside a 16-key step is permuted identically on both
 //    operands, which leaves the contraction unchanged).  The fp32
-//    accumulator (64 rows x HD) lives in the AGPRs; at HD = 256 the score
-//    MFMAs are one asm block that writes the scores to VGPRs, where the
-//    softmax reads them.
+//    accumulator (64 rows x HD) lives in the AGPRs; at HD = 256 each tile is
+//    one hand-scheduled asm block (tile_hd256.inc, see tile_hd256 below).
 //  * K/V tiles of 32 keys go HBM -> LDS by buffer_load ... lds (no register
-//    staging) into two K and two V slots: while tile v's scores are
-//    computed, K of tile v+1 and V of tile v are in flight and the values of
-//    tile v-1 are still being consumed.
+//    staging) into four K and four V slots (tile t in slot t mod 4).  Tiles
+//    run in pairs with one wait and one barrier per pair; while a pair is
+//    computed, the copies of the next pair (K two tiles ahead, V one tile
+//    behind it) are in flight, issued between the score MFMAs.
 //    Rows are stored with a 16-byte-chunk XOR swizzle chosen per operand so
 //    that K reads (32 rows, one chunk) and transposed V reads
 //    (ds_read_b64_tr_b16, 4 rows x 4 chunks) are both bank-conflict free.
@@ -45,7 +45,8 @@
 //    block (one MFMA pair, one V operand read, a slice of softmax work).
 //  * Workgroup ids are remapped so that the workgroups resident on one XCD
 //    share a KV head and walk the same tiles, keeping the re-streamed K/V in
-//    that XCD's L2.
+//    that XCD's L2, with the KV head's row tiles dealt to its XCDs in turn,
+//    longest causal rows first.
 #include "ra_internal.h"
 
 namespace ra {
@@ -62,9 +63,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
