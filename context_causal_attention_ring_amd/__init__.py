@@ -16,9 +16,13 @@ __all__ = ["StripeLayout", "Dims", "RingAttnError", "lib", "ring_attn_prefill",
            "ring_attn_partial", "merge_attn_states", "kv_cache_write", "ra_shard_len",
            "ra_version", "prefill", "two_launch_prefill", "LIB_PATH", "EXPORTED_SYMBOLS",
            "RA_REGION_CACHE", "RA_REGION_CURRENT", "ring_attn_prefill_split",
-           "ra_split_workspace_bytes", "ra_split_suggest", "RA_MAX_SPLITS"]
+           "ra_split_workspace_bytes", "ra_split_suggest", "RA_MAX_SPLITS", "load",
+           "SYNC_LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn.so")
+# The checking build (every tile of the fused kernel fenced by a wait and a
+# barrier); tests compare it bit for bit with the product library.
+SYNC_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn_sync.so")
 EXPORTED_SYMBOLS = ("ring_attn_prefill", "ring_attn_prefill_split", "ra_split_workspace_bytes",
                     "ra_split_suggest",
                     "ring_attn_partial", "merge_attn_states", "kv_cache_write", "ra_shard_len",
@@ -53,40 +57,45 @@ class RingAttnError(RuntimeError):
 _lib = None
 
 
+def load(path):
+    """Open one build of the library with the C signatures declared."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing; build it with "
+                          "`python -m context_causal_attention_ring_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.ring_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i32, StripeLayout, vp, vp,
+                                    ctypes.POINTER(Dims), vp]
+    L.ring_attn_prefill.restype = ctypes.c_int
+    L.ring_attn_prefill_split.argtypes = [vp, vp, vp, vp, vp, i64, i32, StripeLayout, i32,
+                                          vp, i64, vp, vp, ctypes.POINTER(Dims), vp]
+    L.ring_attn_prefill_split.restype = ctypes.c_int
+    L.ra_split_workspace_bytes.argtypes = [ctypes.POINTER(Dims), i32, ctypes.POINTER(i64)]
+    L.ra_split_workspace_bytes.restype = ctypes.c_int
+    L.ra_split_suggest.argtypes = [ctypes.POINTER(Dims), i32, ctypes.POINTER(i32)]
+    L.ra_split_suggest.restype = ctypes.c_int
+    L.ring_attn_partial.argtypes = [vp, vp, vp, vp, vp, i64, i32, StripeLayout, i32, vp, vp,
+                                    ctypes.POINTER(Dims), vp]
+    L.ring_attn_partial.restype = ctypes.c_int
+    L.merge_attn_states.argtypes = [vp, vp, vp, vp, i32, vp, vp, ctypes.POINTER(Dims), vp]
+    L.merge_attn_states.restype = ctypes.c_int
+    L.kv_cache_write.argtypes = [vp, vp, i32, vp, vp, i64, i32, StripeLayout,
+                                 ctypes.POINTER(Dims), vp]
+    L.kv_cache_write.restype = ctypes.c_int
+    L.ra_shard_len.argtypes = [i64, i32, StripeLayout, i32, ctypes.POINTER(i64)]
+    L.ra_shard_len.restype = ctypes.c_int
+    L.ra_last_error.argtypes = []
+    L.ra_last_error.restype = ctypes.c_char_p
+    L.ra_version.argtypes = []
+    L.ra_version.restype = ctypes.c_char_p
+    return L
+
+
 def lib():
     """Load libringattn.so once; raise if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing; build it with "
-                              "`python -m context_causal_attention_ring_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
-        L.ring_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i64, i32, StripeLayout, vp, vp,
-                                        ctypes.POINTER(Dims), vp]
-        L.ring_attn_prefill.restype = ctypes.c_int
-        L.ring_attn_prefill_split.argtypes = [vp, vp, vp, vp, vp, i64, i32, StripeLayout, i32,
-                                              vp, i64, vp, vp, ctypes.POINTER(Dims), vp]
-        L.ring_attn_prefill_split.restype = ctypes.c_int
-        L.ra_split_workspace_bytes.argtypes = [ctypes.POINTER(Dims), i32, ctypes.POINTER(i64)]
-        L.ra_split_workspace_bytes.restype = ctypes.c_int
-        L.ra_split_suggest.argtypes = [ctypes.POINTER(Dims), i32, ctypes.POINTER(i32)]
-        L.ra_split_suggest.restype = ctypes.c_int
-        L.ring_attn_partial.argtypes = [vp, vp, vp, vp, vp, i64, i32, StripeLayout, i32, vp, vp,
-                                        ctypes.POINTER(Dims), vp]
-        L.ring_attn_partial.restype = ctypes.c_int
-        L.merge_attn_states.argtypes = [vp, vp, vp, vp, i32, vp, vp, ctypes.POINTER(Dims), vp]
-        L.merge_attn_states.restype = ctypes.c_int
-        L.kv_cache_write.argtypes = [vp, vp, i32, vp, vp, i64, i32, StripeLayout,
-                                     ctypes.POINTER(Dims), vp]
-        L.kv_cache_write.restype = ctypes.c_int
-        L.ra_shard_len.argtypes = [i64, i32, StripeLayout, i32, ctypes.POINTER(i64)]
-        L.ra_shard_len.restype = ctypes.c_int
-        L.ra_last_error.argtypes = []
-        L.ra_last_error.restype = ctypes.c_char_p
-        L.ra_version.argtypes = []
-        L.ra_version.restype = ctypes.c_char_p
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
 
 

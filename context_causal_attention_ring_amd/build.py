@@ -10,6 +10,10 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libringattn.so")
+# The same library with a wait and a barrier around every tile of the fused
+# kernel: race-free by construction, so a test can require the product
+# library to match it bit for bit.
+SYNC_LIB = os.path.join(PKG, "libringattn_sync.so")
 SOURCES = ["ringattn_api.hip", "ring_attn_fused.hip", "kv_cache_write.hip",
            "merge_attn_states.hip"]
 ARCH = os.environ.get("RINGATTN_ARCH", "gfx950")
@@ -29,10 +33,9 @@ def hipcc():
     raise RuntimeError("hipcc not found; libringattn needs ROCm's hipcc to build")
 
 
-def build(verbose=False):
-    """Compile every source into libringattn.so (always recompiles)."""
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+def _compile(out, extra, verbose):
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,16 +47,23 @@ def build(verbose=False):
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
-def assemble(source="ring_attn_fused.hip", out=None):
+def build(verbose=False):
+    """Compile every source into libringattn.so and the checking build
+    libringattn_sync.so (always recompiles)."""
+    _compile(SYNC_LIB, ["-DRA_SYNC_EVERY_TILE"], verbose)
+    return _compile(LIB, [], verbose)
+
+
+def assemble(source="ring_attn_fused.hip", out=None, extra=()):
     """Device assembly of one source (for reading register use and spills)."""
     out = out or os.path.join(PKG, os.path.splitext(source)[0] + ".s")
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "--cuda-device-only", "-S",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wno-unused-command-line-argument", "-o", out, os.path.join(CSRC, source)]
+           "-Wno-unused-command-line-argument", *extra, "-o", out, os.path.join(CSRC, source)]
     subprocess.run(cmd, check=True, capture_output=True)
     return out
 

@@ -777,6 +777,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   auto body = [&](auto slot, int v) RA_INLINE {
     constexpr int SL = decltype(slot)::value;
     rescale();
+#ifdef RA_SYNC_EVERY_TILE  // checking build: every copy lands, every wave is here
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+#endif
     if constexpr (SL % 2 == 0 && !ASM256) {  // start of a pair: the copies of the next pair
       if (v + 2 <= T) {
         issue_k(n0, kslot((SL + 2) % 4));
@@ -825,6 +829,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       any = pv_softmax(vslot((SL + 3) % 4), S, alpha);
       pack(S, pb, alpha);
     }
+#ifdef RA_SYNC_EVERY_TILE
+    __syncthreads();
+#endif
     if constexpr (SL % 2 == 1) {  // end of a pair
       if constexpr (!ASM256) {  // (the HD = 256 block waits and synchronises itself)
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed

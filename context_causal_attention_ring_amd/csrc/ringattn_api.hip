@@ -6,9 +6,12 @@
 // ring cache phase, fused with the current phase", Design section (striped
 // cache shards visited as ring rounds, the cache bound of a partial last
 // block applied at run time).
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
 
 #include "../../include/ringattn.h"
@@ -80,7 +83,13 @@ extern "C" {
 
 const char* ra_last_error(void) { return g_last_error.c_str(); }
 
-const char* ra_version(void) { return "libringattn 0.1 (gfx950)"; }
+const char* ra_version(void) {
+#ifdef RA_SYNC_EVERY_TILE
+  return "libringattn 0.1 (gfx950, checking build: synchronised every tile)";
+#else
+  return "libringattn 0.1 (gfx950)";
+#endif
+}
 
 int ra_shard_len(int64_t cache_len, int32_t P, ra_stripe_layout_t stripe_layout, int32_t shard,
                  int64_t* len) {
@@ -107,6 +116,24 @@ int64_t split_part_bytes(const ra_dims_t& d, int32_t splits) {
 int64_t split_workspace_bytes(const ra_dims_t& d, int32_t splits) {
   const int64_t l = (int64_t)splits * d.num_q_heads * d.q_rows * 4;
   return split_part_bytes(d, splits) + (l + 255) / 256 * 256;
+}
+
+// With RINGATTN_LOG=1 in the environment, the first fused launch of the
+// process prints its geometry to stderr (once; later launches are silent).
+void log_geometry(const ra::FusedParams& p, int hd) {
+  static std::atomic<bool> done{false};
+  const char* v = std::getenv("RINGATTN_LOG");
+  if (!v || std::strcmp(v, "1") != 0 || done.exchange(true)) return;
+  std::fprintf(stderr,
+               "libringattn: fused launch HD=%d NQ=%d NKV=%d rows=%d (real %d, head %d at %d, "
+               "tail at %d) P=%d I=%d ring_start=%d full=%lld rem=%lld tiles/visit=%d "
+               "row_tiles=%d splits=%d seg_tiles=%d regions=%d workgroups=%d (+%d padding) "
+               "x %d threads, out %s\n",
+               hd, p.nq, p.nkv, p.q_rows, p.real_rows, p.head_rows, p.head_pos, p.tail_pos, p.P,
+               p.interleave, p.ring_start, (long long)p.full, (long long)p.rem, p.nb,
+               p.row_tiles, p.splits, p.seg_tiles, p.regions, p.grid_real,
+               (p.grid_real + 7) / 8 * 8 - p.grid_real, ra::kWaves * 64,
+               p.out_f32 ? "fp32" : "bf16");
 }
 
 // ring_attn_prefill over the regions selected by `regions` (1: cache, 2:
@@ -249,6 +276,7 @@ int prefill_regions(const void* q, const void* k_cache, const void* v_cache, con
   if ((int64_t)p.nb * P >= lim31)
     return fail(RA_ERR_UNSUPPORTED, "too many ring tiles");
 
+  log_geometry(p, HD);
   hipError_t e = ra::launch_fused(p, HD, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(RA_ERR_HIP, "fused attention launch failed: %s", hipGetErrorString(e));

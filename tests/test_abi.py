@@ -239,3 +239,14 @@ def test_generated_tile_block_is_current():
     gen = os.path.join(ROOT, "context_causal_attention_ring_amd", "csrc", "gen_tile_hd256.py")
     res = subprocess.run([sys.executable, gen, "--check"], capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
+
+
+def test_checking_build_exports_the_same_symbols():
+    """The checking build (every tile fenced) is the same ABI under another name."""
+    if not os.path.exists(ra.SYNC_LIB_PATH):
+        pytest.skip("checking build not built")
+    L = ra.load(ra.SYNC_LIB_PATH)
+    for name in header_functions():
+        assert hasattr(L, name), name
+    assert b"checking build" in L.ra_version()
+    assert b"checking build" not in ra.lib().ra_version()

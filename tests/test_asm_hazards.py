@@ -96,9 +96,10 @@ def hazards_after(lines, at, mfmas):
 
 
 @pytest.mark.skipif(not HAS_HIPCC, reason="needs hipcc to assemble the kernel")
-def test_no_compiler_code_races_the_last_mfmas_of_a_tile_block():
+@pytest.mark.parametrize("extra", [(), ("-DRA_SYNC_EVERY_TILE",)], ids=["product", "checking"])
+def test_no_compiler_code_races_the_last_mfmas_of_a_tile_block(extra):
     with tempfile.TemporaryDirectory() as tmp:
-        asm = open(build.assemble(out=os.path.join(tmp, "fused.s"))).read()
+        asm = open(build.assemble(out=os.path.join(tmp, "fused.s"), extra=extra)).read()
     kernels = re.findall(r"^(_ZN2ra\S*fused_kernelILi256\S*):", asm, re.M)
     assert len(kernels) == 2  # bf16 and fp32 output
     for name in kernels:

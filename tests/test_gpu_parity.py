@@ -451,3 +451,47 @@ def test_split_full_size(name, splits):
     rows = list(range(w.real_rows)) if w.q_rows <= 512 else sample_rows(w, 24, seed=w.seed)
     compare(case, out, lse, rows, TOL_BF16)
     check_pads_untouched(case, out, lse)
+
+
+# ---------------------------------------------------------------- race check (checking build)
+
+SYNC_CASES = [(workloads.CONFIGS["tiny"], 0), (FULL_CASES[1], 0), (FULL_CASES[2], 0),
+              (RANK_CASES[2], 0), (workloads.CONFIGS["32k"], 0), (FULL_CASES[2], 7),
+              (workloads.CONFIGS["32k_rank3of8"], 8)]
+
+
+@pytest.mark.parametrize("w,splits", SYNC_CASES,
+                         ids=lambda x: getattr(x, "name", f"splits{x}"))
+def test_checking_build_matches_bitwise(w, splits, monkeypatch):
+    """The library built with a wait for every copy and a barrier around every
+    tile cannot race; the product library, whose waves run ahead of each
+    other within a pair of tiles, must give the same bits."""
+    if not os.path.exists(ra.SYNC_LIB_PATH):
+        pytest.fail(f"{ra.SYNC_LIB_PATH} is missing: build() makes it with the product library")
+    case = Case(w).to_device()
+    go = (lambda: run_split(case, splits)) if splits else (lambda: run(case))
+    out, lse = go()
+    with monkeypatch.context() as m:
+        m.setattr(ra, "_lib", ra.load(ra.SYNC_LIB_PATH))
+        assert "checking build" in ra.ra_version()
+        out_s, lse_s = go()
+    assert torch.equal(out.view(torch.int16), out_s.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse_s.view(torch.int32))
+
+
+def test_launch_log_prints_geometry_once(monkeypatch, capfd):
+    """RINGATTN_LOG=1 prints the fused launch geometry on the first launch
+    of the process only."""
+    w = workloads.CONFIGS["tiny"]
+    case = Case(w).to_device()
+    monkeypatch.setenv("RINGATTN_LOG", "1")
+    capfd.readouterr()
+    run(case)
+    run(case)
+    err = capfd.readouterr().err
+    lines = [l for l in err.splitlines() if l.startswith("libringattn: fused launch")]
+    if not lines:
+        pytest.skip("the geometry was already printed earlier in this process")
+    assert len(lines) == 1, lines
+    assert (f"HD={w.hd} NQ={w.nq} NKV={w.nkv} rows={w.q_rows} (real {w.real_rows}" in lines[0]
+            and f"P={w.P} I={w.interleave}" in lines[0]), lines[0]
