@@ -238,9 +238,9 @@ def softmax_ops(pout):
     # One FMA + exp2 per score; each probability is added to the tile's row
     # sum r after the next FMA (a transcendental's result is not read in the
     # next slot), and each pair of keys is packed to bf16 once both are
-    # summed.  The tile sum is formed first and then l = l * alpha + r: added
-    # one by one to the running sum, the many tiny probabilities of a peaky
-    # row would be rounded away against it.
+    # summed.  The tile sum is formed first and then folded into l (below):
+    # added one by one to the running sum, the many tiny probabilities of a
+    # peaky row would be rounded away against it.
     streams = []
     for rb in range(NRB):
         st = []
@@ -262,8 +262,18 @@ def softmax_ops(pout):
                 ops.append(st[k])
     for rb in range(NRB):
         ops.append(("valu", f"v_add_f32 %[r{rb}], %[r{rb}], {s(rb, 15)}"))
+    # l = l * alpha + r, compensated (Kahan): lk keeps what the rounding of
+    # each fold dropped, so millions of tiny tile sums do not drift.
     for rb in range(NRB):
-        ops.append(("valu", f"v_fma_f32 %[l{rb}], %[l{rb}], %[al{rb}], %[r{rb}]"))
+        ops.append(("valu", f"v_mul_f32 %[a{rb}], %[l{rb}], %[al{rb}]"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_fma_f32 %[b{rb}], -%[lk{rb}], %[al{rb}], %[r{rb}]"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_add_f32 %[l{rb}], %[a{rb}], %[b{rb}]"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_sub_f32 %[lk{rb}], %[l{rb}], %[a{rb}]"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_sub_f32 %[lk{rb}], %[lk{rb}], %[b{rb}]"))
     for rb in range(NRB):
         ops.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, 7)}, {s(rb, 14)}, {s(rb, 15)}"))
     return ops

@@ -29,7 +29,8 @@ struct FusedParams {
   int32_t seg_tiles;        // tiles per segment (the last one of a row tile may be shorter)
   int64_t seg_out_stride;   // elements between the segments' partial outputs
   int32_t grid_real;        // row_tiles * splits * NKV
-  int32_t out_f32;
+  int32_t out_f32;          // fp32 output numerics: exact running max, sums of rounded probabilities
+  int32_t store_f32;        // out is written in fp32 (out_f32, or a split launch's partials)
   int32_t regions;          // 1: cache (ring) only, 2: current only, 3: both
   float scale_log2e;        // softmax scale * log2(e)
 };

@@ -198,7 +198,8 @@ __device__ __forceinline__ float wave_max_pair(float x) {
       [acc11] "+a"(acc[1][1]), [acc12] "+a"(acc[1][2]), [acc13] "+a"(acc[1][3]),               \
       [acc14] "+a"(acc[1][4]), [acc15] "+a"(acc[1][5]), [acc16] "+a"(acc[1][6]),               \
       [acc17] "+a"(acc[1][7]), [ml0] "+v"(ml[0]), [ml1] "+v"(ml[1]), [l0] "+v"(l[0]),          \
-      [l1] "+v"(l[1]), [al0] "=&v"(al[0]), [al1] "=&v"(al[1]), [any] "=&s"(any),              \
+      [l1] "+v"(l[1]), [lk0] "+v"(lk[0]), [lk1] "+v"(lk[1]), [al0] "=&v"(al[0]),               \
+      [al1] "=&v"(al[1]), [any] "=&s"(any),                                                    \
       [a0] "=&v"(a0), [b0] "=&v"(b0), [a1] "=&v"(a1), [b1] "=&v"(b1), [th0] "=&v"(th0),       \
       [th1] "=&v"(th1), [r0] "=&v"(r0), [r1] "=&v"(r1), [c0] "=&s"(c0), [c1] "=&s"(c1),        \
       [st] "=&s"(st), RA_TILE_HD256_KPRE_OPERANDS
@@ -216,6 +217,21 @@ __device__ __forceinline__ float wave_max_pair(float x) {
       [dvb] "v"(dl.vb), [mk0] "i"(MK), [mk1] "i"(MK + 8192), [mk2] "i"(MK + 4096),              \
       [mk3] "i"(MK + 12288), [mv0] "i"(MV), [mv1] "i"(MV + 8192), [mv2] "i"(MV + 4096),         \
       [mv3] "i"(MV + 12288)
+// l <- l * a + r, compensated (Kahan summation): c holds the part of the
+// sum that earlier folds rounded away (negated), and the fold adds it back,
+// so a row sum over millions of keys whose tile sums are tiny against it
+// (a peaky row: one dominant key, the rest near 0) does not drift.  The
+// sum's best value is l - c.  Contraction stays off: t - lp must see the
+// rounded product.
+__device__ __forceinline__ void fold_sum(float& l, float& c, float a, float r) {
+#pragma clang fp contract(off)
+  const float lp = l * a;
+  const float y = r - c * a;
+  const float t = lp + y;
+  c = (t - lp) - y;
+  l = t;
+}
+
 struct CopyLanes {    // a lane's offsets for the block's LDS-DMA copies (see below)
   uint32_t ka, kb, va, vb;
   uint32_t rs16;      // 16 rows' stride in bytes (uniform)
@@ -225,7 +241,8 @@ __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], const bf16x8 (&p
                                            bf16x8 (&pout)[2][2], const bf16x8 (&q)[2][16],
                                            bf16x8 (&kpre)[2], const uint32_t (&ka)[8],
                                            const uint32_t (&va)[4],
-                                           float (&ml)[2], float (&l)[2], float (&al)[2],
+                                           float (&ml)[2], float (&l)[2], float (&lk)[2],
+                                           float (&al)[2],
                                            uint64_t& any, float c2, float tau, uint32_t mflag,
                                            const int (&lim)[2], const i32x4& desck,
                                            const i32x4& descv, uint32_t offk, uint32_t offv,
@@ -322,14 +339,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   }
 
   // Q^T operands: lane holds d = 16 s + 8 h + [0, 8) of each of its rows.
-  // Loaded through a descriptor bounded at the real rows (rows past read 0).
+  // Loaded through a descriptor over this workgroup's tokens only (its base
+  // at the first one, so offsets stay small at any q size), bounded at the
+  // real rows: rows past them read 0.
   bf16x8 qreg[NRB][NKS];
   {
+    const int t0 = row0 / p.group;
+    const int t_end = min(p.real_rows, (row0 + kRowsPerWG - 1) / p.group + 1);
+    const uint32_t q_bytes = t_end > t0 ? (uint32_t)(t_end - t0) * (uint32_t)p.nq * D * 2 : 0u;
     const __amdgpu_buffer_rsrc_t qr =
-        make_rsrc(p.q, (uint32_t)p.real_rows * (uint32_t)p.nq * D * 2);
+        make_rsrc(p.q + (int64_t)t0 * p.nq * D, q_bytes);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-      const uint32_t qoff = ((uint32_t)token[rb] * p.nq + head[rb]) * D * 2 + 16 * h;
+      const uint32_t qoff = ((uint32_t)(token[rb] - t0) * p.nq + head[rb]) * D * 2 + 16 * h;
 #pragma unroll
       for (int s = 0; s < NKS; ++s)
         qreg[rb][s] = __builtin_bit_cast(
@@ -510,11 +532,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   bf16x8 pb[NRB][NPS];  // bf16 probabilities of the previous tile (B operands of P.V)
   bf16x8 pbuf[2][NRB][NPS];  // the same, double-buffered by tile parity (HD = 256 body)
   float mlog[NRB], lsum[NRB], lsum_q[NRB];  // running max (log2 units), row sums
+  float lcomp[NRB], lcomp_q[NRB];            // their compensations (fold_sum)
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     mlog[rb] = kNegInf;
-    lsum[rb] = 0.f;     // exact fp32 sum of this lane's share of the keys
+    lsum[rb] = 0.f;     // fp32 sum of this lane's share of the keys' probabilities
     lsum_q[rb] = 0.f;   // the same over bf16-rounded probabilities (fp32 output)
+    lcomp[rb] = lcomp_q[rb] = 0.f;
   }
   const float c2 = p.scale_log2e;
 
@@ -589,7 +613,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
           S[rb][kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rb][kb][i], c2, -m_use));
           ls += S[rb][kb][i];
         }
-      lsum[rb] = lsum[rb] * alpha[rb] + ls;
+      fold_sum(lsum[rb], lcomp[rb], alpha[rb], ls);
       mlog[rb] = m_new;
       any |= anyrb;
     }
@@ -612,7 +636,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
           pb[rb][2 * kb + (i >> 3)][i & 7] = pr[0];
           pb[rb][2 * kb + (i >> 3)][(i & 7) + 1] = pr[1];
         }
-      if (F32OUT) lsum_q[rb] = lsum_q[rb] * alpha[rb] + lq;
+      if (F32OUT) fold_sum(lsum_q[rb], lcomp_q[rb], alpha[rb], lq);
     }
   };
 
@@ -679,7 +703,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
         ls[rb] += S[rb][kb][i];
       } else {  // row sums
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) lsum[rb] = lsum[rb] * al[rb] + ls[rb];
+        for (int rb = 0; rb < NRB; ++rb) fold_sum(lsum[rb], lcomp[rb], al[rb], ls[rb]);
       }
     };
     bf16x8 vq[3];
@@ -769,7 +793,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
             const bf16x2 pr = {pb[rb][ks][e], pb[rb][ks][e + 1]};
             lq = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lq, false);
           }
-        lsum_q[rb] = lsum_q[rb] * alpha[rb] + lq;
+        fold_sum(lsum_q[rb], lcomp_q[rb], alpha[rb], lq);
       }
     }
   };
@@ -816,7 +840,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
                          __builtin_amdgcn_readfirstlane(vs.vr[3])};
       tile_hd256<SL * TILE_B, ((SL + 3) % 4) * TILE_B, PB ^ 1, ((SL + 2) % 4) * TILE_B,
                  VBASE + ((SL + 1) % 4) * TILE_B, ((SL + 1) % 4) * TILE_B>(
-          acc, pbuf[PB ^ 1], pbuf[PB], qreg, kpre, ka, va, mlog, lsum, alpha, anyf, c2,
+          acc, pbuf[PB ^ 1], pbuf[PB], qreg, kpre, ka, va, mlog, lsum, lcomp, alpha, anyf, c2,
           kTau<F32OUT>, __builtin_amdgcn_readfirstlane(cut ? 1u : 0u), lim, dkr, dvr,
           __builtin_amdgcn_readfirstlane(ks.off), __builtin_amdgcn_readfirstlane(vs.off), m0b,
           dl);
@@ -864,8 +888,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // Epilogue: out = acc / l, lse = ln 2 * (m + log2 l).
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    const float l_tot = lsum[rb] + __shfl_xor(lsum[rb], 32);
-    const float l_norm = F32OUT ? lsum_q[rb] + __shfl_xor(lsum_q[rb], 32) : l_tot;
+    const float l_own = lsum[rb] - lcomp[rb], lq_own = lsum_q[rb] - lcomp_q[rb];
+    const float l_tot = l_own + __shfl_xor(l_own, 32);
+    const float l_norm = F32OUT ? lq_own + __shfl_xor(lq_own, 32) : l_tot;
     if (!row_ok[rb]) continue;
     // a row that saw no key (possible in a one-region launch) gets out = 0
     // and lse = -inf (m = -inf, log2 0 = -inf)
@@ -879,7 +904,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
         const int d0 = db * 32 + i4 * 8 + 4 * h;
         const f32x4 o = {acc[rb][db][4 * i4] * inv, acc[rb][db][4 * i4 + 1] * inv,
                          acc[rb][db][4 * i4 + 2] * inv, acc[rb][db][4 * i4 + 3] * inv};
-        if (F32OUT) {
+        if (F32OUT || p.store_f32) {
           *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase + d0) = o;
         } else {
           const bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};

@@ -106,11 +106,10 @@ int ra_shard_len(int64_t cache_len, int32_t P, ra_stripe_layout_t stripe_layout,
 namespace {
 
 // Bytes of a split launch's workspace: the partial outputs [S, C, NQ, HD]
-// (in the output dtype) then the partial LSEs [S, NQ, C] fp32, both 256-byte
-// aligned.
+// fp32 (a bf16 partial would round twice, once there and once after the
+// merge) then the partial LSEs [S, NQ, C] fp32, both 256-byte aligned.
 int64_t split_part_bytes(const ra_dims_t& d, int32_t splits) {
-  const int64_t o = (int64_t)splits * d.q_rows * d.num_q_heads * d.head_dim *
-                    (d.out_dtype == RA_DTYPE_FP32 ? 4 : 2);
+  const int64_t o = (int64_t)splits * d.q_rows * d.num_q_heads * d.head_dim * 4;
   return (o + 255) / 256 * 256;
 }
 int64_t split_workspace_bytes(const ra_dims_t& d, int32_t splits) {
@@ -208,6 +207,10 @@ int prefill_regions(const void* q, const void* k_cache, const void* v_cache, con
   if (((int64_t)d.cur_len + ra::kBKV) * rowstride >= lim31)
     return fail(RA_ERR_UNSUPPORTED, "the current chunk (%d tokens x %lld bytes) exceeds 2 GiB",
                 d.cur_len, (long long)rowstride);
+  // Each workgroup reads its own tokens' q rows through one descriptor.
+  if ((int64_t)(ra::kRowsPerWG / group + 2) * NQ * HD * 2 >= lim31)
+    return fail(RA_ERR_UNSUPPORTED, "num_q_heads=%d with %d q heads per KV head is too large",
+                NQ, group);
   const int64_t rows_total = (int64_t)d.real_rows * group;
   if (rows_total + ra::kRowsPerWG >= lim31 / 2)
     return fail(RA_ERR_UNSUPPORTED, "real_rows * (NQ/NKV) = %lld is too large",
@@ -217,8 +220,9 @@ int prefill_regions(const void* q, const void* k_cache, const void* v_cache, con
   const int64_t q_bytes = (int64_t)C * NQ * HD * 2;
   const int64_t cur_bytes = (int64_t)d.cur_len * NKV * HD * 2;
   const int64_t cache_bytes = (int64_t)P * d.shard_cap * NKV * HD * 2;
+  // a split launch writes fp32 partials ([splits, C, NQ, HD])
   const int64_t out_bytes =
-      (int64_t)splits * C * NQ * HD * (d.out_dtype == RA_DTYPE_FP32 ? 4 : 2);
+      (int64_t)splits * C * NQ * HD * (d.out_dtype == RA_DTYPE_FP32 || splits > 1 ? 4 : 2);
   const int64_t lse_bytes = (int64_t)splits * NQ * C * 4;
   struct R { const void* p; int64_t n; };
   const R ins[] = {{q, q_bytes}, {k_cache, cache_len > 0 ? cache_bytes : 0},
@@ -270,6 +274,7 @@ int prefill_regions(const void* q, const void* k_cache, const void* v_cache, con
     return fail(RA_ERR_UNSUPPORTED, "too many workgroups");
   p.grid_real = p.row_tiles * splits * NKV;
   p.out_f32 = d.out_dtype == RA_DTYPE_FP32;
+  p.store_f32 = p.out_f32 || splits > 1;
   p.regions = regions;
   const float scale = d.scale == 0.f ? 1.f / std::sqrt((float)HD) : d.scale;
   p.scale_log2e = scale * 1.4426950408889634f;
@@ -391,7 +396,8 @@ int ring_attn_prefill_split(const void* q, const void* k_cache, const void* v_ca
   m.real_rows = d.real_rows;
   m.nq = d.num_q_heads;
   m.hd = d.head_dim;
-  m.parts_f32 = m.out_f32 = d.out_dtype == RA_DTYPE_FP32;
+  m.parts_f32 = 1;
+  m.out_f32 = d.out_dtype == RA_DTYPE_FP32;
   hipError_t e = ra::launch_merge_splits(m, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(RA_ERR_HIP, "split merge launch failed: %s", hipGetErrorString(e));

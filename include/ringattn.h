@@ -121,7 +121,11 @@ typedef struct {
  *            each real row, or NULL to skip
  *
  * k_cache/v_cache may be NULL only when cache_len == 0.  out and lse must
- * not overlap any input.  Each shard's valid bytes must stay below 2^31.
+ * not overlap any input.  Limits (RA_ERR_UNSUPPORTED beyond them): each
+ * shard's valid rows plus one 32-key tile, and cur_len plus one tile, stay
+ * below 2^31 bytes of K (NKV * HD * 2 bytes a row); (256 / (NQ/NKV) + 2) *
+ * NQ * HD * 2 < 2^31 (the q rows one workgroup reads); real_rows * NQ/NKV
+ * < 2^30.  q, out and the caches may be larger than 4 GiB.
  * Returns RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED or RA_ERR_HIP.
  */
 int ring_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
@@ -147,8 +151,8 @@ int ring_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
  *                    ra_split_workspace_bytes() bytes; overwritten; must not
  *                    overlap any tensor argument; unused when splits == 1
  *   workspace_bytes  its size
- * The partials are in the output dtype, so a bf16 result is merged from
- * bf16 partials (within the bf16 tolerance of the unsplit launch).
+ * The partials are fp32 whatever the output dtype, so the result is rounded
+ * once, after the merge.
  */
 int ring_attn_prefill_split(const void* q, const void* k_cache, const void* v_cache,
                             const void* k_cur, const void* v_cur, int64_t cache_len,

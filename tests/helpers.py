@@ -1,6 +1,8 @@
 """Shared test plumbing: seeded inputs -> striped device tensors, and the
 oracle's view of the same bits.  Striping for the device inputs uses the
 oracle's map (test code may call the oracle; the library never does)."""
+import math
+
 import numpy as np
 import torch
 
@@ -65,3 +67,60 @@ def sample_rows(w, n_random, seed=0):
     rng = np.random.default_rng(seed)
     rand = set(rng.choice(real, size=min(n_random, real), replace=False).tolist())
     return sorted(fixed | rand)
+
+
+# ------------------------------------------------------------ needle inputs
+# One KV head, 16 query heads, HD = 256, 16 chunk tokens: row r = 16 t + h
+# of the chunk has q = ALPHA * e_r, and its own "needle" cache token n_r
+# holds k = BETA * e_r and a random v = w_r; every other key and value (the
+# cache's other tokens and the whole current chunk) is zero.  Row r then
+# scores s = scale * ALPHA * BETA on its needle and 0 on each of its other
+# n_vis(r) - 1 visible keys, so the softmax definition gives in closed form
+#   out_r = (e^s w_r + sum_{r' != r} w_r') / (e^s + n_vis(r) - 1)
+#   lse_r = ln(e^s + n_vis(r) - 1),  n_vis(r) = cache_len + t + 1.
+# Any misplaced read of the cache (wrong slot, past the shard) changes it.
+
+NEEDLE_T, NEEDLE_G, NEEDLE_HD = 16, 16, 256
+NEEDLE_ALPHA = NEEDLE_BETA = 16.0
+
+
+def needle_positions(cache_len, seed=0):
+    """256 distinct cache tokens: the last 128 and 128 spread from token 0,
+    dealt to the rows in a seeded order."""
+    n = NEEDLE_T * NEEDLE_G
+    assert cache_len >= n
+    tail = list(range(cache_len - n // 2, cache_len))
+    spread = [k * ((cache_len - n // 2) // (n // 2)) for k in range(n // 2)]
+    pos = np.array(spread + tail, dtype=np.int64)
+    assert len(set(pos.tolist())) == n
+    return np.random.default_rng(seed).permutation(pos)
+
+
+def needle_values(seed=0):
+    """w_r: [256, HD] bf16 values (seeded normal draws)."""
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(NEEDLE_T * NEEDLE_G, NEEDLE_HD, generator=g).to(torch.bfloat16)
+
+
+def needle_q():
+    q = torch.zeros(NEEDLE_T, NEEDLE_G, NEEDLE_HD)
+    r = torch.arange(NEEDLE_T * NEEDLE_G)
+    q.view(-1, NEEDLE_HD)[r, r] = NEEDLE_ALPHA
+    return q.to(torch.bfloat16)
+
+
+def needle_expected(cache_len, w, scale):
+    """Closed form above, fp64: out [T, G, HD], lse [G, T]."""
+    w = w.double().numpy()
+    s = scale * NEEDLE_ALPHA * NEEDLE_BETA
+    es = math.exp(s)
+    total = w.sum(axis=0)
+    out = np.zeros((NEEDLE_T, NEEDLE_G, NEEDLE_HD))
+    lse = np.zeros((NEEDLE_G, NEEDLE_T))
+    for t in range(NEEDLE_T):
+        n_vis = cache_len + t + 1
+        for h in range(NEEDLE_G):
+            r = t * NEEDLE_G + h
+            out[t, h] = (es * w[r] + (total - w[r])) / (es + n_vis - 1)
+            lse[h, t] = math.log(es + n_vis - 1)
+    return out, lse

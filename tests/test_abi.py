@@ -81,6 +81,7 @@ BAD_PREFILL = [
     (dict(d=dims(), out=FAKE + 0x10), 1, "overlaps"),
     (dict(d=dims(), lse=FAKE + 0x3000000), 1, "overlaps"),
     (dict(d=dims(num_kv_heads=1, head_dim=256, shard_cap=1 << 23), cache_len=1 << 24), 2, "2 GiB"),
+    (dict(d=dims(num_q_heads=5462 * 256, num_kv_heads=5462, head_dim=256)), 2, "num_q_heads=1398272"),
     (dict(d=dims(head_pos=-1)), 1, "head_pos"),
     (dict(d=dims(tail_pos=-3)), 1, "tail_pos"),
     (dict(d=dims(cur_len=-1)), 1, "cur_len"),
@@ -137,8 +138,9 @@ def call_split(d, splits=4, ws=FAKE + 0x20000000, ws_bytes=1 << 30):
 def test_split_workspace_bytes():
     d = dims()
     assert ra.ra_split_workspace_bytes(d, 1) == 0
-    # partial outputs [S, C, NQ, HD] bf16 then LSEs [S, NQ, C] fp32, 256-byte aligned
-    assert ra.ra_split_workspace_bytes(d, 3) == 3 * 128 * 4 * 64 * 2 + 3 * 4 * 128 * 4
+    # partial outputs [S, C, NQ, HD] fp32 (whatever the output dtype) then LSEs
+    # [S, NQ, C] fp32, 256-byte aligned
+    assert ra.ra_split_workspace_bytes(d, 3) == 3 * 128 * 4 * 64 * 4 + 3 * 4 * 128 * 4
     d32 = dims(out_dtype=1, q_rows=5, head_rows=5, real_rows=5, tail_pos=5)
     assert ra.ra_split_workspace_bytes(d32, 2) == 2 * 5 * 4 * 64 * 4 + 256  # 160 B of LSE rounds up
 

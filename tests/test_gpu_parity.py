@@ -495,3 +495,104 @@ def test_launch_log_prints_geometry_once(monkeypatch, capfd):
     assert len(lines) == 1, lines
     assert (f"HD={w.hd} NQ={w.nq} NKV={w.nkv} rows={w.q_rows} (real {w.real_rows}" in lines[0]
             and f"P={w.P} I={w.interleave}" in lines[0]), lines[0]
+
+
+# ---------------------------------------------------------------- maximum sizes
+
+# The longest shard the library accepts at NKV = 1, HD = 256 (512-byte K rows):
+# its rows plus one 32-key tile stay below 2^31 bytes.
+MAX_SHARD_LEN = (1 << 31) // 512 - 32 - 1
+
+
+@pytest.mark.parametrize("splits", [1, 16])
+def test_largest_shard_region(splits):
+    """One shard of the largest length the library accepts (its K rows end
+    just under 2 GiB), NKV = 1, HD = 256: needle inputs whose closed form
+    (pinned against the oracle on the CPU) checks that every row finds its
+    own cache token, among them the shard's last 128 slots; slots past the
+    shard's end hold NaN and must never be read."""
+    from helpers import (NEEDLE_G, NEEDLE_HD, NEEDLE_T, needle_expected, needle_positions,
+                         needle_q, needle_values)
+    L = MAX_SHARD_LEN
+    cap = L + 16
+    pos = torch.from_numpy(needle_positions(L, seed=2))
+    w = needle_values(seed=2)
+    r = torch.arange(NEEDLE_T * NEEDLE_G)
+    print(f"[gpu] largest shard region L={L} cap={cap} splits={splits}", flush=True)
+    kc = torch.zeros(1, cap, 1, NEEDLE_HD, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    kc[0, L:] = float("nan")
+    vc[0, L:] = float("nan")
+    kc.view(cap, NEEDLE_HD)[pos.cuda(), r.cuda()] = 16.0
+    vc.view(cap, NEEDLE_HD)[pos.cuda()] = w.cuda()
+    q = needle_q().cuda()
+    cur = torch.zeros(NEEDLE_T, 1, NEEDLE_HD, dtype=torch.bfloat16, device="cuda")
+    out = torch.full((NEEDLE_T, NEEDLE_G, NEEDLE_HD), SENTINEL, dtype=torch.bfloat16,
+                     device="cuda")
+    lse = torch.full((NEEDLE_G, NEEDLE_T), SENTINEL, dtype=torch.float32, device="cuda")
+    dims = ra.make_dims(q, cur, cap, real_rows=NEEDLE_T, head_rows=NEEDLE_T)
+    if splits == 1:
+        ra.ring_attn_prefill(q, kc, vc, cur, cur, L, 1, ra.StripeLayout(1, 0), out, lse, dims)
+    else:
+        ws = torch.empty(ra.ra_split_workspace_bytes(dims, splits), dtype=torch.uint8,
+                         device="cuda")
+        ra.ring_attn_prefill_split(q, kc, vc, cur, cur, L, 1, ra.StripeLayout(1, 0), splits,
+                                   ws, out, lse, dims)
+    torch.cuda.synchronize()
+    o_ref, l_ref = needle_expected(L, w, oracle.attention.default_scale(NEEDLE_HD))
+    d_out = np.abs(out.cpu().double().numpy() - o_ref).max()
+    d_lse = np.abs(lse.cpu().double().numpy() - l_ref).max()
+    print(f"    max|d out|={d_out:.3e} max|d lse|={d_lse:.3e}", flush=True)
+    assert d_out <= TOL_BF16 and d_lse <= TOL_LSE, (d_out, d_lse)
+    del kc, vc
+    torch.cuda.empty_cache()
+
+
+class _RepeatedRows:
+    """q rows repeating a block of R0 rows (row i = block[i % R0]) without
+    materialising them on the host; what the oracle indexes."""
+
+    def __init__(self, block, C):
+        self.block, self.shape = block, (C,) + tuple(block.shape[1:])
+
+    def __getitem__(self, idx):
+        i, rest = idx[0], idx[1:]
+        return self.block[(i % self.block.shape[0],) + tuple(rest)]
+
+
+def test_q_and_out_past_4gib():
+    """NQ = 128, NKV = 8, HD = 256 and 69632 chunk rows: q and out are 4.25
+    GiB each, so rows past token 65536 sit beyond 2^32 bytes.  q repeats a
+    block of 3000 seeded rows (3000 does not divide 65536, so a wrapped
+    offset would read another row's q); sampled rows against the oracle."""
+    C, NQ, NKV, HD, R0 = 69632, 128, 8, 256, 3000
+    L, P = 513, 2
+    g = torch.Generator().manual_seed(11)
+    block = torch.randn(R0, NQ, HD, generator=g).to(torch.bfloat16)
+    k_tok = torch.randn(L, NKV, HD, generator=g).to(torch.bfloat16)
+    v_tok = torch.randn(L, NKV, HD, generator=g).to(torch.bfloat16)
+    k_cur = torch.randn(C, NKV, HD, generator=g).to(torch.bfloat16)
+    v_cur = torch.randn(C, NKV, HD, generator=g).to(torch.bfloat16)
+    cap = max(oracle.shard_lengths(L, P, 1))
+    print(f"[gpu] q/out past 4 GiB C={C} NQ={NQ} NKV={NKV} HD={HD} L={L} P={P}", flush=True)
+    q = block.cuda().repeat((C + R0 - 1) // R0, 1, 1)[:C].contiguous()
+    kc = striped_cache(k_tok, P, 1, cap).cuda()
+    vc = striped_cache(v_tok, P, 1, cap).cuda()
+    kcur, vcur = k_cur.cuda(), v_cur.cuda()
+    out = torch.empty(C, NQ, HD, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(NQ, C, dtype=torch.float32, device="cuda")
+    dims = ra.make_dims(q, kcur, cap, real_rows=C, head_rows=C)
+    ra.ring_attn_prefill(q, kc, vc, kcur, vcur, L, P, ra.StripeLayout(1, 0), out, lse, dims)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = sorted({0, 4095, 4096, 65535, 65536, 65537, C - 2, C - 1} |
+                  set(rng.choice(C, 8, replace=False).tolist()))
+    o = out[rows].cpu().double().numpy()
+    l = lse[:, rows].cpu().double().numpy()
+    del q, out
+    torch.cuda.empty_cache()
+    o_ref, l_ref = oracle.attention_rows(_RepeatedRows(f64(block), C), f64(k_tok), f64(v_tok),
+                                         f64(k_cur), f64(v_cur), rows, oracle.attention.default_scale(HD))
+    d_out, d_lse = np.abs(o - o_ref).max(), np.abs(l - l_ref).max()
+    print(f"    rows={len(rows)} max|d out|={d_out:.3e} max|d lse|={d_lse:.3e}", flush=True)
+    assert d_out <= TOL_BF16 and d_lse <= TOL_LSE, (d_out, d_lse)

@@ -268,3 +268,30 @@ def test_mutations_are_caught(old, new):
     except (ValueError, IndexError):
         caught = True
     assert caught
+
+
+@pytest.mark.parametrize("L", [256, 1000])
+def test_closed_form_needles(L):
+    """The needle inputs (one matching cache key per row, all other keys and
+    values zero) have a closed-form softmax; the oracle reproduces it.  The
+    GPU tests use the same closed form where the cache is too large for the
+    oracle."""
+    from helpers import (NEEDLE_G, NEEDLE_HD, NEEDLE_T, needle_expected, needle_positions,
+                         needle_q, needle_values)
+    pos = needle_positions(L, seed=1)
+    w = needle_values(seed=1)
+    k_tok = np.zeros((L, 1, NEEDLE_HD))
+    v_tok = np.zeros((L, 1, NEEDLE_HD))
+    r = np.arange(NEEDLE_T * NEEDLE_G)
+    k_tok[pos, 0, r] = 16.0
+    v_tok[pos, 0] = w.double().numpy()
+    q = needle_q().double().numpy()
+    zeros = np.zeros((NEEDLE_T, 1, NEEDLE_HD))
+    scale = att.default_scale(NEEDLE_HD)
+    o, l = oracle.attention_rows(q, k_tok, v_tok, zeros, zeros, range(NEEDLE_T), scale)
+    o_ref, l_ref = needle_expected(L, w, scale)
+    assert np.abs(o - o_ref).max() < 1e-12
+    assert np.abs(l - l_ref).max() < 1e-12
+    # the needle carries a weight well inside (0, 1): both terms matter
+    wt = math.exp(16.0) / (math.exp(16.0) + L)
+    assert 0.5 < wt < 1.0 - 1e-5
