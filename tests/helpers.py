@@ -109,8 +109,9 @@ def needle_q():
     return q.to(torch.bfloat16)
 
 
-def needle_expected(cache_len, w, scale):
-    """Closed form above, fp64: out [T, G, HD], lse [G, T]."""
+def needle_expected(cache_len, w, scale, pos0=0):
+    """Closed form above, fp64: out [T, G, HD], lse [G, T]; chunk token t at
+    chunk position pos0 + t (it sees current tokens 0..pos0 + t)."""
     w = w.double().numpy()
     s = scale * NEEDLE_ALPHA * NEEDLE_BETA
     es = math.exp(s)
@@ -118,7 +119,7 @@ def needle_expected(cache_len, w, scale):
     out = np.zeros((NEEDLE_T, NEEDLE_G, NEEDLE_HD))
     lse = np.zeros((NEEDLE_G, NEEDLE_T))
     for t in range(NEEDLE_T):
-        n_vis = cache_len + t + 1
+        n_vis = cache_len + pos0 + t + 1
         for h in range(NEEDLE_G):
             r = t * NEEDLE_G + h
             out[t, h] = (es * w[r] + (total - w[r])) / (es + n_vis - 1)

@@ -548,6 +548,40 @@ def test_largest_shard_region(splits):
     torch.cuda.empty_cache()
 
 
+def test_largest_current_region():
+    """The longest current chunk the library accepts at NKV = 1, HD = 256
+    (4 194 271 tokens, K rows just under 2 GiB), no cache, and 16 query
+    tokens at its last positions, so each row's causal walk spans the whole
+    chunk: needle keys in k_cur (closed form as above, the needles at
+    positions every row sees)."""
+    from helpers import (NEEDLE_G, NEEDLE_HD, NEEDLE_T, needle_expected, needle_positions,
+                         needle_q, needle_values)
+    N = MAX_SHARD_LEN
+    pos0 = N - NEEDLE_T
+    pos = torch.from_numpy(needle_positions(pos0, seed=3))
+    w = needle_values(seed=3)
+    r = torch.arange(NEEDLE_T * NEEDLE_G)
+    print(f"[gpu] largest current region cur_len={N} rows at {pos0}..{N - 1}", flush=True)
+    kcur = torch.zeros(N, 1, NEEDLE_HD, dtype=torch.bfloat16, device="cuda")
+    vcur = torch.zeros_like(kcur)
+    kcur.view(N, NEEDLE_HD)[pos.cuda(), r.cuda()] = 16.0
+    vcur.view(N, NEEDLE_HD)[pos.cuda()] = w.cuda()
+    q = needle_q().cuda()
+    out = torch.full((NEEDLE_T, NEEDLE_G, NEEDLE_HD), SENTINEL, dtype=torch.bfloat16,
+                     device="cuda")
+    lse = torch.full((NEEDLE_G, NEEDLE_T), SENTINEL, dtype=torch.float32, device="cuda")
+    dims = ra.make_dims(q, kcur, 1, real_rows=NEEDLE_T, head_rows=NEEDLE_T, head_pos=pos0)
+    ra.ring_attn_prefill(q, None, None, kcur, vcur, 0, 1, ra.StripeLayout(1, 0), out, lse, dims)
+    torch.cuda.synchronize()
+    o_ref, l_ref = needle_expected(0, w, oracle.attention.default_scale(NEEDLE_HD), pos0=pos0)
+    d_out = np.abs(out.cpu().double().numpy() - o_ref).max()
+    d_lse = np.abs(lse.cpu().double().numpy() - l_ref).max()
+    print(f"    max|d out|={d_out:.3e} max|d lse|={d_lse:.3e}", flush=True)
+    assert d_out <= TOL_BF16 and d_lse <= TOL_LSE, (d_out, d_lse)
+    del kcur, vcur
+    torch.cuda.empty_cache()
+
+
 class _RepeatedRows:
     """q rows repeating a block of R0 rows (row i = block[i % R0]) without
     materialising them on the host; what the oracle indexes."""

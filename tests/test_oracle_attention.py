@@ -295,3 +295,25 @@ def test_closed_form_needles(L):
     # the needle carries a weight well inside (0, 1): both terms matter
     wt = math.exp(16.0) / (math.exp(16.0) + L)
     assert 0.5 < wt < 1.0 - 1e-5
+
+
+def test_closed_form_needles_in_current_chunk():
+    """The same closed form with no cache, the needles in the current chunk
+    and the 16 query tokens at chunk positions pos0..pos0+15."""
+    from helpers import (NEEDLE_G, NEEDLE_HD, NEEDLE_T, needle_expected, needle_positions,
+                         needle_q, needle_values)
+    N = 700
+    pos0 = N - NEEDLE_T
+    pos = needle_positions(pos0, seed=4)
+    w = needle_values(seed=4)
+    k_cur = np.zeros((N, 1, NEEDLE_HD))
+    v_cur = np.zeros((N, 1, NEEDLE_HD))
+    k_cur[pos, 0, np.arange(NEEDLE_T * NEEDLE_G)] = 16.0
+    v_cur[pos, 0] = w.double().numpy()
+    empty = np.zeros((0, 1, NEEDLE_HD))
+    scale = att.default_scale(NEEDLE_HD)
+    o, l = oracle.attention_rows(needle_q().double().numpy(), empty, empty, k_cur, v_cur,
+                                 range(NEEDLE_T), scale, positions=pos0 + np.arange(NEEDLE_T))
+    o_ref, l_ref = needle_expected(0, w, scale, pos0=pos0)
+    assert np.abs(o - o_ref).max() < 1e-12
+    assert np.abs(l - l_ref).max() < 1e-12
