@@ -143,9 +143,29 @@ def dma(i):
                   "offen lds"]
 
 
+def bound_ops():
+    """The tile's key bound, all scalar, in the shadow of the QK^T MFMAs, as
+    groups that keep each compare next to the selects that read it: lm = 1
+    for the current tiles (region wk >= P); mflag when a visit's keys end
+    inside the tile (wlim < 32), on the causal diagonal (wlim > wm31 =
+    smallest row position - 31) or past the walk (vv >= tt); lc = wlim in a
+    visit, 1 - wlim for the current tiles, -32 past the walk."""
+    return [
+        ["s_cmp_ge_i32 %[wk], %[np]", "s_cselect_b32 %[lm], 1, 0"],
+        ["s_cmp_lt_i32 %[wlim], 32", "s_cselect_b32 %[cr], 1, 0"],
+        ["s_cmp_gt_i32 %[wlim], %[wm31]", "s_cselect_b32 %[cc], 1, 0"],
+        ["s_sub_i32 %[lc], 1, %[wlim]"],
+        ["s_cmp_eq_u32 %[lm], 0", "s_cselect_b32 %[mflag], %[cr], %[cc]",
+         "s_cselect_b32 %[lc], %[wlim], %[lc]"],
+        ["s_cmp_ge_i32 %[vv], %[tt]", "s_cselect_b32 %[mflag], 1, %[mflag]",
+         "s_cselect_b32 %[lm], 0, %[lm]", "s_cselect_b32 %[lc], -32, %[lc]"],
+    ]
+
+
 def qk_part():
     # KPRE was read by the block before (or before the loop): wait for it.
     out = ["s_nop 1", "s_waitcnt lgkmcnt(0)"]
+    bound = bound_ops()
     for k in range(NKS):
         wait = None
         if k + 2 < NKS:
@@ -165,18 +185,29 @@ def qk_part():
             out.append(f"v_mfma_f32_32x32x16_bf16 {stile(rb)}, {kop(k)}, {qop(rb, k)}, {c}")
         if k % 2 == 1:  # one copy of the next tiles per two k-steps
             out += dma(k // 2)
+        elif k // 2 < len(bound):
+            out += bound[k // 2]
     return out
 
 
 def mask_part():
     """Keys at or past the row's bound -> -inf, only when the flag is set.
-    Lane half h holds keys 8 (i / 4) + 4 h + i % 4 of the tile; lim = bound
-    - 4 h, so key slot i is kept iff 8 (i / 4) + i % 4 < lim."""
-    out = ["s_cmp_eq_u32 %[mflag], 0", "s_cbranch_scc1 1f", "s_nop 7", "s_nop 7"]
+    The bound of row block rb is lc (a visit's keys left, lm = 0) or
+    pos_rb + lc (current tiles, lm = 1: lc = 1 - first key's position).
+    Lane half h holds keys 8 (i / 4) + 4 h + i % 4 of the tile; with lim =
+    bound - 4 h, key slot i is kept iff 8 (i / 4) + i % 4 < lim."""
+    out = ["s_cmp_eq_u32 %[mflag], 0", "s_cbranch_scc1 1f",
+           "v_mbcnt_lo_u32_b32 %[a0], -1, 0", "v_mbcnt_hi_u32_b32 %[a0], -1, %[a0]",
+           "v_lshrrev_b32 %[a0], 5, %[a0]", "v_lshlrev_b32 %[a0], 2, %[a0]",  # 4 h
+           "s_cmp_eq_u32 %[lm], 0", "s_cbranch_scc0 2f"]
+    out += [f"v_sub_u32 %[th{rb}], %[lc], %[a0]" for rb in range(NRB)] + ["s_branch 3f", "2:"]
+    out += [f"v_sub_u32 %[th{rb}], %[pos{rb}], %[a0]" for rb in range(NRB)]
+    out += [f"v_add_u32 %[th{rb}], %[lc], %[th{rb}]" for rb in range(NRB)]
+    out += ["3:", "s_nop 7", "s_nop 7"]
     for rb in range(NRB):
         for i in range(16):
             c = 8 * (i // 4) + i % 4
-            out.append(f"v_sub_u32 %[a0], {c}, %[lim{rb}]")   # < 0 iff kept
+            out.append(f"v_sub_u32 %[a0], {c}, %[th{rb}]")    # < 0 iff kept
             out.append("v_ashrrev_i32 %[a0], 31, %[a0]")      # all ones iff kept
             out.append(f"v_bfi_b32 {s(rb, i)}, %[a0], {s(rb, i)}, %[ninf]")
     out.append("1:")

@@ -202,12 +202,14 @@ __device__ __forceinline__ float wave_max_pair(float x) {
       [al1] "=&v"(al[1]), [any] "=&s"(any),                                                    \
       [a0] "=&v"(a0), [b0] "=&v"(b0), [a1] "=&v"(a1), [b1] "=&v"(b1), [th0] "=&v"(th0),       \
       [th1] "=&v"(th1), [r0] "=&v"(r0), [r1] "=&v"(r1), [c0] "=&s"(c0), [c1] "=&s"(c1),        \
-      [st] "=&s"(st), RA_TILE_HD256_KPRE_OPERANDS
+      [st] "=&s"(st), [mflag] "=&s"(mflag), [lc] "=&s"(lc), [lm] "=&s"(lm), [cr] "=&s"(cr),     \
+      [cc] "=&s"(cc), RA_TILE_HD256_KPRE_OPERANDS
 #define RA_TILE_INPUT_OPERANDS                                                                  \
   [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [ka2] "v"(ka[2]), [ka3] "v"(ka[3]), [ka4] "v"(ka[4]),    \
       [ka5] "v"(ka[5]), [ka6] "v"(ka[6]), [ka7] "v"(ka[7]), [va0] "v"(va[0]), [va1] "v"(va[1]), \
-      [va2] "v"(va[2]), [va3] "v"(va[3]), [c2] "s"(c2), [tau] "s"(tau), [mflag] "s"(mflag),     \
-      [lim0] "v"(lim[0]), [lim1] "v"(lim[1]), [ninf] "v"(ninf), [ko0] "i"(KOFF),                \
+      [va2] "v"(va[2]), [va3] "v"(va[3]), [c2] "s"(c2), [tau] "s"(tau), [wk] "s"(wb.k),         \
+      [np] "s"(wb.np), [wlim] "s"(wb.lim), [wm31] "s"(wb.wm31), [vv] "s"(wb.v), [tt] "s"(wb.t),  \
+      [pos0] "v"(pos[0]), [pos1] "v"(pos[1]), [ninf] "v"(ninf), [ko0] "i"(KOFF),                \
       [ko1] "i"(KOFF + 256), [vo000] "i"(VOFF), [vo001] "i"(VOFF + 4096),                       \
       [vo010] "i"(VOFF + 256), [vo011] "i"(VOFF + 256 + 4096), [vo100] "i"(VOFF + 8192),        \
       [vo101] "i"(VOFF + 8192 + 4096), [vo110] "i"(VOFF + 8192 + 256),                          \
@@ -232,6 +234,13 @@ __device__ __forceinline__ void fold_sum(float& l, float& c, float a, float r) {
   l = t;
 }
 
+struct TileBound {    // what the block derives the tile's key bound from (uniform)
+  int k, np;          // the tile's region and P (k >= P: current tiles)
+  int lim;            // a visit's keys left from the tile, or its first key's position
+  int wm31;           // smallest chunk position of the workgroup's rows - 31
+  int v, t;           // the tile and the walk's length (v >= t: past the walk)
+};
+
 struct CopyLanes {    // a lane's offsets for the block's LDS-DMA copies (see below)
   uint32_t ka, kb, va, vb;
   uint32_t rs16;      // 16 rows' stride in bytes (uniform)
@@ -243,13 +252,14 @@ __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], const bf16x8 (&p
                                            const uint32_t (&va)[4],
                                            float (&ml)[2], float (&l)[2], float (&lk)[2],
                                            float (&al)[2],
-                                           uint64_t& any, float c2, float tau, uint32_t mflag,
-                                           const int (&lim)[2], const i32x4& desck,
+                                           uint64_t& any, float c2, float tau,
+                                           const TileBound& wb, const int (&pos)[2],
+                                           const i32x4& desck,
                                            const i32x4& descv, uint32_t offk, uint32_t offv,
                                            uint32_t m0b, const CopyLanes& dl) {
 #if defined(__HIP_DEVICE_COMPILE__)
   float a0, b0, a1, b1, th0, th1, r0, r1;
-  uint32_t st;
+  uint32_t st, mflag, lc, lm, cr, cc;
   uint64_t c0, c1;
   const float ninf = kNegInf;
   if constexpr (PIN == 0) {
@@ -385,68 +395,67 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   const uint32_t cur_bytes = (uint32_t)(wg_max_pos + 1) * rowstride;
   const int full_i = (int)p.full * p.interleave;  // < 2^31: bounded by a shard's length
 
-  // Per-tile source, chosen by value: descriptors of the region (sized to
-  // its valid rows), the tile's first byte, and the key bound.
-  struct Src {
-    i32x4 kr, vr;
-    uint32_t off;     // byte offset of the tile's first row
-    int lim_ring;     // ring: valid keys of the shard left from this tile
-    int key0;         // current: chunk position of the tile's first key
-    bool in_ring;
+  // The walk, one tile at a time from virtual tile v0: region k < P is the
+  // visit of shard (ring_start - k) mod P (nb tiles), region P the current
+  // tiles (n_cur), regions past it zero-size fetches (the slot fills with
+  // zeros).  Three walkers hold one position of it each: the K copy two
+  // tiles ahead, the V copy one tile ahead and the tile being computed
+  // (its key bound).  A step adds to an offset and a bound; only entering
+  // the next region, once per nb tiles, builds a descriptor.  The region's
+  // descriptor is sized to its valid rows, so rows past them load as zeros.
+  // Everything here is wave-uniform.
+  struct Walker {
+    uint32_t lo, hi, size;  // the region's K or V descriptor (base address, bytes)
+    uint32_t off;           // byte offset of the tile's first row
+    int lim;                // ring: valid keys of the visit left from this tile;
+                            // current: chunk position of the tile's first key
+    int left;               // tiles of the region from this one on
+    int k;                  // region
   };
-  // The walk, one tile per call, from virtual tile v0: shard visit k (ring
-  // order), tile b within it, then the current tiles c; past the end,
-  // zero-size fetches (the slot fills with zeros).  Everything here is
-  // wave-uniform.
-  int wk, wb = 0, wc = 0;
-  if (v0 < n_ring) {
-    wk = v0 / p.nb;
-    wb = v0 - wk * p.nb;
-  } else {
-    wk = p.P;
-    wc = v0 - n_ring;
-  }
-  i32x4 vis_k, vis_v;
-  int vis_len = 0;
-  auto load_visit = [&]() RA_INLINE {  // shard visit wk: its descriptors and length
-    if (wk < p.P) {
-      int sh = p.ring_start - wk;
+  // enter region k at its tile b; side 0: K, 1: V
+  auto enter = [&](Walker& w, int k, int b, int side) RA_INLINE {
+    uint64_t base;
+    w.k = k;
+    if (k < p.P) {
+      int sh = p.ring_start - k;
       sh += (sh < 0) ? p.P : 0;
-      vis_len = full_i + min(max((int)p.rem - sh * p.interleave, 0), p.interleave);
-      const int64_t base = ((int64_t)sh * p.shard_cap * p.nkv + g) * D;
-      const uint32_t bytes = (uint32_t)vis_len * rowstride;
-      vis_k = make_desc(p.k_cache + base, bytes);
-      vis_v = make_desc(p.v_cache + base, bytes);
-    }
-  };
-  load_visit();
-  auto next_src = [&]() RA_INLINE {
-    Src s;
-    if (wk < p.P) {
-      s.kr = vis_k;
-      s.vr = vis_v;
-      s.off = (uint32_t)wb * tile_stride;
-      s.lim_ring = vis_len - wb * kBKV;
-      s.key0 = 0;
-      s.in_ring = true;
-      if (++wb == p.nb) {
-        wb = 0;
-        ++wk;
-        load_visit();
-      }
+      const int len = full_i + min(max((int)p.rem - sh * p.interleave, 0), p.interleave);
+      base = (uint64_t)(uintptr_t)(side ? p.v_cache : p.k_cache) +
+             (uint64_t)(((int64_t)sh * p.shard_cap * p.nkv + g) * D) * 2u;
+      w.size = (uint32_t)len * rowstride;
+      w.lim = len - b * kBKV;
+      w.left = p.nb - b;
     } else {
-      const bool live = wc < n_cur;
-      s.kr = make_desc(p.k_cur + g * D, live ? cur_bytes : 0u);
-      s.vr = make_desc(p.v_cur + g * D, live ? cur_bytes : 0u);
-      s.off = live ? (uint32_t)wc * tile_stride : 0u;
-      s.lim_ring = 0;
-      s.key0 = wc * kBKV;
-      s.in_ring = false;
-      wc += live ? 1 : 0;
+      base = (uint64_t)(uintptr_t)(side ? p.v_cur : p.k_cur) + (uint64_t)g * D * 2u;
+      const bool cur = k == p.P && b < n_cur;
+      w.size = cur ? cur_bytes : 0u;
+      w.lim = b * kBKV;
+      w.left = cur ? n_cur - b : (1 << 30);
     }
-    return s;
+    w.lo = (uint32_t)base;
+    w.hi = (uint32_t)(base >> 32) & 0xffffu;
+    w.off = (uint32_t)b * tile_stride;
   };
-
+  // one tile on; the region ends after `left` tiles
+  auto step = [&](Walker& w, int side) RA_INLINE {
+    w.off += tile_stride;
+    w.lim += w.k < p.P ? -kBKV : kBKV;
+    if (__builtin_expect(--w.left == 0, 0)) enter(w, w.k + 1, 0, side);
+  };
+  // the walkers at this workgroup's first tile
+  Walker wk_, wv_, wb_;
+  {
+    int k0 = p.P, b0 = v0 - n_ring;
+    if (n_ring == 0) {
+      k0 = p.P;
+    } else if (v0 < n_ring) {
+      k0 = v0 / p.nb;
+      b0 = v0 - k0 * p.nb;
+    }
+    enter(wk_, k0, b0, 0);
+    enter(wv_, k0, b0, 1);
+    wb_ = wk_;
+  }
   // DMA: wave-instruction i of this wave fills physical chunks
   // [(wave*DPW + i)*64, +64) of a tile, lane L the chunk at +L; the lane
   // fetches the logical chunk that the swizzle stores there.  The swizzles
@@ -461,20 +470,25 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       (uint32_t)dma_r * rowstride + (uint32_t)((dma_pc ^ swz_k(dma_r, CPR)) << 4);
   const uint32_t dma_vbase =
       (uint32_t)dma_r * rowstride + (uint32_t)((dma_pc ^ swz_v(dma_r, CPR)) << 4);
-  auto issue_k = [&](const Src& s, uint16_t* dst) RA_INLINE {
+  auto desc_of = [](const Walker& w) RA_INLINE {
+    return i32x4{(int)w.lo, (int)w.hi, (int)w.size, 0x00020000};
+  };
+  auto issue_k = [&](const Walker& w, uint16_t* dst) RA_INLINE {
+    const i32x4 d = desc_of(w);
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int R = (wave * DPW + i) * RPI;
-      dma16(s.kr, dst + (wave * DPW + i) * 512, dma_kbase ^ (uint32_t)(swz_k(R, CPR) << 4),
-            s.off + (uint32_t)R * rowstride);
+      dma16(d, dst + (wave * DPW + i) * 512, dma_kbase ^ (uint32_t)(swz_k(R, CPR) << 4),
+            w.off + (uint32_t)R * rowstride);
     }
   };
-  auto issue_v = [&](const Src& s, uint16_t* dst) RA_INLINE {
+  auto issue_v = [&](const Walker& w, uint16_t* dst) RA_INLINE {
+    const i32x4 d = desc_of(w);
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int R = (wave * DPW + i) * RPI;
-      dma16(s.vr, dst + (wave * DPW + i) * 512, dma_vbase ^ (uint32_t)(swz_v(R, CPR) << 4),
-            s.off + (uint32_t)R * rowstride);
+      dma16(d, dst + (wave * DPW + i) * 512, dma_vbase ^ (uint32_t)(swz_v(R, CPR) << 4),
+            w.off + (uint32_t)R * rowstride);
     }
   };
   // The copies issued from the HD = 256 tile block split the rows another
@@ -642,15 +656,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
 
   // Region by value: each row's key bound within the tile, and whether any
   // bound of the workgroup cuts into the tile (then the compare is needed).
-  auto bounds = [&](const Src& src, int (&lim)[NRB]) RA_INLINE {
-    if (src.in_ring) {
+  auto bounds = [&](const Walker& w, int (&lim)[NRB]) RA_INLINE {
+    const bool ring = w.k < p.P;
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) lim[rb] = src.lim_ring;
-      return src.lim_ring < kBKV;
-    }
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) lim[rb] = pos[rb] + 1 - src.key0;
-    return src.key0 + kBKV > wg_min_pos + 1;
+    for (int rb = 0; rb < NRB; ++rb) lim[rb] = ring ? w.lim : pos[rb] + 1 - w.lim;
+    return ring ? w.lim < kBKV : w.lim + kBKV > wg_min_pos + 1;
   };
 
   // P.V of the previous tile with the softmax of the current one (generic
@@ -737,16 +747,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // this workgroup's walk (t >= T) are fully masked: pass T carries the P.V
   // of the last tile.  Tile 0 runs the same body: its "previous" V slot is
   // filled with zeros and the probabilities start at zero.
-  Src c0 = next_src(), c1 = next_src();  // tiles 2j, 2j+1
-  Src n0 = next_src(), n1 = next_src();  // tiles 2j+2, 2j+3
   {
-    Src zero = c0;
-    zero.vr = make_desc(p.v_cur, 0);  // a zero-size fetch: the slot fills with zeros
+    Walker zero = wv_;
+    zero.size = 0;  // a zero-size fetch: the slot fills with zeros
     zero.off = 0;
-    issue_k(c0, kslot(0));
-    issue_k(c1, kslot(1));
+    issue_k(wk_, kslot(0));
+    step(wk_, 0);
+    issue_k(wk_, kslot(1));
+    step(wk_, 0);  // K copies run two tiles ahead ...
     issue_v(zero, vslot(3));
-    issue_v(c0, vslot(0));
+    issue_v(wv_, vslot(0));
+    step(wv_, 1);  // ... V copies one
   }
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
@@ -768,7 +779,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   bool any = false;       // the previous tile asked for a rescale ...
   float alpha[NRB];       // ... by these factors
   auto rescale = [&]() RA_INLINE {
-    if (any) {
+    if (__builtin_expect(any, 0)) {
 #if defined(__HIP_DEVICE_COMPILE__)
       // the last P.V MFMAs may still be writing acc: wait them out
       asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
@@ -807,46 +818,43 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
 #endif
     if constexpr (SL % 2 == 0 && !ASM256) {  // start of a pair: the copies of the next pair
       if (v + 2 <= T) {
-        issue_k(n0, kslot((SL + 2) % 4));
-        issue_k(n1, kslot((SL + 3) % 4));
-        issue_v(c1, vslot((SL + 1) % 4));
-        issue_v(n0, vslot((SL + 2) % 4));
+        issue_k(wk_, kslot((SL + 2) % 4));
+        step(wk_, 0);
+        issue_k(wk_, kslot((SL + 3) % 4));
+        step(wk_, 0);
+        issue_v(wv_, vslot((SL + 1) % 4));
+        step(wv_, 1);
+        issue_v(wv_, vslot((SL + 2) % 4));
+        step(wv_, 1);
       }
     }
-    int lim[NRB];
-    bool cut = bounds(SL % 2 == 0 ? c0 : c1, lim);
-    if (v >= T) {  // past the walk: every key masked
-      cut = true;
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) lim[rb] = -kBKV;
-    }
     if constexpr (ASM256) {
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) lim[rb] -= 4 * h;
+      // the block derives the key bound from these (scalar, in the shadow
+      // of its QK^T MFMAs)
+      const TileBound tb{wb_.k, p.P, wb_.lim, wg_min_pos - 31, v, T};
+      step(wb_, 0);
       uint64_t anyf;
       // tile v's probabilities go to buffer v & 1; tile v-1's are read
       constexpr int PB = SL & 1;
-      // this block's copies: K of tile v + 2 and V of tile v + 1 (for an
-      // even v the sources are n0 and c1, for an odd v n1 and n0)
-      const Src& ks = SL % 2 == 0 ? n0 : n1;
-      const Src& vs = SL % 2 == 0 ? c1 : n0;
-      const i32x4 dkr = {__builtin_amdgcn_readfirstlane(ks.kr[0]),
-                         __builtin_amdgcn_readfirstlane(ks.kr[1]),
-                         __builtin_amdgcn_readfirstlane(ks.kr[2]),
-                         __builtin_amdgcn_readfirstlane(ks.kr[3])};
-      const i32x4 dvr = {__builtin_amdgcn_readfirstlane(vs.vr[0]),
-                         __builtin_amdgcn_readfirstlane(vs.vr[1]),
-                         __builtin_amdgcn_readfirstlane(vs.vr[2]),
-                         __builtin_amdgcn_readfirstlane(vs.vr[3])};
+      // this block's copies: K of tile v + 2 and V of tile v + 1
+      const i32x4 dkr = desc_of(wk_), dvr = desc_of(wv_);
       tile_hd256<SL * TILE_B, ((SL + 3) % 4) * TILE_B, PB ^ 1, ((SL + 2) % 4) * TILE_B,
                  VBASE + ((SL + 1) % 4) * TILE_B, ((SL + 1) % 4) * TILE_B>(
           acc, pbuf[PB ^ 1], pbuf[PB], qreg, kpre, ka, va, mlog, lsum, lcomp, alpha, anyf, c2,
-          kTau<F32OUT>, __builtin_amdgcn_readfirstlane(cut ? 1u : 0u), lim, dkr, dvr,
-          __builtin_amdgcn_readfirstlane(ks.off), __builtin_amdgcn_readfirstlane(vs.off), m0b,
-          dl);
+          kTau<F32OUT>, tb, pos, dkr, dvr, wk_.off, wv_.off, m0b, dl);
+      step(wk_, 0);
+      step(wv_, 1);
       any = anyf != 0;
       sum_rounded(pbuf[PB]);
     } else {
+      int lim[NRB];
+      bool cut = bounds(wb_, lim);
+      step(wb_, 0);
+      if (v >= T) {  // past the walk: every key masked
+        cut = true;
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) lim[rb] = -kBKV;
+      }
       f32x16 S[NRB][NKB];
       qk(kslot(SL), S);
       if (cut) mask(S, lim);
@@ -861,10 +869,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
         __syncthreads();
       }
-      c0 = n0;
-      c1 = n1;
-      n0 = next_src();
-      n1 = next_src();
     }
   };
   // Tiles 0 .. T (pass T is the P.V of the last tile), four per trip so that

@@ -7,8 +7,9 @@ that follows a block must not, before those MFMAs are done, write a
 register the block's last two MFMAs read or touch a register they write.
 Inside the block this holds by construction; this test checks the
 compiler's side on the device assembly of the kernel as it is built: the
-first WINDOW instructions after every tile block do none of that unless two
-s_nop 15 (32 wait states) come first.  A block may also leave LDS reads of
+first WINDOW instructions after every tile block (up to the next asm
+statement) do none of that unless two s_nop 15 (32 wait states) come
+first.  A block may also leave LDS reads of
 the next tile's first K operands (KPRE) in flight, so no compiler
 instruction between two blocks may touch those registers.
 """
@@ -75,6 +76,8 @@ def hazards_after(lines, at, mfmas):
         src |= regs(ops[1]) | regs(ops[2])
     found, n, nops = [], 0, 0
     for line in lines[at:at + 10 * WINDOW]:
+        if ";;#ASMSTART" in line:  # the next block: its ring refills are LDS reads, as inside
+            break                  # a block, landing long after an MFMA has read its operands
         ins = line.split(";")[0].strip()
         if not ins or ins.startswith("."):
             continue
