@@ -249,10 +249,12 @@ def softmax_ops(pout):
         ops.append(("valu", f"v_cmp_gt_f32_e64 %[c{rb}], %[a{rb}], %[th{rb}]"))
     for rb in range(NRB):
         ops.append(("valu", f"v_max_f32 %[b{rb}], %[ml{rb}], %[a{rb}]"))
-    ops.append(("salu", "s_or_b64 %[any], %[c0], %[c1]"))
+    # c{rb}: all ones if some row of the block voted; bit rb of resc the same
     for rb in range(NRB):
         ops.append(("salu", f"s_cmp_lg_u64 %[c{rb}], 0"))
         ops.append(("salu", f"s_cselect_b64 %[c{rb}], -1, 0"))
+        ops.append(("salu", f"s_cselect_b32 %[v{rb}], {1 << rb}, 0"))
+    ops.append(("salu", "s_or_b32 %[resc], %[v0], %[v1]"))
     ops.append(("nop", "s_nop 1"))
     for rb in range(NRB):  # m_new
         ops.append(("valu", f"v_cndmask_b32_e64 %[b{rb}], %[ml{rb}], %[b{rb}], %[c{rb}]"))

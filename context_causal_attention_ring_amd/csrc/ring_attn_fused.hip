@@ -173,8 +173,8 @@ __device__ __forceinline__ float wave_max_pair(float x) {
 // and leaves it in flight (the next block waits for it).  On return pout
 // holds tile v's bf16 probabilities, ml and l the updated running max (log2
 // units) and row sums, al the factor the accumulator must be scaled by, and
-// `any` is non-zero when some row of the wave asked for that rescale (al ==
-// 1 for every row otherwise).
+// bit rb of resc is set when some row of row block rb asked for that
+// rescale (al == 1 for every row of the other blocks).
 //   ka[j]  LDS address of this lane's K row at chunk (2j + h) ^ swizzle;
 //          k-step s reads ka[s % 8] + KOFF + 256 (s / 8)
 //   va[d]  LDS address of this lane's transposed V read for d blocks d and
@@ -199,9 +199,9 @@ __device__ __forceinline__ float wave_max_pair(float x) {
       [acc14] "+a"(acc[1][4]), [acc15] "+a"(acc[1][5]), [acc16] "+a"(acc[1][6]),               \
       [acc17] "+a"(acc[1][7]), [ml0] "+v"(ml[0]), [ml1] "+v"(ml[1]), [l0] "+v"(l[0]),          \
       [l1] "+v"(l[1]), [lk0] "+v"(lk[0]), [lk1] "+v"(lk[1]), [al0] "=&v"(al[0]),               \
-      [al1] "=&v"(al[1]), [any] "=&s"(any),                                                    \
+      [al1] "=&v"(al[1]), [resc] "=&s"(resc),                                                    \
       [a0] "=&v"(a0), [b0] "=&v"(b0), [a1] "=&v"(a1), [b1] "=&v"(b1), [th0] "=&v"(th0),       \
-      [th1] "=&v"(th1), [r0] "=&v"(r0), [r1] "=&v"(r1), [c0] "=&s"(c0), [c1] "=&s"(c1),        \
+      [th1] "=&v"(th1), [r0] "=&v"(r0), [r1] "=&v"(r1), [c0] "=&s"(c0), [c1] "=&s"(c1), [v0] "=&s"(v0), [v1] "=&s"(v1),        \
       [st] "=&s"(st), [mflag] "=&s"(mflag), [lc] "=&s"(lc), [lm] "=&s"(lm), [cr] "=&s"(cr),     \
       [cc] "=&s"(cc), RA_TILE_HD256_KPRE_OPERANDS
 #define RA_TILE_INPUT_OPERANDS                                                                  \
@@ -252,14 +252,14 @@ __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], const bf16x8 (&p
                                            const uint32_t (&va)[4],
                                            float (&ml)[2], float (&l)[2], float (&lk)[2],
                                            float (&al)[2],
-                                           uint64_t& any, float c2, float tau,
+                                           uint32_t& resc, float c2, float tau,
                                            const TileBound& wb, const int (&pos)[2],
                                            const i32x4& desck,
                                            const i32x4& descv, uint32_t offk, uint32_t offv,
                                            uint32_t m0b, const CopyLanes& dl) {
 #if defined(__HIP_DEVICE_COMPILE__)
   float a0, b0, a1, b1, th0, th1, r0, r1;
-  uint32_t st, mflag, lc, lm, cr, cc;
+  uint32_t st, mflag, lc, lm, cr, cc, v0, v1;
   uint64_t c0, c1;
   const float ninf = kNegInf;
   if constexpr (PIN == 0) {
@@ -596,43 +596,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     }
   };
 
-  // Online softmax of one tile, in place: S becomes the probabilities
-  // (fp32).  alpha[rb] is the factor the accumulator must be scaled by (1
-  // unless some row of the wave raised its running max by more than kTau;
-  // the return value reports whether any did).  lsum is the exact fp32 row
-  // sum (for the LSE and, with bf16 output, the normalisation); for fp32
-  // output the normalisation uses lsum_q instead (see pack).
-  auto softmax = [&](f32x16 (&S)[NRB][NKB], float (&alpha)[NRB]) RA_INLINE {
-    bool any = false;
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2)
-          mx = __builtin_elementwise_maximum(
-              mx, __builtin_elementwise_maximum(S[rb][kb][i], S[rb][kb][i + 1]));
-      mx = wave_max_pair(mx) * c2;  // scale > 0, so max commutes with the scaling
-      const bool need = mx > mlog[rb] + kTau<F32OUT>;
-      const bool anyrb = __builtin_amdgcn_ballot_w64(need) != 0;
-      const float m_new = anyrb ? __builtin_elementwise_maximum(mlog[rb], mx) : mlog[rb];
-      alpha[rb] = (m_new == mlog[rb]) ? 1.f : __builtin_amdgcn_exp2f(mlog[rb] - m_new);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          S[rb][kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[rb][kb][i], c2, -m_use));
-          ls += S[rb][kb][i];
-        }
-      fold_sum(lsum[rb], lcomp[rb], alpha[rb], ls);
-      mlog[rb] = m_new;
-      any |= anyrb;
-    }
-    return any;
-  };
   // Probabilities -> bf16 B operands of P.V.  For fp32 output also the sum
   // of the bf16-rounded probabilities (v_dot2 against (1, 1)): numerator
   // and denominator then weight every key identically.
@@ -668,7 +631,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // operand, read two slots ahead, for every row block) and then a fixed
   // slice of softmax work.  Softmax work units, in dependency order: the
   // in-lane max of each row block, the cross-lane reduction and new running
-  // max, one exp2 per score, the row sums.
+  // max, one exp2 per score, the row sums.  Returns the row blocks whose
+  // rows must rescale the accumulator (al; 1 for the other rows).
   auto pv_softmax = [&](const uint16_t* vt, f32x16 (&S)[NRB][NKB], float (&al)[NRB]) RA_INLINE {
     constexpr int NT = NPS * NDB;                  // P.V steps
     constexpr int NE = NRB * NKB * 16;              // exp2 units
@@ -682,7 +646,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       return __builtin_bit_cast(bf16x8, x);
     };
     float mx[NRB], m_use[NRB], ls[NRB];
-    bool any = false;
+    uint32_t any = 0;  // row blocks asking for a rescale
     auto unit = [&](int u) RA_INLINE {
       if (u < NRB) {  // in-lane max of row block u
         float m = kNegInf;
@@ -704,7 +668,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
           m_use[rb] = m_new == kNegInf ? 0.f : m_new;
           mlog[rb] = m_new;
           ls[rb] = 0.f;
-          any |= anyrb;
+          any |= anyrb ? 1u << rb : 0u;
         }
       } else if (u < NRB + 1 + NE) {  // one probability
         const int q = u - NRB - 1;
@@ -776,18 +740,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
                  : "memory");
 #endif
 
-  bool any = false;       // the previous tile asked for a rescale ...
-  float alpha[NRB];       // ... by these factors
+  uint32_t resc = 0;      // row blocks whose rows the previous tile asked to rescale ...
+  float alpha[NRB];       // ... by these factors (1 for the other rows)
   auto rescale = [&]() RA_INLINE {
-    if (__builtin_expect(any, 0)) {
+    if (__builtin_expect(resc != 0, 0)) {
 #if defined(__HIP_DEVICE_COMPILE__)
       // the last P.V MFMAs may still be writing acc: wait them out
       asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
 #endif
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
+        if (resc & (1u << rb)) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) scale_agprs(acc[rb][db], alpha[rb]);
+          for (int db = 0; db < NDB; ++db) scale_agprs(acc[rb][db], alpha[rb]);
+        }
     }
   };
   // For fp32 output: the row sums over the bf16-rounded probabilities.
@@ -833,18 +799,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       // of its QK^T MFMAs)
       const TileBound tb{wb_.k, p.P, wb_.lim, wg_min_pos - 31, v, T};
       step(wb_, 0);
-      uint64_t anyf;
+
       // tile v's probabilities go to buffer v & 1; tile v-1's are read
       constexpr int PB = SL & 1;
       // this block's copies: K of tile v + 2 and V of tile v + 1
       const i32x4 dkr = desc_of(wk_), dvr = desc_of(wv_);
       tile_hd256<SL * TILE_B, ((SL + 3) % 4) * TILE_B, PB ^ 1, ((SL + 2) % 4) * TILE_B,
                  VBASE + ((SL + 1) % 4) * TILE_B, ((SL + 1) % 4) * TILE_B>(
-          acc, pbuf[PB ^ 1], pbuf[PB], qreg, kpre, ka, va, mlog, lsum, lcomp, alpha, anyf, c2,
+          acc, pbuf[PB ^ 1], pbuf[PB], qreg, kpre, ka, va, mlog, lsum, lcomp, alpha, resc, c2,
           kTau<F32OUT>, tb, pos, dkr, dvr, wk_.off, wv_.off, m0b, dl);
       step(wk_, 0);
       step(wv_, 1);
-      any = anyf != 0;
       sum_rounded(pbuf[PB]);
     } else {
       int lim[NRB];
@@ -858,7 +823,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       f32x16 S[NRB][NKB];
       qk(kslot(SL), S);
       if (cut) mask(S, lim);
-      any = pv_softmax(vslot((SL + 3) % 4), S, alpha);
+      resc = pv_softmax(vslot((SL + 3) % 4), S, alpha);
       pack(S, pb, alpha);
     }
 #ifdef RA_SYNC_EVERY_TILE
