@@ -134,6 +134,10 @@ FULL_CASES = [
           tail_rows=40),
     small("mha", nq=2, nkv=2, hd=256, cache_len=129, P=2, real_rows=65, head_rows=33,
           tail_rows=33),
+    # 64 shards of 10-11 tokens: every visit is one partial tile, so the walk
+    # enters a new region at every tile
+    small("P64-one-tile-visits", nq=32, nkv=2, hd=256, cache_len=700, P=64, head_rows=96,
+          tail_rows=96, real_rows=192),
 ]
 
 
@@ -423,7 +427,7 @@ def run_split(case, splits, out_fp32=False):
 
 SPLIT_CASES = [(workloads.CONFIGS["tiny"], 3), (FULL_CASES[1], 2), (FULL_CASES[2], 7),
                (RANK_CASES[2], 5), (small("split-nocache", cache_len=0, P=1), 4),
-               (small("split-many", cache_len=1000, P=3), 64)]
+               (small("split-many", cache_len=1000, P=3), 64), (FULL_CASES[-1], 7)]
 
 
 @pytest.mark.parametrize("w,splits", SPLIT_CASES, ids=lambda x: getattr(x, "name", str(x)))
