@@ -75,11 +75,18 @@ def torch_device_index():
 
 
 def fused_source_sha():
-    """sha256 over the fused kernel's sources (the kernel and its generated tile block)."""
+    """sha256 over the fused kernel's sources (the kernel and its generated
+    tile block), comments and blank space left out: a comment edit does not
+    change the kernel the counters were taken on.  (No string literal in
+    these sources holds a comment marker.)"""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in FUSED_SOURCES:
-        h.update(open(f, "rb").read())
+        text = open(f).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -26,7 +26,10 @@
 //    staging) into four K and four V slots (tile t in slot t mod 4).  Tiles
 //    run in pairs with one wait and one barrier per pair; while a pair is
 //    computed, the copies of the next pair (K two tiles ahead, V one tile
-//    behind it) are in flight, issued between the score MFMAs.
+//    behind it) are in flight, issued between the score MFMAs.  Their
+//    sources, and each tile's key bound, come from three scalar walkers
+//    (region descriptor, tile offset, bound, tiles left) that step with two
+//    adds and build a descriptor only on entering the next region.
 //    Rows are stored with a 16-byte-chunk XOR swizzle chosen per operand so
 //    that K reads (32 rows, one chunk) and transposed V reads
 //    (ds_read_b64_tr_b16, 4 rows x 4 chunks) are both bank-conflict free.
@@ -37,10 +40,10 @@
 //    one bound per row, key < lim, with lim = shard length in the ring
 //    region and token + 1 (causal) in the current region; tiles that no
 //    bound cuts skip the compare entirely.
-//  * Online softmax in log2 units with a lazy running max: the
-//    accumulator is rescaled only when some row's max grows by more than
-//    kTau (a wave vote), so the common tile costs max, fma, exp2, add and
-//    a bf16 pack per score.  The softmax of tile v is issued between the
+//  * Online softmax in log2 units with a lazy running max: a 32-row block
+//    of the accumulator is rescaled only when some row of it raised its max
+//    by more than kTau (a vote), so the common tile costs max, fma, exp2,
+//    add and a bf16 pack per score.  The softmax of tile v is issued between the
 //    P.V MFMAs of tile v-1, which do not depend on it, in a hand-ordered
 //    block (one MFMA pair, one V operand read, a slice of softmax work).
 //  * Workgroup ids are remapped so that the workgroups resident on one XCD
