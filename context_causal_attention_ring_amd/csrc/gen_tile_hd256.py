@@ -312,6 +312,73 @@ def softmax_ops(pout):
     return ops
 
 
+def softmax_ops_stale(pout):
+    """The common case of tile v's online softmax (bf16 output): every score
+    is taken against the running max as it stands (a row that has seen no
+    key yet uses -FLT_MAX), the tile's row sums r and the bf16 packing as
+    in softmax_ops, and l = l + r compensated (alpha = 1).  Valid while
+    every probability is at most 2^tau, which r <= 2^tau (pbnd) proves:
+    otherwise (a row's max grew by more than tau, or the first tile) the
+    block's slow path recomputes the tile with softmax_ops.  l and lk are
+    kept in th and al (unused here) for that path."""
+    ops = [("nop", "s_nop 4"), ("salu", "s_mov_b32 %[resc], 0")]
+    for rb in range(NRB):
+        ops.append(("valu", f"v_max_f32 %[a{rb}], 0xff7fffff, %[ml{rb}]"))
+    streams = []
+    for rb in range(NRB):
+        st = []
+        for i in range(16):
+            st.append(("valu", f"v_fma_f32 {s(rb, i)}, {s(rb, i)}, %[c2], -%[a{rb}]"))
+            if i == 2:
+                st.append(("valu", f"v_add_f32 %[r{rb}], {s(rb, 0)}, {s(rb, 1)}"))
+            elif i > 2:
+                st.append(("valu", f"v_add_f32 %[r{rb}], %[r{rb}], {s(rb, i - 1)}"))
+            if i >= 2 and i % 2 == 0:
+                j = i // 2 - 1
+                st.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, j)}, {s(rb, 2 * j)}, "
+                                   f"{s(rb, 2 * j + 1)}"))
+            st.append(("trans", f"v_exp_f32 {s(rb, i)}, {s(rb, i)}"))
+        streams.append(st)
+    for k in range(max(len(x) for x in streams)):
+        for st in streams:
+            if k < len(st):
+                ops.append(st[k])
+    for rb in range(NRB):
+        ops.append(("valu", f"v_add_f32 %[r{rb}], %[r{rb}], {s(rb, 15)}"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_mov_b32 %[th{rb}], %[l{rb}]"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_mov_b32 %[al{rb}], %[lk{rb}]"))
+    for rb in range(NRB):  # y = r - lk; l = l + y; lk = (l - l_old) - y
+        ops.append(("valu", f"v_sub_f32 %[a{rb}], %[r{rb}], %[lk{rb}]"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_add_f32 %[l{rb}], %[th{rb}], %[a{rb}]"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_sub_f32 %[lk{rb}], %[l{rb}], %[th{rb}]"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_sub_f32 %[lk{rb}], %[lk{rb}], %[a{rb}]"))
+    for rb in range(NRB):
+        ops.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, 7)}, {s(rb, 14)}, {s(rb, 15)}"))
+    for rb in range(NRB):  # some probability of the lane may exceed 2^tau
+        ops.append(("valu", f"v_cmp_gt_f32_e64 %[c{rb}], %[r{rb}], %[pbnd]"))
+    ops.append(("salu", "s_or_b64 %[any], %[c0], %[c1]"))
+    return ops
+
+
+def qk_again():
+    """S^T = K Q^T of this tile once more, every K operand read from LDS
+    (the slow path; the ring's last readers, P.V MFMAs, are long done)."""
+    out = [kread(0), kread(1)]
+    for k in range(NKS):
+        if k + 2 < NKS:
+            out.append(kread(k + 2))
+        out.append(f"s_waitcnt lgkmcnt({min(2, NKS - 1 - k)})")
+        for rb in range(NRB):
+            c = "0" if k == 0 else stile(rb)
+            out.append(f"v_mfma_f32_32x32x16_bf16 {stile(rb)}, {grp(kgroup(k))}, {qop(rb, k)}, {c}")
+    return out + ["s_nop 15", "s_nop 15"]  # the scores are read by VALU next
+
+
 def assign(ops, ngaps):
     """Split the ops into ngaps consecutive groups of even cumulative cost."""
     total = sum(COST[k] for k, _ in ops)
@@ -326,7 +393,7 @@ def assign(ops, ngaps):
     return gaps, per
 
 
-def pv_part(pin):
+def pv_part(pin, lazy=True):
     """P.V of the previous tile with this tile's softmax.  Variant P1 is the
     even tile of a pair: it reads the odd tile's KPRE at step KPRE_STEP
     (that K landed before the previous pair's barrier).  Variant P0, the odd
@@ -334,7 +401,8 @@ def pv_part(pin):
     at the barrier, then read the next pair's first KPRE, left in flight
     for the next block to wait on."""
     even = pin == 1
-    gaps, per = assign(softmax_ops(1 - pin), NRB * NT)
+    ops = softmax_ops_stale(1 - pin) if lazy else softmax_ops(1 - pin)
+    gaps, per = assign(ops, NRB * NT)
     out = []
     for t in range(NT):
         ks, db = divmod(t, NDB)
@@ -351,9 +419,20 @@ def pv_part(pin):
                 if t + 2 < NT:
                     out += vreads(t + 2)
             out += gaps[NRB * t + rb]
-    if not even:
-        out += ["s_waitcnt vmcnt(0)", "s_barrier"] + kpre_reads()
-    return out, per
+    tail = [] if even else ["s_waitcnt vmcnt(0)", "s_barrier"] + kpre_reads()
+    if not lazy:
+        return out + tail, per
+    # Some lane's probabilities may exceed the bound: the slow path (label
+    # 8) restores l, recomputes the scores, masks them again if the tile is
+    # cut, and runs the full softmax (running-max vote, rescale factors).
+    # The odd tile's barrier waits for it: after the barrier the other
+    # waves may refill this tile's K slot.
+    out += ["s_cmp_lg_u64 %[any], 0", "s_cbranch_scc1 8f"] + tail + ["s_branch 9f", "8:",
+            "s_nop 15", "s_nop 15"]
+    out += [f"v_mov_b32 %[l{rb}], %[th{rb}]" for rb in range(NRB)]
+    out += [f"v_mov_b32 %[lk{rb}], %[al{rb}]" for rb in range(NRB)]
+    out += qk_again() + mask_part() + [text for _, text in softmax_ops(1 - pin)]
+    return out + tail + ["9:"], per
 
 
 def macro(name, lines, sep="\\n\\t"):
@@ -377,14 +456,18 @@ def render():
            "// One 32-key tile at HD = 256: S^T = K Q^T, the optional key-bound mask,",
            "// and O^T += V^T P^T of the previous tile with this tile's online softmax",
            "// in its shadow.  Variant P<b> reads the bf16 probabilities from buffer b",
-           "// and writes the new ones to buffer 1 - b.  Operands are bound by the asm",
-           "// statement in ring_attn_fused.hip."]
+           "// and writes the new ones to buffer 1 - b.  ASM blocks (bf16 output) take",
+           "// the scores against the running max as it stands and fall back to a slow",
+           "// path when a probability may exceed 2^tau; F32 blocks (fp32 output) keep",
+           "// the exact running max.  Operands are bound by the asm statement in",
+           "// ring_attn_fused.hip."]
     per = None
-    for pin in (0, 1):
-        pv, per = pv_part(pin)
-        out.append(f"// P.V block of variant P{pin}: about {per:.1f} full-rate VALU issue slots"
-                   " of softmax work per MFMA.")
-        out += macro(f"RA_TILE_HD256_ASM_P{pin}", qk_part() + mask_part() + pv)
+    for lazy, name in ((True, "ASM"), (False, "F32")):
+        for pin in (0, 1):
+            pv, per = pv_part(pin, lazy)
+            out.append(f"// P.V block of variant {name}_P{pin}: about {per:.1f} full-rate VALU issue"
+                       " slots of softmax work per MFMA.")
+            out += macro(f"RA_TILE_HD256_{name}_P{pin}", qk_part() + mask_part() + pv)
     q = [f'[q{rb}_{k}] "{{{qop(rb, k)}}}"(q[{rb}][{k}])' for rb in range(NRB) for k in range(NKS)]
     out += operand_list("RA_TILE_HD256_Q_OPERANDS", q)
     kp = [f'[kp{k}] "+{{v[{KPRE + 4 * k}:{KPRE + 4 * k + 3}]}}"(kpre[{k}])' for k in range(2)]

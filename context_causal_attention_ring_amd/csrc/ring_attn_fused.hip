@@ -75,6 +75,11 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // probability of each row is exactly 1 and carries no bf16 rounding.
 template <bool F32OUT>
 constexpr float kTau = F32OUT ? 0.0f : 8.0f;
+// With bf16 output the HD = 256 block first takes each tile's scores against
+// the running max as it stands; a lane whose 16 probabilities sum to more
+// than 2^kTau may hold one above 2^kTau, and then the block recomputes the
+// tile with the max updated.
+constexpr float kPBound = 256.0f;  // 2^kTau<false>
 
 // Chunk swizzles (16-byte chunks within a tile row).  K rows are read 32 at
 // a time at one chunk: 16 consecutive rows must land in 16 distinct bank
@@ -202,7 +207,7 @@ __device__ __forceinline__ float wave_max_pair(float x) {
       [acc14] "+a"(acc[1][4]), [acc15] "+a"(acc[1][5]), [acc16] "+a"(acc[1][6]),               \
       [acc17] "+a"(acc[1][7]), [ml0] "+v"(ml[0]), [ml1] "+v"(ml[1]), [l0] "+v"(l[0]),          \
       [l1] "+v"(l[1]), [lk0] "+v"(lk[0]), [lk1] "+v"(lk[1]), [al0] "=&v"(al[0]),               \
-      [al1] "=&v"(al[1]), [resc] "=&s"(resc),                                                    \
+      [al1] "=&v"(al[1]), [resc] "=&s"(resc), [any] "=&s"(any),                                                    \
       [a0] "=&v"(a0), [b0] "=&v"(b0), [a1] "=&v"(a1), [b1] "=&v"(b1), [th0] "=&v"(th0),       \
       [th1] "=&v"(th1), [r0] "=&v"(r0), [r1] "=&v"(r1), [c0] "=&s"(c0), [c1] "=&s"(c1), [v0] "=&s"(v0), [v1] "=&s"(v1),        \
       [st] "=&s"(st), [mflag] "=&s"(mflag), [lc] "=&s"(lc), [lm] "=&s"(lm), [cr] "=&s"(cr),     \
@@ -210,7 +215,7 @@ __device__ __forceinline__ float wave_max_pair(float x) {
 #define RA_TILE_INPUT_OPERANDS                                                                  \
   [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [ka2] "v"(ka[2]), [ka3] "v"(ka[3]), [ka4] "v"(ka[4]),    \
       [ka5] "v"(ka[5]), [ka6] "v"(ka[6]), [ka7] "v"(ka[7]), [va0] "v"(va[0]), [va1] "v"(va[1]), \
-      [va2] "v"(va[2]), [va3] "v"(va[3]), [c2] "s"(c2), [tau] "s"(tau), [wk] "s"(wb.k),         \
+      [va2] "v"(va[2]), [va3] "v"(va[3]), [c2] "s"(c2), [tau] "s"(tau), [pbnd] "s"(pbnd), [wk] "s"(wb.k),         \
       [np] "s"(wb.np), [wlim] "s"(wb.lim), [wm31] "s"(wb.wm31), [vv] "s"(wb.v), [tt] "s"(wb.t),  \
       [pos0] "v"(pos[0]), [pos1] "v"(pos[1]), [ninf] "v"(ninf), [ko0] "i"(KOFF),                \
       [ko1] "i"(KOFF + 256), [vo000] "i"(VOFF), [vo001] "i"(VOFF + 4096),                       \
@@ -248,14 +253,15 @@ struct CopyLanes {    // a lane's offsets for the block's LDS-DMA copies (see be
   uint32_t ka, kb, va, vb;
   uint32_t rs16;      // 16 rows' stride in bytes (uniform)
 };
-template <uint32_t KOFF, uint32_t VOFF, int PIN, uint32_t MK, uint32_t MV, uint32_t KPO>
+template <bool F32, uint32_t KOFF, uint32_t VOFF, int PIN, uint32_t MK, uint32_t MV,
+          uint32_t KPO>
 __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], const bf16x8 (&pin)[2][2],
                                            bf16x8 (&pout)[2][2], const bf16x8 (&q)[2][16],
                                            bf16x8 (&kpre)[2], const uint32_t (&ka)[8],
                                            const uint32_t (&va)[4],
                                            float (&ml)[2], float (&l)[2], float (&lk)[2],
                                            float (&al)[2],
-                                           uint32_t& resc, float c2, float tau,
+                                           uint32_t& resc, float c2, float tau, float pbnd,
                                            const TileBound& wb, const int (&pos)[2],
                                            const i32x4& desck,
                                            const i32x4& descv, uint32_t offk, uint32_t offv,
@@ -263,15 +269,25 @@ __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], const bf16x8 (&p
 #if defined(__HIP_DEVICE_COMPILE__)
   float a0, b0, a1, b1, th0, th1, r0, r1;
   uint32_t st, mflag, lc, lm, cr, cc, v0, v1;
-  uint64_t c0, c1;
+  uint64_t c0, c1, any;
   const float ninf = kNegInf;
-  if constexpr (PIN == 0) {
+  if constexpr (PIN == 0 && !F32) {
     asm volatile(RA_TILE_HD256_ASM_P0
                  : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_PB_OUT1
                  : RA_TILE_HD256_Q_OPERANDS, RA_TILE_HD256_PB_IN0, RA_TILE_INPUT_OPERANDS
                  : RA_TILE_HD256_CLOBBERS, "memory", "scc", "m0");
-  } else {
+  } else if constexpr (!F32) {
     asm volatile(RA_TILE_HD256_ASM_P1
+                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_PB_OUT0
+                 : RA_TILE_HD256_Q_OPERANDS, RA_TILE_HD256_PB_IN1, RA_TILE_INPUT_OPERANDS
+                 : RA_TILE_HD256_CLOBBERS, "memory", "scc", "m0");
+  } else if constexpr (PIN == 0) {
+    asm volatile(RA_TILE_HD256_F32_P0
+                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_PB_OUT1
+                 : RA_TILE_HD256_Q_OPERANDS, RA_TILE_HD256_PB_IN0, RA_TILE_INPUT_OPERANDS
+                 : RA_TILE_HD256_CLOBBERS, "memory", "scc", "m0");
+  } else {
+    asm volatile(RA_TILE_HD256_F32_P1
                  : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_PB_OUT0
                  : RA_TILE_HD256_Q_OPERANDS, RA_TILE_HD256_PB_IN1, RA_TILE_INPUT_OPERANDS
                  : RA_TILE_HD256_CLOBBERS, "memory", "scc", "m0");
@@ -807,10 +823,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       constexpr int PB = SL & 1;
       // this block's copies: K of tile v + 2 and V of tile v + 1
       const i32x4 dkr = desc_of(wk_), dvr = desc_of(wv_);
-      tile_hd256<SL * TILE_B, ((SL + 3) % 4) * TILE_B, PB ^ 1, ((SL + 2) % 4) * TILE_B,
+      tile_hd256<F32OUT, SL * TILE_B, ((SL + 3) % 4) * TILE_B, PB ^ 1, ((SL + 2) % 4) * TILE_B,
                  VBASE + ((SL + 1) % 4) * TILE_B, ((SL + 1) % 4) * TILE_B>(
           acc, pbuf[PB ^ 1], pbuf[PB], qreg, kpre, ka, va, mlog, lsum, lcomp, alpha, resc, c2,
-          kTau<F32OUT>, tb, pos, dkr, dvr, wk_.off, wv_.off, m0b, dl);
+          kTau<F32OUT>, kPBound, tb, pos, dkr, dvr, wk_.off, wv_.off, m0b, dl);
       step(wk_, 0);
       step(wv_, 1);
       sum_rounded(pbuf[PB]);

@@ -44,13 +44,21 @@ def regs(text):
 
 
 def tile_blocks(lines):
-    """(start, index after the block, last two MFMAs) for every big inline-asm block."""
+    """(start, index after the block, last two MFMAs) for every big inline-asm
+    block.  A block with a slow path (label 8, reached by a branch after the
+    P.V MFMAs) leaves by two ways: the common one right after those MFMAs,
+    and the slow path, whose last MFMAs are followed by two s_nop 15 and the
+    softmax reading their results; the MFMAs that matter are the common
+    path's last ones."""
     start = None
     for i, line in enumerate(lines):
         if ";;#ASMSTART" in line:
             start = i
         elif ";;#ASMEND" in line and start is not None and i - start > 300:
-            mfma = [x.strip() for x in lines[start:i] if x.strip().startswith("v_mfma")]
+            body = [x.strip() for x in lines[start:i]]
+            if "8:" in body:
+                body = body[:body.index("8:")]
+            mfma = [x for x in body if x.startswith("v_mfma")]
             yield start, i + 1, mfma[-2:]
 
 
