@@ -199,6 +199,30 @@ def test_negative_control():
     assert d_bad >= 10 * max(d_ok, 1e-4)
 
 
+def test_running_max_jumps_mid_walk():
+    """Every row's running max jumps by about 6 (natural units, > 8 in log2)
+    on the third tile of the first shard visit, which the shard's end cuts
+    (shards of 87-88 tokens, token round-robin: slots 0-63, tokens below
+    512, fill the first two tiles): the HD = 256 block's recompute path
+    with the mask, after the first tile.  q carries 4 in dimension 0 and
+    cached keys before token 512 carry -24 there (scores lowered by 6),
+    later ones 0; the rows stay as spread as the plain workload (exact in
+    bf16)."""
+    w = small("max-jump-mid-walk", nq=32, nkv=2, hd=256, cache_len=700, P=8, head_rows=96,
+              tail_rows=96, real_rows=192)
+    case = Case(w)
+    case.t["q"][:, :, 0] = 4.0
+    case.t["k_cache_tok"][:512, :, 0] = -24.0
+    case.t["k_cache_tok"][512:, :, 0] = 0.0
+    case.t["k_cur"][:, :, 0] = 0.0
+    case.kc = striped_cache(case.t["k_cache_tok"], w.P, w.interleave, w.shard_cap)
+    case.to_device()
+    out, lse = run(case)
+    compare(case, out, lse, list(range(w.real_rows)), TOL_BF16)
+    out32, lse32 = run(case, out_fp32=True)
+    compare(case, out32, lse32, list(range(w.real_rows)), TOL_F32)
+
+
 def test_two_region_merge_agreement():
     """The fused result equals the oracle's two-pass (cache-only + current-only) merge."""
     w = FULL_CASES[1]
