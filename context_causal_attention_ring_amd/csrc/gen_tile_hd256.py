@@ -15,12 +15,19 @@ Tiles run in pairs (K and V slots t mod 4).  One block, in order:
   2. Only when the tile is cut by a key bound (a uniform flag): the scores
      of keys at or past each row's bound become -inf.
   3. O^T += V^T P^T of tile v-1: 32 MFMAs.  After each MFMA an even share
-     (by issue cost) of tile v's online softmax is issued: the row max (two
-     in-lane max3 chains, one v_permlane32_swap exchange with lane ^ 32),
-     the lazy running-max vote, one FMA + exp2 per score, the row sums, and
-     the bf16 packing of the probabilities into the next P.V operands.  The
-     even tile of a pair reads the odd tile's KPRE here.
-  4. Odd tile only (the end of the pair): wait for this wave's copies, meet
+     (by issue cost) of tile v's online softmax is issued.  ASM blocks (bf16
+     output): one FMA + exp2 per score against the running max as it
+     stands, the row sums, their compensated fold, the bf16 packing of the
+     probabilities into the next P.V operands, and a test that no lane's
+     probabilities sum past 2^tau.  F32 blocks (fp32 output): first the row
+     max (two in-lane max3 chains, one v_permlane32_swap exchange with lane
+     ^ 32) and the running-max vote, then the same.  The even tile of a
+     pair reads the odd tile's KPRE here.
+  4. ASM blocks, when the test fails (the first tile; a row's max grew by
+     more than tau): restore the row sums, compute the tile's scores again
+     from its K slot, mask them again, and run the F32 blocks' softmax
+     (vote, rescale factors, exact new max where voted).
+  5. Odd tile only (the end of the pair): wait for this wave's copies, meet
      the other waves at the pair's barrier, and read the next pair's first
      KPRE, left in flight: the scalar code between blocks hides its latency.
 The block is a single asm statement so that the softmax stays in the MFMAs'
