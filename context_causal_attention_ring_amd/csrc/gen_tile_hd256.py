@@ -203,8 +203,12 @@ def mask_part():
     pos_rb + lc (current tiles, lm = 1: lc = 1 - first key's position).
     Lane half h holds keys 8 (i / 4) + 4 h + i % 4 of the tile; with lim =
     bound - 4 h, key slot i is kept iff 8 (i / 4) + i % 4 < lim."""
-    out = ["s_cmp_eq_u32 %[mflag], 0", "s_cbranch_scc1 1f",
-           "v_mbcnt_lo_u32_b32 %[a0], -1, 0", "v_mbcnt_hi_u32_b32 %[a0], -1, %[a0]",
+    return ["s_cmp_eq_u32 %[mflag], 0", "s_cbranch_scc1 1f"] + mask_body() + ["1:"]
+
+
+def mask_body():
+    """mask_part without its test: the per-row bounds, then the compares."""
+    out = ["v_mbcnt_lo_u32_b32 %[a0], -1, 0", "v_mbcnt_hi_u32_b32 %[a0], -1, %[a0]",
            "v_lshrrev_b32 %[a0], 5, %[a0]", "v_lshlrev_b32 %[a0], 2, %[a0]",  # 4 h
            "s_cmp_eq_u32 %[lm], 0", "s_cbranch_scc0 2f"]
     out += [f"v_sub_u32 %[th{rb}], %[lc], %[a0]" for rb in range(NRB)] + ["s_branch 3f", "2:"]
@@ -217,7 +221,6 @@ def mask_part():
             out.append(f"v_sub_u32 %[a0], {c}, %[th{rb}]")    # < 0 iff kept
             out.append("v_ashrrev_i32 %[a0], 31, %[a0]")      # all ones iff kept
             out.append(f"v_bfi_b32 {s(rb, i)}, %[a0], {s(rb, i)}, %[ninf]")
-    out.append("1:")
     return out
 
 
@@ -434,8 +437,9 @@ def pv_part(pin, lazy=True):
     # cut, and runs the full softmax (running-max vote, rescale factors).
     # The odd tile's barrier waits for it: after the barrier the other
     # waves may refill this tile's K slot.
-    out += ["s_cmp_lg_u64 %[any], 0", "s_cbranch_scc1 8f"] + tail + ["s_branch 9f", "8:",
-            "s_nop 15", "s_nop 15"]
+    out += ["s_cmp_lg_u64 %[any], 0", "s_cbranch_scc1 8f"] + tail + ["s_branch 9f"]
+    out += ["7:"] + mask_body() + ["s_branch 6b"]  # the mask, out of the common path
+    out += ["8:", "s_nop 15", "s_nop 15"]
     out += [f"v_mov_b32 %[l{rb}], %[th{rb}]" for rb in range(NRB)]
     out += [f"v_mov_b32 %[lk{rb}], %[al{rb}]" for rb in range(NRB)]
     out += qk_again() + mask_part() + [text for _, text in softmax_ops(1 - pin)]
@@ -474,7 +478,10 @@ def render():
             pv, per = pv_part(pin, lazy)
             out.append(f"// P.V block of variant {name}_P{pin}: about {per:.1f} full-rate VALU issue"
                        " slots of softmax work per MFMA.")
-            out += macro(f"RA_TILE_HD256_{name}_P{pin}", qk_part() + mask_part() + pv)
+            # ASM blocks branch to the mask (rare) and back, F32 blocks skip it
+            mask = (["s_cmp_lg_u32 %[mflag], 0", "s_cbranch_scc1 7f", "6:"] if lazy
+                    else mask_part())
+            out += macro(f"RA_TILE_HD256_{name}_P{pin}", qk_part() + mask + pv)
     q = [f'[q{rb}_{k}] "{{{qop(rb, k)}}}"(q[{rb}][{k}])' for rb in range(NRB) for k in range(NKS)]
     out += operand_list("RA_TILE_HD256_Q_OPERANDS", q)
     kp = [f'[kp{k}] "+{{v[{KPRE + 4 * k}:{KPRE + 4 * k + 3}]}}"(kpre[{k}])' for k in range(2)]
