@@ -762,7 +762,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   uint32_t resc = 0;      // row blocks whose rows the previous tile asked to rescale ...
   float alpha[NRB];       // ... by these factors (1 for the other rows)
   auto rescale = [&]() RA_INLINE {
-    if (__builtin_expect(resc != 0, 0)) {
+    // (readfirstlane: resc is uniform, and so the test stays scalar)
+    if (__builtin_expect(__builtin_amdgcn_readfirstlane(resc) != 0, 0)) {
 #if defined(__HIP_DEVICE_COMPILE__)
       // the last P.V MFMAs may still be writing acc: wait them out
       asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
