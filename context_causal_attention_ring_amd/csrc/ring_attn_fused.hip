@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // descriptor is sized to its valid rows, so rows past them load as zeros.
   // Everything here is wave-uniform.
   struct Walker {
-    uint32_t lo, hi, size;  // the region's K or V descriptor (base address, bytes)
+    i32x4 d;                // the region's K or V descriptor (base address, size in bytes)
     uint32_t off;           // byte offset of the tile's first row
     int lim;                // ring: valid keys of the visit left from this tile;
                             // current: chunk position of the tile's first key
@@ -434,6 +434,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // enter region k at its tile b; side 0: K, 1: V
   auto enter = [&](Walker& w, int k, int b, int side) RA_INLINE {
     uint64_t base;
+    uint32_t size;
     w.k = k;
     if (k < p.P) {
       int sh = p.ring_start - k;
@@ -441,18 +442,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       const int len = full_i + min(max((int)p.rem - sh * p.interleave, 0), p.interleave);
       base = (uint64_t)(uintptr_t)(side ? p.v_cache : p.k_cache) +
              (uint64_t)(((int64_t)sh * p.shard_cap * p.nkv + g) * D) * 2u;
-      w.size = (uint32_t)len * rowstride;
+      size = (uint32_t)len * rowstride;
       w.lim = len - b * kBKV;
       w.left = p.nb - b;
     } else {
       base = (uint64_t)(uintptr_t)(side ? p.v_cur : p.k_cur) + (uint64_t)g * D * 2u;
       const bool cur = k == p.P && b < n_cur;
-      w.size = cur ? cur_bytes : 0u;
+      size = cur ? cur_bytes : 0u;
       w.lim = b * kBKV;
       w.left = cur ? n_cur - b : (1 << 30);
     }
-    w.lo = (uint32_t)base;
-    w.hi = (uint32_t)(base >> 32) & 0xffffu;
+    w.d = make_desc(reinterpret_cast<const void*>(base), size);
     w.off = (uint32_t)b * tile_stride;
   };
   // one tile on; the region ends after `left` tiles
@@ -489,9 +489,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       (uint32_t)dma_r * rowstride + (uint32_t)((dma_pc ^ swz_k(dma_r, CPR)) << 4);
   const uint32_t dma_vbase =
       (uint32_t)dma_r * rowstride + (uint32_t)((dma_pc ^ swz_v(dma_r, CPR)) << 4);
-  auto desc_of = [](const Walker& w) RA_INLINE {
-    return i32x4{(int)w.lo, (int)w.hi, (int)w.size, 0x00020000};
-  };
+  auto desc_of = [](const Walker& w) RA_INLINE { return w.d; };
   auto issue_k = [&](const Walker& w, uint16_t* dst) RA_INLINE {
     const i32x4 d = desc_of(w);
 #pragma unroll
@@ -732,7 +730,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // filled with zeros and the probabilities start at zero.
   {
     Walker zero = wv_;
-    zero.size = 0;  // a zero-size fetch: the slot fills with zeros
+    zero.d[2] = 0;  // a zero-size fetch: the slot fills with zeros
     zero.off = 0;
     issue_k(wk_, kslot(0));
     step(wk_, 0);
