@@ -429,7 +429,7 @@ def test_two_launch_matches_fused_at_32k():
 
 # ---------------------------------------------------------------- split walk (partials in HBM)
 
-def run_split(case, splits, out_fp32=False):
+def run_split(case, splits, out_fp32=False, ring_start=0):
     w, d = case.w, case.d
     C, NQ, HD = w.q_rows, w.nq, w.hd
     out = torch.full((C, NQ, HD), SENTINEL, device="cuda",
@@ -443,7 +443,7 @@ def run_split(case, splits, out_fp32=False):
     print(f"[gpu] ring_attn_prefill_split {w.name} splits={splits} C={C} L={w.cache_len}",
           flush=True)
     ra.ring_attn_prefill_split(d["q"], d["k_cache"], d["v_cache"], d["k_cur"], d["v_cur"],
-                               w.cache_len, w.P, ra.StripeLayout(w.interleave, 0), splits, ws,
+                               w.cache_len, w.P, ra.StripeLayout(w.interleave, ring_start), splits, ws,
                                out, lse, dims)
     torch.cuda.synchronize()
     return out.cpu(), lse.cpu()
@@ -461,6 +461,20 @@ def test_split_parity(w, splits):
     case = Case(w).to_device()
     out, lse = run_split(case, splits)
     compare(case, out, lse, list(range(w.real_rows)), TOL_BF16)
+    check_pads_untouched(case, out, lse)
+
+
+@pytest.mark.parametrize("w,splits,ring_start,fp32", [
+    (FULL_CASES[4], 5, 1, False),     # 16-token stripes, visits from shard 1
+    (RANK_CASES[2], 6, 0, True),      # a rank share's pieces, fp32 output
+    (FULL_CASES[9], 3, 1, True),      # MHA (group 1), HD = 256
+], ids=lambda x: getattr(x, "name", str(x)))
+def test_split_layouts_and_fp32(w, splits, ring_start, fp32):
+    """The split walk with other stripe units, another first shard and fp32
+    output: the same rows as the definition."""
+    case = Case(w).to_device()
+    out, lse = run_split(case, splits, out_fp32=fp32, ring_start=ring_start)
+    compare(case, out, lse, list(range(w.real_rows)), TOL_F32 if fp32 else TOL_BF16)
     check_pads_untouched(case, out, lse)
 
 
