@@ -872,9 +872,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   if constexpr (ASM256) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15" ::: "memory");
 #endif
 
-  // Epilogue: out = acc / l, lse = ln 2 * (m + log2 l).
+  // Epilogue: out = acc / l, lse = ln 2 * (m + log2 l).  The lane's rows
+  // are derived again here (lane id by mbcnt) rather than kept live through
+  // the walk, where registers are scarce.
+  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int lr_e = lane_e & 31, h_e = lane_e >> 5;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
+    const int row = row0 + wave * kRowsPerWave + rb * 32 + lr_e;
+    token[rb] = row / p.group;
+    head[rb] = g * p.group + (row - token[rb] * p.group);
+    row_ok[rb] = token[rb] < p.real_rows;
     const float l_own = lsum[rb] - lcomp[rb], lq_own = lsum_q[rb] - lcomp_q[rb];
     const float l_tot = l_own + __shfl_xor(l_own, 32);
     const float l_norm = F32OUT ? lq_own + __shfl_xor(lq_own, 32) : l_tot;
@@ -888,7 +896,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const int d0 = db * 32 + i4 * 8 + 4 * h;
+        const int d0 = db * 32 + i4 * 8 + 4 * h_e;
         const f32x4 o = {acc[rb][db][4 * i4] * inv, acc[rb][db][4 * i4 + 1] * inv,
                          acc[rb][db][4 * i4 + 2] * inv, acc[rb][db][4 * i4 + 3] * inv};
         if (F32OUT || p.store_f32) {
@@ -899,7 +907,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
         }
       }
     }
-    if (h == 0 && p.lse != nullptr)
+    if (h_e == 0 && p.lse != nullptr)
       p.lse[((int64_t)seg * p.nq + head[rb]) * p.q_rows + token[rb]] =
           (mlog[rb] + __log2f(l_tot)) * kLn2;
   }
