@@ -169,10 +169,14 @@ def bound_ops():
     ]
 
 
-def qk_part():
+def qk_part(extra=()):
+    """S^T = K Q^T with the block's copies and bound ops; `extra` VALU ops
+    (independent of the scores) are spread over the k-steps, two per step."""
     # KPRE was read by the block before (or before the loop): wait for it.
     out = ["s_nop 1", "s_waitcnt lgkmcnt(0)"]
     bound = bound_ops()
+    extra = list(extra)
+    per = -(-len(extra) // NKS) if extra else 0
     for k in range(NKS):
         wait = None
         if k + 2 < NKS:
@@ -194,7 +198,49 @@ def qk_part():
             out += dma(k // 2)
         elif k // 2 < len(bound):
             out += bound[k // 2]
+        out += extra[k * per:(k + 1) * per]
     return out
+
+
+def rsum_ops(pin):
+    """bf16 output: the row sums of the previous tile's bf16-rounded
+    probabilities (the B operands its P.V uses, buffer pin), folded into
+    lq with Kahan compensation (lqk), so that the output is normalised by
+    exactly the weights its numerator took.  One v_dot2 against (1, 1) per
+    pair of keys; the fold's rescale by alpha happens before the block (in
+    the kernel, with the accumulator's).  Runs in the QK^T half, where the
+    vector unit is otherwise idle.  Uses r, a and b as scratch."""
+    chains = []
+    for rb in range(NRB):
+        st = [f"v_dot2_f32_bf16 %[r{rb}], {pbreg(pin, rb, 0)}, %[one2], 0"]
+        st += [f"v_dot2_f32_bf16 %[r{rb}], {pbreg(pin, rb, j)}, %[one2], %[r{rb}]"
+               for j in range(1, 8)]
+        # y = r - c; t = lq + y; c = (t - lq) - y; lq = t
+        st += [f"v_sub_f32 %[a{rb}], %[r{rb}], %[lqk{rb}]",
+               f"v_add_f32 %[b{rb}], %[lq{rb}], %[a{rb}]",
+               f"v_sub_f32 %[lqk{rb}], %[b{rb}], %[lq{rb}]",
+               f"v_sub_f32 %[lqk{rb}], %[lqk{rb}], %[a{rb}]",
+               f"v_mov_b32 %[lq{rb}], %[b{rb}]"]
+        chains.append(st)
+    return [op for pair in zip(*chains) for op in pair]
+
+
+def pack_f32(rb, j, direct):
+    """fp32 output: split the probabilities of keys 2j, 2j + 1 of row block
+    rb into hi = the bf16 truncation (exact: the upper half of the fp32
+    word) and lo = bf16(p - hi), so that hi + lo holds p to about 2^-16
+    relative and the P.V MFMAs on both carry no bf16 rounding of the
+    weights.  direct: write the hi and lo operands at once (their buffer is
+    no longer read); else leave hi packed in the odd score register and lo
+    in the even one for a later move.  a0 and b0 are scratch."""
+    i0, i1 = s(rb, 2 * j), s(rb, 2 * j + 1)
+    hi, lo = (pbreg(0, rb, j), pbreg(1, rb, j)) if direct else (i1, i0)
+    return [("valu", f"v_and_b32 %[a0], %[hmask], {i0}"),
+            ("valu", f"v_and_b32 %[b0], %[hmask], {i1}"),
+            ("valu", f"v_sub_f32 {i0}, {i0}, %[a0]"),
+            ("valu", f"v_sub_f32 {i1}, {i1}, %[b0]"),
+            ("valu", f"v_cvt_pk_bf16_f32 {lo}, {i0}, {i1}"),
+            ("valu", f"v_perm_b32 {hi}, %[b0], %[a0], %[psel]")]
 
 
 def mask_part():
@@ -224,8 +270,9 @@ def mask_body():
     return out
 
 
-def softmax_ops(pout):
-    """The online softmax of tile v as (kind, text) in dependency order."""
+def softmax_ops(pout, pack=True):
+    """The online softmax of tile v as (kind, text) in dependency order
+    (pack: the bf16 packing of the probabilities into buffer pout)."""
     ops = [("nop", "s_nop 4")]  # the last score MFMAs' results (after one more MFMA)
     for rb in range(NRB):  # threshold for the lazy rescale: mlog + tau
         ops.append(("valu", f"v_add_f32 %[th{rb}], %[tau], %[ml{rb}]"))
@@ -293,7 +340,7 @@ def softmax_ops(pout):
                 st.append(("valu", f"v_add_f32 %[r{rb}], {s(rb, 0)}, {s(rb, 1)}"))
             elif i > 2:
                 st.append(("valu", f"v_add_f32 %[r{rb}], %[r{rb}], {s(rb, i - 1)}"))
-            if i >= 2 and i % 2 == 0:
+            if pack and i >= 2 and i % 2 == 0:
                 j = i // 2 - 1
                 st.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, j)}, {s(rb, 2 * j)}, "
                                    f"{s(rb, 2 * j + 1)}"))
@@ -317,8 +364,10 @@ def softmax_ops(pout):
         ops.append(("valu", f"v_sub_f32 %[lk{rb}], %[l{rb}], %[a{rb}]"))
     for rb in range(NRB):
         ops.append(("valu", f"v_sub_f32 %[lk{rb}], %[lk{rb}], %[b{rb}]"))
-    for rb in range(NRB):
-        ops.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, 7)}, {s(rb, 14)}, {s(rb, 15)}"))
+    if pack:
+        for rb in range(NRB):
+            ops.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, 7)}, {s(rb, 14)}, "
+                                f"{s(rb, 15)}"))
     return ops
 
 
@@ -446,6 +495,56 @@ def pv_part(pin, lazy=True):
     return out + tail + ["9:"], per
 
 
+# fp32 output, P.V step t: hi rb0, hi rb1, lo rb0, lo rb1 (MFMA 4 t + u).
+# The last reader of the 16-key step ks = 0 operands is MFMA 4 * NDB - 1;
+# its operands may be overwritten from the gap after MFMA F32_KS0_FREE on.
+F32_KS0_FREE = 4 * NDB - 1 + 4
+
+
+def pv_part_f32(even):
+    """fp32 output: O^T += V^T (P_hi + P_lo)^T of tile v-1 with tile v's
+    exact-max softmax (vote, rescale factors) in the MFMAs' shadow.  The
+    probabilities are single-buffered (the register file holds no second
+    hi/lo pair): the packing of the step-0 operands waits until the MFMAs
+    reading them are done, and the step-1 operands are packed into the
+    score registers and moved into place after the last MFMA."""
+    nm = 2 * NRB * NT
+    soft = softmax_ops(0, pack=False)
+    late = [op for rb in range(NRB) for j in range(4, 8) for op in pack_f32(rb, j, False)]
+    direct = [op for rb in range(NRB) for j in range(4) for op in pack_f32(rb, j, True)]
+    ca = sum(COST[k] for k, _ in soft + late)
+    cd = sum(COST[k] for k, _ in direct)
+    g1 = max(F32_KS0_FREE + 1, round(nm * ca / (ca + cd)))
+    ga, per = assign(soft + late, g1)
+    gd, _ = assign(direct, nm - g1)
+    gaps = ga + gd
+    out = []
+    for t in range(NT):
+        ks, db = divmod(t, NDB)
+        wait = 2 if t + 1 < NT else 0
+        if even and t == KPRE_STEP + 1:
+            wait = 4
+        out.append(f"s_waitcnt lgkmcnt({wait})")
+        for u in range(2 * NRB):
+            buf, rb = divmod(u, NRB)
+            out.append(f"v_mfma_f32_32x32x16_bf16 %[acc{rb}{db}], {grp(vgroup(t))}, "
+                       f"{pbop(buf, rb, ks)}, %[acc{rb}{db}]")
+            if u == 2 * NRB - 1:
+                if even and t == KPRE_STEP:
+                    out += kpre_reads()
+                if t + 2 < NT:
+                    out += vreads(t + 2)
+            out += gaps[2 * NRB * t + u]
+    # the step-1 operands: the last MFMAs read them while they run
+    out += ["s_nop 15", "s_nop 15"]
+    for rb in range(NRB):
+        for j in range(4, 8):
+            out.append(f"v_mov_b32 {pbreg(0, rb, j)}, {s(rb, 2 * j + 1)}")
+            out.append(f"v_mov_b32 {pbreg(1, rb, j)}, {s(rb, 2 * j)}")
+    tail = [] if even else ["s_waitcnt vmcnt(0)", "s_barrier"] + kpre_reads()
+    return out + tail, per
+
+
 def macro(name, lines, sep="\\n\\t"):
     out = [f"#define {name} \\"]
     for ln in lines:
@@ -475,24 +574,31 @@ def render():
     per = None
     for lazy, name in ((True, "ASM"), (False, "F32")):
         for pin in (0, 1):
-            pv, per = pv_part(pin, lazy)
+            if lazy:
+                pv, per = pv_part(pin, True)
+                # the rounded sums of the previous tile (buffer pin) in the
+                # QK^T half; the mask (rare) is out of line, branched to
+                body = qk_part(rsum_ops(pin)) + ["s_cmp_lg_u32 %[mflag], 0", "s_cbranch_scc1 7f",
+                                                 "6:"] + pv
+            else:
+                pv, per = pv_part_f32(pin == 1)
+                body = qk_part() + mask_part() + pv
             out.append(f"// P.V block of variant {name}_P{pin}: about {per:.1f} full-rate VALU issue"
                        " slots of softmax work per MFMA.")
-            # ASM blocks branch to the mask (rare) and back, F32 blocks skip it
-            mask = (["s_cmp_lg_u32 %[mflag], 0", "s_cbranch_scc1 7f", "6:"] if lazy
-                    else mask_part())
-            out += macro(f"RA_TILE_HD256_{name}_P{pin}", qk_part() + mask + pv)
+            out += macro(f"RA_TILE_HD256_{name}_P{pin}", body)
     q = [f'[q{rb}_{k}] "{{{qop(rb, k)}}}"(q[{rb}][{k}])' for rb in range(NRB) for k in range(NKS)]
     out += operand_list("RA_TILE_HD256_Q_OPERANDS", q)
     kp = [f'[kp{k}] "+{{v[{KPRE + 4 * k}:{KPRE + 4 * k + 3}]}}"(kpre[{k}])' for k in range(2)]
     out += operand_list("RA_TILE_HD256_KPRE_OPERANDS", kp)
+    # probability buffers: p0 at PB[0], p1 at PB[1].  bf16 output: one is
+    # read (the previous tile's), the other written; fp32 output: hi in p0,
+    # lo in p1, both read and rewritten.
     for buf in (0, 1):
-        ins = [f'"{{{pbop(buf, rb, ks)}}}"(pin[{rb}][{ks}])' for rb in range(NRB)
-               for ks in range(NPS)]
-        outs = [f'"=&{{{pbop(buf, rb, ks)}}}"(pout[{rb}][{ks}])' for rb in range(NRB)
+        regs = [(pbop(buf, rb, ks), f"p{buf}[{rb}][{ks}]") for rb in range(NRB)
                 for ks in range(NPS)]
-        out += operand_list(f"RA_TILE_HD256_PB_IN{buf}", ins)
-        out += operand_list(f"RA_TILE_HD256_PB_OUT{buf}", outs)
+        out += operand_list(f"RA_TILE_HD256_PB_IN{buf}", [f'"{{{r}}}"({c})' for r, c in regs])
+        out += operand_list(f"RA_TILE_HD256_PB_OUT{buf}", [f'"=&{{{r}}}"({c})' for r, c in regs])
+        out += operand_list(f"RA_TILE_HD256_PB_RW{buf}", [f'"+{{{r}}}"({c})' for r, c in regs])
     clob = [f'"v{r}"' for r in list(range(S0, S0 + 32)) + list(range(RING0, RING0 + 12))]
     out += operand_list("RA_TILE_HD256_CLOBBERS", clob)
     return "\n".join(out) + "\n"

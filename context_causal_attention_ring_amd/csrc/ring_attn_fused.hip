@@ -70,11 +70,13 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
-// Lazy-rescale threshold (log2 units): probabilities stay <= 2^kTau.  With
-// fp32 output the running max is exact (threshold 0), so the dominant
-// probability of each row is exactly 1 and carries no bf16 rounding.
+// Lazy-rescale threshold (log2 units): probabilities stay <= 2^kTau.  The
+// P.V product never sees a weight rounded relative to another: with bf16
+// output the output is normalised by the sum of the same bf16-rounded
+// probabilities the MFMAs take; with fp32 output each probability enters
+// P.V as a bf16 pair hi + lo that holds it to about 2^-16.
 template <bool F32OUT>
-constexpr float kTau = F32OUT ? 0.0f : 8.0f;
+constexpr float kTau = 8.0f;
 // With bf16 output the HD = 256 block first takes each tile's scores against
 // the running max as it stands; a lane whose 16 probabilities sum to more
 // than 2^kTau may hold one above 2^kTau, and then the block recomputes the
@@ -212,6 +214,9 @@ __device__ __forceinline__ float wave_max_pair(float x) {
       [th1] "=&v"(th1), [r0] "=&v"(r0), [r1] "=&v"(r1), [c0] "=&s"(c0), [c1] "=&s"(c1), [v0] "=&s"(v0), [v1] "=&s"(v1),        \
       [st] "=&s"(st), [mflag] "=&s"(mflag), [lc] "=&s"(lc), [lm] "=&s"(lm), [cr] "=&s"(cr),     \
       [cc] "=&s"(cc), RA_TILE_HD256_KPRE_OPERANDS
+// bf16 output: the compensated sums of the rounded probabilities
+#define RA_TILE_LQ_OPERANDS                                                                     \
+  [lq0] "+v"(lq[0]), [lq1] "+v"(lq[1]), [lqk0] "+v"(lqk[0]), [lqk1] "+v"(lqk[1])
 #define RA_TILE_INPUT_OPERANDS                                                                  \
   [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [ka2] "v"(ka[2]), [ka3] "v"(ka[3]), [ka4] "v"(ka[4]),    \
       [ka5] "v"(ka[5]), [ka6] "v"(ka[6]), [ka7] "v"(ka[7]), [va0] "v"(va[0]), [va1] "v"(va[1]), \
@@ -255,12 +260,12 @@ struct CopyLanes {    // a lane's offsets for the block's LDS-DMA copies (see be
 };
 template <bool F32, uint32_t KOFF, uint32_t VOFF, int PIN, uint32_t MK, uint32_t MV,
           uint32_t KPO>
-__device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], const bf16x8 (&pin)[2][2],
-                                           bf16x8 (&pout)[2][2], const bf16x8 (&q)[2][16],
+__device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], bf16x8 (&p0)[2][2],
+                                           bf16x8 (&p1)[2][2], const bf16x8 (&q)[2][16],
                                            bf16x8 (&kpre)[2], const uint32_t (&ka)[8],
                                            const uint32_t (&va)[4],
                                            float (&ml)[2], float (&l)[2], float (&lk)[2],
-                                           float (&al)[2],
+                                           float (&lq)[2], float (&lqk)[2], float (&al)[2],
                                            uint32_t& resc, float c2, float tau, float pbnd,
                                            const TileBound& wb, const int (&pos)[2],
                                            const i32x4& desck,
@@ -271,30 +276,38 @@ __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], const bf16x8 (&p
   uint32_t st, mflag, lc, lm, cr, cc, v0, v1;
   uint64_t c0, c1, any;
   const float ninf = kNegInf;
+  const uint32_t one2 = 0x3F803F80u;   // bf16 pair (1, 1): v_dot2 sums a packed pair
+  const uint32_t hmask = 0xFFFF0000u;  // the bf16 truncation of an fp32 word
+  const uint32_t psel = 0x07060302u;   // v_perm: the upper halves of two words
   if constexpr (PIN == 0 && !F32) {
     asm volatile(RA_TILE_HD256_ASM_P0
-                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_PB_OUT1
-                 : RA_TILE_HD256_Q_OPERANDS, RA_TILE_HD256_PB_IN0, RA_TILE_INPUT_OPERANDS
+                 : RA_TILE_STATE_OPERANDS, RA_TILE_LQ_OPERANDS, RA_TILE_HD256_PB_OUT1
+                 : RA_TILE_HD256_Q_OPERANDS, RA_TILE_HD256_PB_IN0, RA_TILE_INPUT_OPERANDS,
+                   [one2] "s"(one2)
                  : RA_TILE_HD256_CLOBBERS, "memory", "scc", "m0");
   } else if constexpr (!F32) {
     asm volatile(RA_TILE_HD256_ASM_P1
-                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_PB_OUT0
-                 : RA_TILE_HD256_Q_OPERANDS, RA_TILE_HD256_PB_IN1, RA_TILE_INPUT_OPERANDS
+                 : RA_TILE_STATE_OPERANDS, RA_TILE_LQ_OPERANDS, RA_TILE_HD256_PB_OUT0
+                 : RA_TILE_HD256_Q_OPERANDS, RA_TILE_HD256_PB_IN1, RA_TILE_INPUT_OPERANDS,
+                   [one2] "s"(one2)
                  : RA_TILE_HD256_CLOBBERS, "memory", "scc", "m0");
   } else if constexpr (PIN == 0) {
     asm volatile(RA_TILE_HD256_F32_P0
-                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_PB_OUT1
-                 : RA_TILE_HD256_Q_OPERANDS, RA_TILE_HD256_PB_IN0, RA_TILE_INPUT_OPERANDS
+                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_PB_RW0, RA_TILE_HD256_PB_RW1
+                 : RA_TILE_HD256_Q_OPERANDS, RA_TILE_INPUT_OPERANDS, [hmask] "s"(hmask),
+                   [psel] "s"(psel)
                  : RA_TILE_HD256_CLOBBERS, "memory", "scc", "m0");
   } else {
     asm volatile(RA_TILE_HD256_F32_P1
-                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_PB_OUT0
-                 : RA_TILE_HD256_Q_OPERANDS, RA_TILE_HD256_PB_IN1, RA_TILE_INPUT_OPERANDS
+                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_PB_RW0, RA_TILE_HD256_PB_RW1
+                 : RA_TILE_HD256_Q_OPERANDS, RA_TILE_INPUT_OPERANDS, [hmask] "s"(hmask),
+                   [psel] "s"(psel)
                  : RA_TILE_HD256_CLOBBERS, "memory", "scc", "m0");
   }
 #endif
 }
 #undef RA_TILE_STATE_OPERANDS
+#undef RA_TILE_LQ_OPERANDS
 #undef RA_TILE_INPUT_OPERANDS
 
 template <int D, bool F32OUT>
@@ -560,15 +573,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[rb][db] = f32x16{};
-  bf16x8 pb[NRB][NPS];  // bf16 probabilities of the previous tile (B operands of P.V)
-  bf16x8 pbuf[2][NRB][NPS];  // the same, double-buffered by tile parity (HD = 256 body)
+  // bf16 probabilities of the previous tile (B operands of P.V); with fp32
+  // output pb holds each probability's bf16 part and pbl the rest, rounded
+  bf16x8 pb[NRB][NPS], pbl[NRB][NPS];
+  // HD = 256 body: bf16 output double-buffers the probabilities by tile
+  // parity; fp32 output keeps hi in pbuf[0] and lo in pbuf[1]
+  bf16x8 pbuf[2][NRB][NPS];
   float mlog[NRB], lsum[NRB], lsum_q[NRB];  // running max (log2 units), row sums
   float lcomp[NRB], lcomp_q[NRB];            // their compensations (fold_sum)
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     mlog[rb] = kNegInf;
-    lsum[rb] = 0.f;     // fp32 sum of this lane's share of the keys' probabilities
-    lsum_q[rb] = 0.f;   // the same over bf16-rounded probabilities (fp32 output)
+    lsum[rb] = 0.f;     // fp32 sum of this lane's share of the keys' probabilities (LSE)
+    lsum_q[rb] = 0.f;   // the same over the bf16-rounded ones (bf16 output's normaliser)
     lcomp[rb] = lcomp_q[rb] = 0.f;
   }
   const float c2 = p.scale_log2e;
@@ -613,10 +630,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     }
   };
 
-  // Probabilities -> bf16 B operands of P.V.  For fp32 output also the sum
-  // of the bf16-rounded probabilities (v_dot2 against (1, 1)): numerator
-  // and denominator then weight every key identically.
-  auto pack = [&](const f32x16 (&S)[NRB][NKB], bf16x8 (&pb)[NRB][NPS], const float (&alpha)[NRB]) RA_INLINE {
+  // Probabilities -> bf16 B operands of P.V.  bf16 output: also the sum of
+  // the bf16-rounded probabilities (v_dot2 against (1, 1)), the output's
+  // normaliser, so numerator and denominator weight every key identically.
+  // fp32 output: p = hi + lo, hi = bf16(p) and lo = bf16(p - hi), both
+  // taken by P.V.
+  auto pack = [&](const f32x16 (&S)[NRB][NKB], const float (&alpha)[NRB]) RA_INLINE {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
@@ -626,11 +645,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
           const bf16x2 pr = {(__bf16)S[rb][kb][i], (__bf16)S[rb][kb][i + 1]};
-          if (F32OUT) lq = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lq, false);
+          if (!F32OUT) lq = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lq, false);
           pb[rb][2 * kb + (i >> 3)][i & 7] = pr[0];
           pb[rb][2 * kb + (i >> 3)][(i & 7) + 1] = pr[1];
+          if (F32OUT) {
+            pbl[rb][2 * kb + (i >> 3)][i & 7] = (__bf16)(S[rb][kb][i] - (float)pr[0]);
+            pbl[rb][2 * kb + (i >> 3)][(i & 7) + 1] = (__bf16)(S[rb][kb][i + 1] - (float)pr[1]);
+          }
         }
-      if (F32OUT) fold_sum(lsum_q[rb], lcomp_q[rb], alpha[rb], lq);
+      if (!F32OUT) fold_sum(lsum_q[rb], lcomp_q[rb], alpha[rb], lq);
     }
   };
 
@@ -708,6 +731,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       for (int rb = 0; rb < NRB; ++rb)
         acc[rb][db] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[t % 3], pb[rb][ks], acc[rb][db], 0, 0, 0);
+      if constexpr (F32OUT) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[t % 3], pbl[rb][ks],
+                                                                acc[rb][db], 0, 0, 0);
+      }
       // units [t*NU/NT, (t+1)*NU/NT), the rest after the last slot
 #pragma unroll
       for (int u = t * NU / NT; u < (t + 1) * NU / NT; ++u) unit(u);
@@ -743,7 +772,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-    for (int ks = 0; ks < NPS; ++ks) pb[rb][ks] = pbuf[0][rb][ks] = pbuf[1][rb][ks] = bf16x8{};
+    for (int ks = 0; ks < NPS; ++ks)
+      pb[rb][ks] = pbl[rb][ks] = pbuf[0][rb][ks] = pbuf[1][rb][ks] = bf16x8{};
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
   __syncthreads();
   // HD = 256: the first two K operands of tile 0 (each block reads them for
@@ -771,25 +801,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
         if (resc & (1u << rb)) {
 #pragma unroll
           for (int db = 0; db < NDB; ++db) scale_agprs(acc[rb][db], alpha[rb]);
-        }
-    }
-  };
-  // For fp32 output: the row sums over the bf16-rounded probabilities.
-  auto sum_rounded = [&](const bf16x8 (&pb)[NRB][NPS]) RA_INLINE {
-    if constexpr (F32OUT) {
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        float lq = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < NPS; ++ks)
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const bf16x2 pr = {pb[rb][ks][e], pb[rb][ks][e + 1]};
-            lq = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lq, false);
+          // HD = 256, bf16 output: the block adds the previous tile's
+          // rounded sums to lsum_q after this rescale, as P.V does to acc
+          if constexpr (ASM256 && !F32OUT) {
+            lsum_q[rb] *= alpha[rb];
+            lcomp_q[rb] *= alpha[rb];
           }
-        fold_sum(lsum_q[rb], lcomp_q[rb], alpha[rb], lq);
-      }
+        }
     }
   };
   // Tile v, in slot SL = v mod 4.
@@ -824,11 +842,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       const i32x4 dkr = desc_of(wk_), dvr = desc_of(wv_);
       tile_hd256<F32OUT, SL * TILE_B, ((SL + 3) % 4) * TILE_B, PB ^ 1, ((SL + 2) % 4) * TILE_B,
                  VBASE + ((SL + 1) % 4) * TILE_B, ((SL + 1) % 4) * TILE_B>(
-          acc, pbuf[PB ^ 1], pbuf[PB], qreg, kpre, ka, va, mlog, lsum, lcomp, alpha, resc, c2,
-          kTau<F32OUT>, kPBound, tb, pos, dkr, dvr, wk_.off, wv_.off, m0b, dl);
+          acc, pbuf[0], pbuf[1], qreg, kpre, ka, va, mlog, lsum, lcomp, lsum_q, lcomp_q, alpha,
+          resc, c2, kTau<F32OUT>, kPBound, tb, pos, dkr, dvr, wk_.off, wv_.off, m0b, dl);
       step(wk_, 0);
       step(wv_, 1);
-      sum_rounded(pbuf[PB]);
     } else {
       int lim[NRB];
       bool cut = bounds(wb_, lim);
@@ -842,7 +859,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       qk(kslot(SL), S);
       if (cut) mask(S, lim);
       resc = pv_softmax(vslot((SL + 3) % 4), S, alpha);
-      pack(S, pb, alpha);
+      pack(S, alpha);
     }
 #ifdef RA_SYNC_EVERY_TILE
     __syncthreads();
@@ -883,9 +900,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     token[rb] = row / p.group;
     head[rb] = g * p.group + (row - token[rb] * p.group);
     row_ok[rb] = token[rb] < p.real_rows;
+    // the LSE takes the fp32 sum; bf16 output is normalised by the sum of
+    // the rounded probabilities its numerator took, fp32 output (hi + lo
+    // probabilities) by the fp32 sum
     const float l_own = lsum[rb] - lcomp[rb], lq_own = lsum_q[rb] - lcomp_q[rb];
     const float l_tot = l_own + __shfl_xor(l_own, 32);
-    const float l_norm = F32OUT ? lq_own + __shfl_xor(lq_own, 32) : l_tot;
+    const float l_norm = F32OUT ? l_tot : lq_own + __shfl_xor(lq_own, 32);
     if (!row_ok[rb]) continue;
     // a row that saw no key (possible in a one-region launch) gets out = 0
     // and lse = -inf (m = -inf, log2 0 = -inf)

@@ -12,6 +12,12 @@ statement) do none of that unless two s_nop 15 (32 wait states) come
 first.  A block may also leave LDS reads of
 the next tile's first K operands (KPRE) in flight, so no compiler
 instruction between two blocks may touch those registers.
+
+The LDS-DMA copies set M0 (their LDS destination) inside asm statements
+that declare it clobbered, which the compiler honours but warns may be
+undefined behaviour.  So that this can never matter, no instruction the
+compiler emits in any fused kernel may use M0 at all: neither name it nor
+be one of the instructions that read it implicitly.
 """
 import importlib.util
 import os
@@ -126,3 +132,40 @@ def test_no_compiler_code_races_the_last_mfmas_of_a_tile_block(extra):
         first, last = blocks[0][0], blocks[-1][1]
         touch = [ins for ins in compiler_code(lines[first:last]) if regs(ins) & KPRE]
         assert not touch, f"{name}: compiler code touches the KPRE registers: {touch[:4]}"
+
+
+# Instructions that read or write M0 without naming it (gfx9 family).
+IMPLICIT_M0 = ("s_movrel", "v_movrel", "s_sendmsg", "ds_gws", "ds_append", "ds_consume",
+               "ds_ordered", "ds_read_addtid", "ds_write_addtid", "v_interp", "s_set_gpr_idx")
+
+
+def m0_users(code):
+    """Compiler instructions that use M0: naming it, reading it implicitly,
+    or an LDS-DMA load (`... lds`, whose LDS address M0 holds)."""
+    return [ins for ins in code
+            if re.search(r"\bm0\b", ins) or re.search(r"\blds\s*$", ins)
+            or ins.split(None, 1)[0].startswith(IMPLICIT_M0)]
+
+
+@pytest.mark.skipif(not HAS_HIPCC, reason="needs hipcc to assemble the kernel")
+@pytest.mark.parametrize("extra", [(), ("-DRA_SYNC_EVERY_TILE",)], ids=["product", "checking"])
+def test_compiler_code_never_uses_m0(extra):
+    with tempfile.TemporaryDirectory() as tmp:
+        asm = open(build.assemble(out=os.path.join(tmp, "fused.s"), extra=extra)).read()
+    kernels = re.findall(r"^(_ZN2ra\S*fused_kernel\S*):", asm, re.M)
+    assert len(kernels) == 6  # HD 64, 128, 256 x bf16 / fp32 output
+    for name in kernels:
+        body = asm[asm.index(name + ":"):asm.index(".Lfunc_end", asm.index(name + ":"))]
+        bad = m0_users(compiler_code(body.splitlines()))
+        assert not bad, f"{name}: compiler code uses M0: {bad[:4]}"
+
+
+def test_m0_check_has_teeth():
+    """The M0 check flags explicit and implicit users, and passes plain code."""
+    assert m0_users(["s_mov_b32 m0, s4", "s_sendmsg sendmsg(MSG_INTERRUPT)",
+                     "buffer_load_dword v1, v2, s[4:7], 0 offen lds",
+                     "v_readlane_b32 s0, v1, m0"]) == [
+        "s_mov_b32 m0, s4", "s_sendmsg sendmsg(MSG_INTERRUPT)",
+        "buffer_load_dword v1, v2, s[4:7], 0 offen lds", "v_readlane_b32 s0, v1, m0"]
+    assert m0_users(["v_add_f32 v1, v2, v3", "s_add_u32 s0, s1, s2",
+                     "v_readlane_b32 s0, v1, 5", "ds_read_b128 v[0:3], v4"]) == []

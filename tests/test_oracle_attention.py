@@ -229,6 +229,18 @@ def test_bf16_bits_decode():
     assert got[:4].tolist() == [1.0, -2.0, 0.25, math.inf] and got[4] == 2.0 ** -133
 
 
+def test_default_scale_values():
+    """default_scale is the softmax temperature 1/sqrt(HD) of the pages'
+    attention; the head dims this library takes have exact values (HD 64,
+    256: powers of two) that a wrong formula (1/HD, sqrt(HD), 1/sqrt(HD/2))
+    would miss.  The needle closed forms take their score scale from it, so
+    this pins it outside them."""
+    assert att.default_scale(64) == 0.125
+    assert att.default_scale(256) == 0.0625
+    assert att.default_scale(4) == 0.5
+    assert abs(att.default_scale(128) - 2.0 ** -3.5) < 1e-16
+
+
 # --- mutation checks: a plausible mistake in the oracle must fail a pin ---
 
 MUTATIONS = [
