@@ -104,7 +104,7 @@ def measured_traffic(path=TRAFFIC_SUMMARY):
     return rec["bytes_per_launch"] if rec.get("source_sha256") == fused_source_sha() else None
 
 
-def setup(w, device):
+def setup(w, device, out_fp32=False):
     import torch
     import context_causal_attention_ring_amd as ra
     import workloads
@@ -117,7 +117,7 @@ def setup(w, device):
     layout = ra.StripeLayout(w.interleave, 0)
     dims = ra.make_dims(d["q"], d["k_cur"], w.shard_cap, real_rows=w.real_rows,
                         head_rows=w.head_rows, scale=w.scale, head_pos=w.head_pos,
-                        tail_pos=w.tail_start)
+                        tail_pos=w.tail_start, out_fp32=out_fp32)
     if w.cache_len:
         k_tok = t["k_cache_tok"].to(device)
         v_tok = t["v_cache_tok"].to(device)
@@ -125,7 +125,8 @@ def setup(w, device):
                           dims)
         torch.cuda.synchronize()
         del k_tok, v_tok
-    d["out"] = torch.empty(C, w.nq, w.hd, device=device, dtype=torch.bfloat16)
+    d["out"] = torch.empty(C, w.nq, w.hd, device=device,
+                           dtype=torch.float32 if out_fp32 else torch.bfloat16)
     d["lse"] = torch.empty(w.nq, C, device=device, dtype=torch.float32)
     return t, d, layout, dims
 
@@ -152,11 +153,16 @@ def cpu_baseline(w, t, budget_s=12.0):
         flops += sum(4 * w.hd * w.nq * (w.cache_len + w.positions[i] + 1) for i in rows)
         done += len(rows)
         blk = min(64, blk * 2)
+    try:
+        host_cpus = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        host_cpus = os.cpu_count()
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpus": host_cpus, "host_cpus_total": os.cpu_count(),
             "sample": f"fp64 oracle on {done} random real rows of the {w.name} chunk "
                       f"(all {w.nq} heads, {w.cache_len} cached + causal keys), "
-                      f"{elapsed:.1f} s; TFLOP/s of the same algorithmic count"}
+                      f"{elapsed:.1f} s; TFLOP/s of the same algorithmic count; cores = the "
+                      f"BLAS threads the oracle's matrix products ran on"}
 
 
 def main():
@@ -169,6 +175,8 @@ def main():
                     help="cut each row's key walk into this many segments (partials merged by "
                          "LSE); 0 (default): the library's suggestion for this GPU")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--out-fp32", action="store_true",
+                    help="time the fp32-output mode (hi + lo probabilities in P.V)")
     ap.add_argument("--no-two-launch", action="store_true",
                     help="skip timing the two-launch comparator (cache-only + current-only + merge)")
     ap.add_argument("--traffic", default=TRAFFIC_SUMMARY,
@@ -203,7 +211,7 @@ def main():
 
     w = workloads.CONFIGS[args.config]
     with_write = True
-    t, d, layout, dims = setup(w, dev)
+    t, d, layout, dims = setup(w, dev, args.out_fp32)
     stream = torch.cuda.current_stream()
     if args.splits == 0:
         args.splits = ra.ra_split_suggest(dims, torch.cuda.get_device_properties(dev)
@@ -281,7 +289,7 @@ def main():
     F = alg_flops(w)
     value = F / (ms_per_step * 1e-3) / 1e12
     achieved = F / (kern_ms_avg * 1e-3) / 1e12
-    traffic = measured_traffic(args.traffic) if w.name == "32k" else None
+    traffic = measured_traffic(args.traffic) if w.name == "32k" and not args.out_fp32 else None
     props = torch.cuda.get_device_properties(dev)
     res = {
         "metric": METRIC,
@@ -295,6 +303,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
+        "out_dtype": "fp32" if args.out_fp32 else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: fused ring+current prefill of one {w.q_rows}-row "
                                f"chunk share (head {w.head_rows} rows at chunk position "

@@ -65,7 +65,7 @@ KPRE_STEP = 2      # P.V step of an even tile after which the odd tile's KPRE is
 
 # Issue cost of one instruction, in units of one full-rate VALU op (measured
 # on gfx950: v_exp_f32 is half rate; SALU and s_nop issue in about a cycle).
-COST = {"valu": 1.0, "trans": 2.0, "salu": 0.5, "nop": 0.5}
+COST = {"valu": 1.0, "trans": 2.0, "dot": 2.0, "salu": 0.5, "nop": 0.5}
 
 
 def grp(j, half=None):
@@ -202,27 +202,65 @@ def qk_part(extra=()):
     return out
 
 
-def rsum_ops(pin):
-    """bf16 output: the row sums of the previous tile's bf16-rounded
-    probabilities (the B operands its P.V uses, buffer pin), folded into
-    lq with Kahan compensation (lqk), so that the output is normalised by
-    exactly the weights its numerator took.  One v_dot2 against (1, 1) per
-    pair of keys; the fold's rescale by alpha happens before the block (in
-    the kernel, with the accumulator's).  Runs in the QK^T half, where the
-    vector unit is otherwise idle.  Uses r, a and b as scratch."""
+SIG_SHIFT = -4  # a tile is significant when its sum exceeds 2^SIG_SHIFT of the running sum
+
+
+def sig_ops(buf):
+    """bf16 output, a significant tile (a lane's tile sum r is above its
+    bound: 2^SIG_SHIFT of the lane's running sum, at most 2^tau): the
+    tile's bf16-rounded probabilities (buffer buf, just packed) are summed
+    (one v_dot2 against (1, 1) per pair of keys) and their difference from
+    the fp32 tile sum r is added to dq.  The output is normalised by
+    l + dq, so for every significant tile numerator and denominator weight
+    each key identically; each other tile holds at most 2^SIG_SHIFT of the
+    row's weight, so the bf16 rounding of its weights (2^-9 each, random
+    sign) moves the output little.  Then bnd = min(2^SIG_SHIFT l, 2^tau).
+    The bound only grows in the common path (l does), so a stale bound is
+    conservative.  a and b are scratch.  A v_dot2 result is read by another
+    VALU instruction only after DOT_WAIT more instructions (the hardware
+    does not wait for it): the bound update and an s_nop sit between."""
     chains = []
     for rb in range(NRB):
-        st = [f"v_dot2_f32_bf16 %[r{rb}], {pbreg(pin, rb, 0)}, %[one2], 0"]
-        st += [f"v_dot2_f32_bf16 %[r{rb}], {pbreg(pin, rb, j)}, %[one2], %[r{rb}]"
+        st = [f"v_dot2_f32_bf16 %[b{rb}], {pbreg(buf, rb, 0)}, %[one2], 0"]
+        st += [f"v_dot2_f32_bf16 %[b{rb}], {pbreg(buf, rb, j)}, %[one2], %[b{rb}]"
                for j in range(1, 8)]
-        # y = r - c; t = lq + y; c = (t - lq) - y; lq = t
-        st += [f"v_sub_f32 %[a{rb}], %[r{rb}], %[lqk{rb}]",
-               f"v_add_f32 %[b{rb}], %[lq{rb}], %[a{rb}]",
-               f"v_sub_f32 %[lqk{rb}], %[b{rb}], %[lq{rb}]",
-               f"v_sub_f32 %[lqk{rb}], %[lqk{rb}], %[a{rb}]",
-               f"v_mov_b32 %[lq{rb}], %[b{rb}]"]
         chains.append(st)
-    return [op for pair in zip(*chains) for op in pair]
+    out = [op for pair in zip(*chains) for op in pair]
+    out += [f"v_ldexp_f32 %[a{rb}], %[l{rb}], {SIG_SHIFT}" for rb in range(NRB)]
+    out += [f"v_min_f32 %[bnd{rb}], %[pbnd], %[a{rb}]" for rb in range(NRB)]
+    out += [f"s_nop {DOT_WAIT - 1}"]
+    out += [f"v_sub_f32 %[b{rb}], %[b{rb}], %[r{rb}]" for rb in range(NRB)]
+    out += [f"v_add_f32 %[dq{rb}], %[dq{rb}], %[b{rb}]" for rb in range(NRB)]
+    return out
+
+
+# Wait states after a v_dot2 writes a VGPR before another (non-dot) VALU
+# instruction may read it; back-to-back v_dot2 accumulating into the same
+# register are forwarded.
+DOT_WAIT = 4
+
+
+def check_dot_hazards(lines):
+    """Raise if an instruction other than v_dot2 reads a VGPR a v_dot2
+    wrote fewer than DOT_WAIT wait states before (s_nop n counts n + 1;
+    labels and branches end the window)."""
+    import re
+    pending = []  # (register text, wait states since the write)
+    for ln in lines:
+        op = ln.split(None, 1)[0] if ln.strip() else ""
+        if op.endswith(":") or op.startswith(("s_branch", "s_cbranch")):
+            pending = []
+            continue
+        args = ln.split(None, 1)[1] if " " in ln else ""
+        dst, srcs = (args.split(",", 1) + [""])[:2] if args else ("", "")
+        if not op.startswith("v_dot2"):
+            for reg, _ in pending:
+                if re.search(re.escape(reg) + r"(?![\w\]])", srcs if op.startswith("v_") else args):
+                    raise AssertionError(f"{ln!r} reads {reg} too soon after a v_dot2")
+        n = int(args) + 1 if op == "s_nop" else 1
+        pending = [(r, w + n) for r, w in pending if w + n < DOT_WAIT]
+        if op.startswith("v_dot2"):
+            pending = [(r, w) for r, w in pending if r != dst.strip()] + [(dst.strip(), 0)]
 
 
 def pack_f32(rb, j, direct):
@@ -398,10 +436,12 @@ def softmax_ops_stale(pout):
                                    f"{s(rb, 2 * j + 1)}"))
             st.append(("trans", f"v_exp_f32 {s(rb, i)}, {s(rb, i)}"))
         streams.append(st)
+    main = []
     for k in range(max(len(x) for x in streams)):
         for st in streams:
             if k < len(st):
-                ops.append(st[k])
+                main.append(st[k])
+    ops += main
     for rb in range(NRB):
         ops.append(("valu", f"v_add_f32 %[r{rb}], %[r{rb}], {s(rb, 15)}"))
     for rb in range(NRB):
@@ -418,8 +458,10 @@ def softmax_ops_stale(pout):
         ops.append(("valu", f"v_sub_f32 %[lk{rb}], %[lk{rb}], %[a{rb}]"))
     for rb in range(NRB):
         ops.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, 7)}, {s(rb, 14)}, {s(rb, 15)}"))
-    for rb in range(NRB):  # some probability of the lane may exceed 2^tau
-        ops.append(("valu", f"v_cmp_gt_f32_e64 %[c{rb}], %[r{rb}], %[pbnd]"))
+    # some probability of the lane may exceed 2^tau, or the tile is
+    # significant: bnd <= 2^tau (see sig_ops)
+    for rb in range(NRB):
+        ops.append(("valu", f"v_cmp_gt_f32_e64 %[c{rb}], %[r{rb}], %[bnd{rb}]"))
     ops.append(("salu", "s_or_b64 %[any], %[c0], %[c1]"))
     return ops
 
@@ -481,17 +523,25 @@ def pv_part(pin, lazy=True):
     tail = [] if even else ["s_waitcnt vmcnt(0)", "s_barrier"] + kpre_reads()
     if not lazy:
         return out + tail, per
-    # Some lane's probabilities may exceed the bound: the slow path (label
-    # 8) restores l, recomputes the scores, masks them again if the tile is
-    # cut, and runs the full softmax (running-max vote, rescale factors).
-    # The odd tile's barrier waits for it: after the barrier the other
-    # waves may refill this tile's K slot.
+    # Some lane's tile sum passed its bound (label 8): if some probability
+    # may exceed 2^tau the slow path (label 5) restores l, recomputes the
+    # scores, masks them again if the tile is cut, and runs the full softmax
+    # (running-max vote, rescale factors, dq rescaled with them); either
+    # way the tile is then treated as significant (sig_ops).  The odd
+    # tile's barrier waits for both: after the barrier the other waves may
+    # refill this tile's K slot.
     out += ["s_cmp_lg_u64 %[any], 0", "s_cbranch_scc1 8f"] + tail + ["s_branch 9f"]
     out += ["7:"] + mask_body() + ["s_branch 6b"]  # the mask, out of the common path
-    out += ["8:", "s_nop 15", "s_nop 15"]
+    out += ["8:"] + [f"v_cmp_gt_f32_e64 %[c{rb}], %[r{rb}], %[pbnd]" for rb in range(NRB)]
+    out += ["s_nop 1", "s_or_b64 %[any], %[c0], %[c1]", "s_cmp_lg_u64 %[any], 0",
+            "s_cbranch_scc1 5f"]
+    out += sig_ops(1 - pin) + tail + ["s_branch 9f"]
+    out += ["5:", "s_nop 15", "s_nop 15"]
     out += [f"v_mov_b32 %[l{rb}], %[th{rb}]" for rb in range(NRB)]
     out += [f"v_mov_b32 %[lk{rb}], %[al{rb}]" for rb in range(NRB)]
     out += qk_again() + mask_part() + [text for _, text in softmax_ops(1 - pin)]
+    out += [f"v_mul_f32 %[dq{rb}], %[dq{rb}], %[al{rb}]" for rb in range(NRB)]
+    out += sig_ops(1 - pin)
     return out + tail + ["9:"], per
 
 
@@ -576,15 +626,14 @@ def render():
         for pin in (0, 1):
             if lazy:
                 pv, per = pv_part(pin, True)
-                # the rounded sums of the previous tile (buffer pin) in the
-                # QK^T half; the mask (rare) is out of line, branched to
-                body = qk_part(rsum_ops(pin)) + ["s_cmp_lg_u32 %[mflag], 0", "s_cbranch_scc1 7f",
-                                                 "6:"] + pv
+                # the mask (rare) is out of line, branched to
+                body = qk_part() + ["s_cmp_lg_u32 %[mflag], 0", "s_cbranch_scc1 7f", "6:"] + pv
             else:
                 pv, per = pv_part_f32(pin == 1)
                 body = qk_part() + mask_part() + pv
             out.append(f"// P.V block of variant {name}_P{pin}: about {per:.1f} full-rate VALU issue"
                        " slots of softmax work per MFMA.")
+            check_dot_hazards(body)
             out += macro(f"RA_TILE_HD256_{name}_P{pin}", body)
     q = [f'[q{rb}_{k}] "{{{qop(rb, k)}}}"(q[{rb}][{k}])' for rb in range(NRB) for k in range(NKS)]
     out += operand_list("RA_TILE_HD256_Q_OPERANDS", q)

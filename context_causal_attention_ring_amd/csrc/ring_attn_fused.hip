@@ -214,9 +214,10 @@ __device__ __forceinline__ float wave_max_pair(float x) {
       [th1] "=&v"(th1), [r0] "=&v"(r0), [r1] "=&v"(r1), [c0] "=&s"(c0), [c1] "=&s"(c1), [v0] "=&s"(v0), [v1] "=&s"(v1),        \
       [st] "=&s"(st), [mflag] "=&s"(mflag), [lc] "=&s"(lc), [lm] "=&s"(lm), [cr] "=&s"(cr),     \
       [cc] "=&s"(cc), RA_TILE_HD256_KPRE_OPERANDS
-// bf16 output: the compensated sums of the rounded probabilities
+// bf16 output: the rounded-minus-fp32 sums of the significant tiles, and
+// the tile-sum bound past which a tile is significant
 #define RA_TILE_LQ_OPERANDS                                                                     \
-  [lq0] "+v"(lq[0]), [lq1] "+v"(lq[1]), [lqk0] "+v"(lqk[0]), [lqk1] "+v"(lqk[1])
+  [dq0] "+v"(dq[0]), [dq1] "+v"(dq[1]), [bnd0] "+v"(bnd[0]), [bnd1] "+v"(bnd[1])
 #define RA_TILE_INPUT_OPERANDS                                                                  \
   [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [ka2] "v"(ka[2]), [ka3] "v"(ka[3]), [ka4] "v"(ka[4]),    \
       [ka5] "v"(ka[5]), [ka6] "v"(ka[6]), [ka7] "v"(ka[7]), [va0] "v"(va[0]), [va1] "v"(va[1]), \
@@ -265,7 +266,7 @@ __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], bf16x8 (&p0)[2][
                                            bf16x8 (&kpre)[2], const uint32_t (&ka)[8],
                                            const uint32_t (&va)[4],
                                            float (&ml)[2], float (&l)[2], float (&lk)[2],
-                                           float (&lq)[2], float (&lqk)[2], float (&al)[2],
+                                           float (&dq)[2], float (&bnd)[2], float (&al)[2],
                                            uint32_t& resc, float c2, float tau, float pbnd,
                                            const TileBound& wb, const int (&pos)[2],
                                            const i32x4& desck,
@@ -581,12 +582,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   bf16x8 pbuf[2][NRB][NPS];
   float mlog[NRB], lsum[NRB], lsum_q[NRB];  // running max (log2 units), row sums
   float lcomp[NRB], lcomp_q[NRB];            // their compensations (fold_sum)
+  // HD = 256, bf16 output: the output's normaliser is lsum + dq, dq the sum
+  // over significant tiles of (rounded - fp32) tile sums; a tile is
+  // significant when a lane's tile sum exceeds its bound sbnd
+  float dq[NRB], sbnd[NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     mlog[rb] = kNegInf;
     lsum[rb] = 0.f;     // fp32 sum of this lane's share of the keys' probabilities (LSE)
-    lsum_q[rb] = 0.f;   // the same over the bf16-rounded ones (bf16 output's normaliser)
+    lsum_q[rb] = 0.f;   // the same over the bf16-rounded ones (generic bf16 normaliser)
     lcomp[rb] = lcomp_q[rb] = 0.f;
+    dq[rb] = sbnd[rb] = 0.f;
   }
   const float c2 = p.scale_log2e;
 
@@ -801,12 +807,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
         if (resc & (1u << rb)) {
 #pragma unroll
           for (int db = 0; db < NDB; ++db) scale_agprs(acc[rb][db], alpha[rb]);
-          // HD = 256, bf16 output: the block adds the previous tile's
-          // rounded sums to lsum_q after this rescale, as P.V does to acc
-          if constexpr (ASM256 && !F32OUT) {
-            lsum_q[rb] *= alpha[rb];
-            lcomp_q[rb] *= alpha[rb];
-          }
         }
     }
   };
@@ -842,8 +842,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       const i32x4 dkr = desc_of(wk_), dvr = desc_of(wv_);
       tile_hd256<F32OUT, SL * TILE_B, ((SL + 3) % 4) * TILE_B, PB ^ 1, ((SL + 2) % 4) * TILE_B,
                  VBASE + ((SL + 1) % 4) * TILE_B, ((SL + 1) % 4) * TILE_B>(
-          acc, pbuf[0], pbuf[1], qreg, kpre, ka, va, mlog, lsum, lcomp, lsum_q, lcomp_q, alpha,
-          resc, c2, kTau<F32OUT>, kPBound, tb, pos, dkr, dvr, wk_.off, wv_.off, m0b, dl);
+          acc, pbuf[0], pbuf[1], qreg, kpre, ka, va, mlog, lsum, lcomp, dq, sbnd, alpha, resc, c2,
+          kTau<F32OUT>, kPBound, tb, pos, dkr, dvr, wk_.off, wv_.off, m0b, dl);
       step(wk_, 0);
       step(wv_, 1);
     } else {
@@ -901,9 +901,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     head[rb] = g * p.group + (row - token[rb] * p.group);
     row_ok[rb] = token[rb] < p.real_rows;
     // the LSE takes the fp32 sum; bf16 output is normalised by the sum of
-    // the rounded probabilities its numerator took, fp32 output (hi + lo
-    // probabilities) by the fp32 sum
-    const float l_own = lsum[rb] - lcomp[rb], lq_own = lsum_q[rb] - lcomp_q[rb];
+    // the rounded probabilities its numerator took (HD = 256: of the
+    // significant tiles), fp32 output (hi + lo probabilities) by the fp32
+    // sum
+    const float l_own = lsum[rb] - lcomp[rb];
+    const float lq_own = ASM256 ? l_own + dq[rb] : lsum_q[rb] - lcomp_q[rb];
     const float l_tot = l_own + __shfl_xor(l_own, 32);
     const float l_norm = F32OUT ? l_tot : lq_own + __shfl_xor(lq_own, 32);
     if (!row_ok[rb]) continue;
