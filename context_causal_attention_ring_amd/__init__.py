@@ -17,17 +17,19 @@ __all__ = ["StripeLayout", "Dims", "RingAttnError", "lib", "ring_attn_prefill",
            "ra_version", "prefill", "two_launch_prefill", "LIB_PATH", "EXPORTED_SYMBOLS",
            "RA_REGION_CACHE", "RA_REGION_CURRENT", "ring_attn_prefill_split",
            "ra_split_workspace_bytes", "ra_split_suggest", "RA_MAX_SPLITS", "load",
-           "SYNC_LIB_PATH"]
+           "SYNC_LIB_PATH", "ring_attn_prefill_split_noalloc", "RA_NOALLOC_SCRATCH_BYTES"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn.so")
 # The checking build (every tile of the fused kernel fenced by a wait and a
 # barrier); tests compare it bit for bit with the product library.
 SYNC_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn_sync.so")
 EXPORTED_SYMBOLS = ("ring_attn_prefill", "ring_attn_prefill_split", "ra_split_workspace_bytes",
+                    "ring_attn_prefill_split_noalloc",
                     "ra_split_suggest",
                     "ring_attn_partial", "merge_attn_states", "kv_cache_write", "ra_shard_len",
                     "ra_last_error", "ra_version")
 RA_MAX_SPLITS = 64
+RA_NOALLOC_SCRATCH_BYTES = 72 << 20
 
 RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP = 0, 1, 2, 3
 RA_DTYPE_BF16, RA_DTYPE_FP32 = 0, 1
@@ -70,6 +72,9 @@ def load(path):
     L.ring_attn_prefill_split.argtypes = [vp, vp, vp, vp, vp, i64, i32, StripeLayout, i32,
                                           vp, i64, vp, vp, ctypes.POINTER(Dims), vp]
     L.ring_attn_prefill_split.restype = ctypes.c_int
+    L.ring_attn_prefill_split_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i32, StripeLayout,
+                                                  i32, vp, vp, ctypes.POINTER(Dims), vp]
+    L.ring_attn_prefill_split_noalloc.restype = ctypes.c_int
     L.ra_split_workspace_bytes.argtypes = [ctypes.POINTER(Dims), i32, ctypes.POINTER(i64)]
     L.ra_split_workspace_bytes.restype = ctypes.c_int
     L.ra_split_suggest.argtypes = [ctypes.POINTER(Dims), i32, ctypes.POINTER(i32)]
@@ -161,6 +166,15 @@ def ring_attn_prefill_split(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, str
                                          _ptr(v_cur), cache_len, P, stripe_layout, splits,
                                          _ptr(workspace), nbytes, _ptr(out), _ptr(lse),
                                          ctypes.byref(dims), _stream(stream)))
+
+
+def ring_attn_prefill_split_noalloc(q, k_cache, v_cache, k_cur, v_cur, cache_len, P,
+                                    stripe_layout, splits, out, lse, dims, stream=None):
+    """Same arguments as the C entry point, with torch tensors for buffers."""
+    _check(lib().ring_attn_prefill_split_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                 _ptr(k_cur), _ptr(v_cur), cache_len, P,
+                                                 stripe_layout, splits, _ptr(out), _ptr(lse),
+                                                 ctypes.byref(dims), _stream(stream)))
 
 
 def ring_attn_partial(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout, regions,

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/ringattn.h"
@@ -402,6 +403,68 @@ int ring_attn_prefill_split(const void* q, const void* k_cache, const void* v_ca
   if (e != hipSuccess)
     return fail(RA_ERR_HIP, "split merge launch failed: %s", hipGetErrorString(e));
   return RA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of ring_attn_prefill_split_noalloc: one array per GPU in the
+// library's own device memory, reserved when the code object is loaded and
+// held until the process ends.  Host code must not use this name as an
+// address (on the host it stands in for the symbol only); it uses the
+// device address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[RA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device
+
+// The current device's copy of `scratch`, looked up once per device.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(RA_ERR_UNSUPPORTED, "device %d is past the %d devices this build supports", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(RA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ring_attn_prefill_split_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                    const void* k_cur, const void* v_cur, int64_t cache_len,
+                                    int32_t P, ra_stripe_layout_t stripe_layout, int32_t splits,
+                                    void* out, float* lse, const ra_dims_t* dims, void* stream) {
+  int64_t need = 0;
+  if (int rc = ra_split_workspace_bytes(dims, splits, &need)) return rc;
+  if (need > RA_NOALLOC_SCRATCH_BYTES)
+    return fail(RA_ERR_UNSUPPORTED,
+                "splits=%d over q_rows=%d x num_q_heads=%d x head_dim=%d needs %lld bytes of "
+                "workspace; the library's own holds %lld (use ring_attn_prefill_split with a "
+                "workspace of your own)",
+                splits, dims->q_rows, dims->num_q_heads, dims->head_dim, (long long)need,
+                (long long)RA_NOALLOC_SCRATCH_BYTES);
+  if (splits == 1)
+    return ring_attn_prefill(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
+                             out, lse, dims, stream);
+  void* ws = nullptr;
+  if (int rc = scratch_on_current_device(&ws)) return rc;
+  return ring_attn_prefill_split(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
+                                 splits, ws, RA_NOALLOC_SCRATCH_BYTES, out, lse, dims, stream);
 }
 
 int merge_attn_states(const void* o1, const float* lse1, const void* o2, const float* lse2,

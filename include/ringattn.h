@@ -160,6 +160,38 @@ int ring_attn_prefill_split(const void* q, const void* k_cache, const void* v_ca
                             void* workspace, int64_t workspace_bytes, void* out, float* lse,
                             const ra_dims_t* dims, void* stream);
 
+/* Bytes of the workspace ring_attn_prefill_split_noalloc keeps in the
+ * library's own device memory (one copy per GPU, held until the process
+ * ends): 72 MiB, e.g. splits = 4 over a 512-row rank share at NQ = 32,
+ * HD = 256. */
+#define RA_NOALLOC_SCRATCH_BYTES (72ll << 20)
+
+/*
+ * ring_attn_prefill_split_noalloc -- ring_attn_prefill_split without a
+ * caller workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The segments' partials go to a workspace of
+ * RA_NOALLOC_SCRATCH_BYTES that the library holds per GPU; the call itself
+ * allocates nothing.  Same arguments and result as ring_attn_prefill_split
+ * minus workspace / workspace_bytes.  The stream must belong to the
+ * current device (hipSetDevice); the first call on a device looks the
+ * workspace up there.
+ *
+ * Every call on one GPU shares that GPU's workspace, and the workspace
+ * keeps the last call's contents (every partial a call reads is written by
+ * the same call first, so nothing needs clearing).  Calls that overlap on
+ * one GPU -- on different streams, or in parallel host threads -- race on
+ * it: order them on one stream.
+ *
+ * Returns RA_ERR_UNSUPPORTED (nothing launched) when splits > 1 needs more
+ * than RA_NOALLOC_SCRATCH_BYTES (see ra_split_workspace_bytes), else as
+ * ring_attn_prefill_split.
+ */
+int ring_attn_prefill_split_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                    const void* k_cur, const void* v_cur, int64_t cache_len,
+                                    int32_t P, ra_stripe_layout_t stripe_layout, int32_t splits,
+                                    void* out, float* lse, const ra_dims_t* dims, void* stream);
+
 /* Host-only: a split count for these dims on a GPU with num_cus compute
  * units.  One workgroup (256 query rows of one KV head) runs per CU at a
  * time; the count is chosen so that the workgroups of all segments fill the

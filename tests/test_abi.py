@@ -252,3 +252,26 @@ def test_checking_build_exports_the_same_symbols():
         assert hasattr(L, name), name
     assert b"checking build" in L.ra_version()
     assert b"checking build" not in ra.lib().ra_version()
+
+
+def test_noalloc_split_refuses_workspace_beyond_its_own():
+    """The no-allocation split keeps its partials in the library's own
+    RA_NOALLOC_SCRATCH_BYTES per GPU; a request that needs more is refused
+    before any HIP call (splits = 4 over 4096 rows x 32 heads x 256 needs
+    512 MiB), and bad split counts are refused as for the split entry."""
+    d = dims(num_q_heads=32, num_kv_heads=2, head_dim=256, q_rows=4096, head_rows=2048,
+             real_rows=4096, tail_pos=2048, cur_len=4096, shard_cap=4096)
+    need = ra.ra_split_workspace_bytes(d, 4)
+    assert need > ra.RA_NOALLOC_SCRATCH_BYTES
+    args = (FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000, FAKE + 0x4000000,
+            28672, 8, ra.StripeLayout(1, 0))
+    rc = ra.lib().ring_attn_prefill_split_noalloc(*args, 4, FAKE + 0x8000000, None,
+                                                  ctypes.byref(d), None)
+    assert rc == 2 and b"workspace" in ra.lib().ra_last_error()
+    for bad in (0, ra.RA_MAX_SPLITS + 1):
+        rc = ra.lib().ring_attn_prefill_split_noalloc(*args, bad, FAKE + 0x8000000, None,
+                                                      ctypes.byref(d), None)
+        assert rc == 1 and b"splits" in ra.lib().ra_last_error()
+    # the largest rank share the workspace was sized for fits: 512 rows, 4 splits
+    d.q_rows, d.real_rows, d.head_rows = 512, 512, 256
+    assert ra.ra_split_workspace_bytes(d, 4) <= ra.RA_NOALLOC_SCRATCH_BYTES
