@@ -226,7 +226,7 @@ def sig_ops(buf):
                for j in range(1, 8)]
         chains.append(st)
     out = [op for pair in zip(*chains) for op in pair]
-    out += [f"v_ldexp_f32 %[a{rb}], %[l{rb}], {SIG_SHIFT}" for rb in range(NRB)]
+    out += [f"v_ldexp_f32 %[a{rb}], %[lo{rb}], {SIG_SHIFT}" for rb in range(NRB)]
     out += [f"v_min_f32 %[bnd{rb}], %[pbnd], %[a{rb}]" for rb in range(NRB)]
     out += [f"s_nop {DOT_WAIT - 1}"]
     out += [f"v_sub_f32 %[b{rb}], %[b{rb}], %[r{rb}]" for rb in range(NRB)]
@@ -353,10 +353,10 @@ def softmax_ops(pout, pack=True):
     ops.append(("nop", "s_nop 1"))
     for rb in range(NRB):  # m_new
         ops.append(("valu", f"v_cndmask_b32_e64 %[b{rb}], %[ml{rb}], %[b{rb}], %[c{rb}]"))
-    # m_use = max(m_new, -FLT_MAX): a row that has seen only masked keys
-    # subtracts a finite value, so its probabilities are exp2(-inf) = 0.
+    # the running max starts at -FLT_MAX (finite), so m_new is finite and a
+    # row that has seen only masked keys gets exp2(-inf) = 0
     for rb in range(NRB):
-        ops.append(("valu", f"v_max_f32 %[a{rb}], 0xff7fffff, %[b{rb}]"))
+        ops.append(("valu", f"v_mov_b32 %[a{rb}], %[b{rb}]"))
     for rb in range(NRB):
         ops.append(("valu", f"v_sub_f32 %[al{rb}], %[ml{rb}], %[a{rb}]"))
     for rb in range(NRB):
@@ -391,17 +391,20 @@ def softmax_ops(pout, pack=True):
     for rb in range(NRB):
         ops.append(("valu", f"v_add_f32 %[r{rb}], %[r{rb}], {s(rb, 15)}"))
     # l = l * alpha + r, compensated (Kahan): lk keeps what the rounding of
-    # each fold dropped, so millions of tiny tile sums do not drift.
+    # each fold dropped, so millions of tiny tile sums do not drift.  The
+    # sums are read from li / lki and written to lo / lko (two register
+    # sets used by even and odd tiles in turn), so a slow path finds the
+    # sums before this tile's fold untouched.
     for rb in range(NRB):
-        ops.append(("valu", f"v_mul_f32 %[a{rb}], %[l{rb}], %[al{rb}]"))
+        ops.append(("valu", f"v_mul_f32 %[a{rb}], %[li{rb}], %[al{rb}]"))
     for rb in range(NRB):
-        ops.append(("valu", f"v_fma_f32 %[b{rb}], -%[lk{rb}], %[al{rb}], %[r{rb}]"))
+        ops.append(("valu", f"v_fma_f32 %[b{rb}], -%[lki{rb}], %[al{rb}], %[r{rb}]"))
     for rb in range(NRB):
-        ops.append(("valu", f"v_add_f32 %[l{rb}], %[a{rb}], %[b{rb}]"))
+        ops.append(("valu", f"v_add_f32 %[lo{rb}], %[a{rb}], %[b{rb}]"))
     for rb in range(NRB):
-        ops.append(("valu", f"v_sub_f32 %[lk{rb}], %[l{rb}], %[a{rb}]"))
+        ops.append(("valu", f"v_sub_f32 %[lko{rb}], %[lo{rb}], %[a{rb}]"))
     for rb in range(NRB):
-        ops.append(("valu", f"v_sub_f32 %[lk{rb}], %[lk{rb}], %[b{rb}]"))
+        ops.append(("valu", f"v_sub_f32 %[lko{rb}], %[lko{rb}], %[b{rb}]"))
     if pack:
         for rb in range(NRB):
             ops.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, 7)}, {s(rb, 14)}, "
@@ -411,21 +414,19 @@ def softmax_ops(pout, pack=True):
 
 def softmax_ops_stale(pout):
     """The common case of tile v's online softmax (bf16 output): every score
-    is taken against the running max as it stands (a row that has seen no
-    key yet uses -FLT_MAX), the tile's row sums r and the bf16 packing as
-    in softmax_ops, and l = l + r compensated (alpha = 1).  Valid while
-    every probability is at most 2^tau, which r <= 2^tau (pbnd) proves:
-    otherwise (a row's max grew by more than tau, or the first tile) the
-    block's slow path recomputes the tile with softmax_ops.  l and lk are
-    kept in th and al (unused here) for that path."""
+    is taken against the running max as it stands (it starts at -FLT_MAX,
+    so a row that has seen no key gets +inf probabilities and the slow
+    path), the tile's row sums r and the bf16 packing as in softmax_ops,
+    and lo = li + r compensated (alpha = 1).  Valid while every
+    probability is at most 2^tau, which r <= 2^tau (pbnd) proves: otherwise
+    (a row's max grew by more than tau, or the first tile) the block's
+    slow path recomputes the tile with softmax_ops, from li as it was."""
     ops = [("nop", "s_nop 4"), ("salu", "s_mov_b32 %[resc], 0")]
-    for rb in range(NRB):
-        ops.append(("valu", f"v_max_f32 %[a{rb}], 0xff7fffff, %[ml{rb}]"))
     streams = []
     for rb in range(NRB):
         st = []
         for i in range(16):
-            st.append(("valu", f"v_fma_f32 {s(rb, i)}, {s(rb, i)}, %[c2], -%[a{rb}]"))
+            st.append(("valu", f"v_fma_f32 {s(rb, i)}, {s(rb, i)}, %[c2], -%[ml{rb}]"))
             if i == 2:
                 st.append(("valu", f"v_add_f32 %[r{rb}], {s(rb, 0)}, {s(rb, 1)}"))
             elif i > 2:
@@ -444,18 +445,14 @@ def softmax_ops_stale(pout):
     ops += main
     for rb in range(NRB):
         ops.append(("valu", f"v_add_f32 %[r{rb}], %[r{rb}], {s(rb, 15)}"))
+    for rb in range(NRB):  # y = r - lki; lo = li + y; lko = (lo - li) - y
+        ops.append(("valu", f"v_sub_f32 %[a{rb}], %[r{rb}], %[lki{rb}]"))
     for rb in range(NRB):
-        ops.append(("valu", f"v_mov_b32 %[th{rb}], %[l{rb}]"))
+        ops.append(("valu", f"v_add_f32 %[lo{rb}], %[li{rb}], %[a{rb}]"))
     for rb in range(NRB):
-        ops.append(("valu", f"v_mov_b32 %[al{rb}], %[lk{rb}]"))
-    for rb in range(NRB):  # y = r - lk; l = l + y; lk = (l - l_old) - y
-        ops.append(("valu", f"v_sub_f32 %[a{rb}], %[r{rb}], %[lk{rb}]"))
+        ops.append(("valu", f"v_sub_f32 %[lko{rb}], %[lo{rb}], %[li{rb}]"))
     for rb in range(NRB):
-        ops.append(("valu", f"v_add_f32 %[l{rb}], %[th{rb}], %[a{rb}]"))
-    for rb in range(NRB):
-        ops.append(("valu", f"v_sub_f32 %[lk{rb}], %[l{rb}], %[th{rb}]"))
-    for rb in range(NRB):
-        ops.append(("valu", f"v_sub_f32 %[lk{rb}], %[lk{rb}], %[a{rb}]"))
+        ops.append(("valu", f"v_sub_f32 %[lko{rb}], %[lko{rb}], %[a{rb}]"))
     for rb in range(NRB):
         ops.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, 7)}, {s(rb, 14)}, {s(rb, 15)}"))
     # some probability of the lane may exceed 2^tau, or the tile is
@@ -524,7 +521,7 @@ def pv_part(pin, lazy=True):
     if not lazy:
         return out + tail, per
     # Some lane's tile sum passed its bound (label 8): if some probability
-    # may exceed 2^tau the slow path (label 5) restores l, recomputes the
+    # may exceed 2^tau the slow path (label 5) recomputes the
     # scores, masks them again if the tile is cut, and runs the full softmax
     # (running-max vote, rescale factors, dq rescaled with them); either
     # way the tile is then treated as significant (sig_ops).  The odd
@@ -537,8 +534,6 @@ def pv_part(pin, lazy=True):
             "s_cbranch_scc1 5f"]
     out += sig_ops(1 - pin) + tail + ["s_branch 9f"]
     out += ["5:", "s_nop 15", "s_nop 15"]
-    out += [f"v_mov_b32 %[l{rb}], %[th{rb}]" for rb in range(NRB)]
-    out += [f"v_mov_b32 %[lk{rb}], %[al{rb}]" for rb in range(NRB)]
     out += qk_again() + mask_part() + [text for _, text in softmax_ops(1 - pin)]
     out += [f"v_mul_f32 %[dq{rb}], %[dq{rb}], %[al{rb}]" for rb in range(NRB)]
     out += sig_ops(1 - pin)

@@ -181,8 +181,10 @@ __device__ __forceinline__ float wave_max_pair(float x) {
 // KPO during its P.V; the odd tile (PIN = 0) ends with the pair's wait for
 // this wave's copies and barrier, then reads the next pair's kpre (slot KPO)
 // and leaves it in flight (the next block waits for it).  On return pout
-// holds tile v's bf16 probabilities, ml and l the updated running max (log2
-// units) and row sums, al the factor the accumulator must be scaled by, and
+// holds tile v's bf16 probabilities, ml the updated running max (log2
+// units), lo / lko the row sums li / lki with this tile folded in (the
+// caller alternates two register sets by tile parity, so a slow path
+// still finds li as it was), al the factor the accumulator must be scaled by, and
 // bit rb of resc is set when some row of row block rb asked for that
 // rescale (al == 1 for every row of the other blocks).
 //   ka[j]  LDS address of this lane's K row at chunk (2j + h) ^ swizzle;
@@ -207,8 +209,8 @@ __device__ __forceinline__ float wave_max_pair(float x) {
       [acc06] "+a"(acc[0][6]), [acc07] "+a"(acc[0][7]), [acc10] "+a"(acc[1][0]),               \
       [acc11] "+a"(acc[1][1]), [acc12] "+a"(acc[1][2]), [acc13] "+a"(acc[1][3]),               \
       [acc14] "+a"(acc[1][4]), [acc15] "+a"(acc[1][5]), [acc16] "+a"(acc[1][6]),               \
-      [acc17] "+a"(acc[1][7]), [ml0] "+v"(ml[0]), [ml1] "+v"(ml[1]), [l0] "+v"(l[0]),          \
-      [l1] "+v"(l[1]), [lk0] "+v"(lk[0]), [lk1] "+v"(lk[1]), [al0] "=&v"(al[0]),               \
+      [acc17] "+a"(acc[1][7]), [ml0] "+v"(ml[0]), [ml1] "+v"(ml[1]), [lo0] "=&v"(lo[0]),       \
+      [lo1] "=&v"(lo[1]), [lko0] "=&v"(lko[0]), [lko1] "=&v"(lko[1]), [al0] "=&v"(al[0]),      \
       [al1] "=&v"(al[1]), [resc] "=&s"(resc), [any] "=&s"(any),                                                    \
       [a0] "=&v"(a0), [b0] "=&v"(b0), [a1] "=&v"(a1), [b1] "=&v"(b1), [th0] "=&v"(th0),       \
       [th1] "=&v"(th1), [r0] "=&v"(r0), [r1] "=&v"(r1), [c0] "=&s"(c0), [c1] "=&s"(c1), [v0] "=&s"(v0), [v1] "=&s"(v1),        \
@@ -221,7 +223,9 @@ __device__ __forceinline__ float wave_max_pair(float x) {
 #define RA_TILE_INPUT_OPERANDS                                                                  \
   [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [ka2] "v"(ka[2]), [ka3] "v"(ka[3]), [ka4] "v"(ka[4]),    \
       [ka5] "v"(ka[5]), [ka6] "v"(ka[6]), [ka7] "v"(ka[7]), [va0] "v"(va[0]), [va1] "v"(va[1]), \
-      [va2] "v"(va[2]), [va3] "v"(va[3]), [c2] "s"(c2), [tau] "s"(tau), [pbnd] "s"(pbnd), [wk] "s"(wb.k),         \
+      [va2] "v"(va[2]), [va3] "v"(va[3]), [c2] "s"(c2), [tau] "s"(tau), [pbnd] "s"(pbnd),       \
+      [wk] "s"(wb.k), [li0] "v"(li[0]), [li1] "v"(li[1]), [lki0] "v"(lki[0]),                   \
+      [lki1] "v"(lki[1]),                                                                      \
       [np] "s"(wb.np), [wlim] "s"(wb.lim), [wm31] "s"(wb.wm31), [vv] "s"(wb.v), [tt] "s"(wb.t),  \
       [pos0] "v"(pos[0]), [pos1] "v"(pos[1]), [ninf] "v"(ninf), [ko0] "i"(KOFF),                \
       [ko1] "i"(KOFF + 256), [vo000] "i"(VOFF), [vo001] "i"(VOFF + 4096),                       \
@@ -265,7 +269,8 @@ __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], bf16x8 (&p0)[2][
                                            bf16x8 (&p1)[2][2], const bf16x8 (&q)[2][16],
                                            bf16x8 (&kpre)[2], const uint32_t (&ka)[8],
                                            const uint32_t (&va)[4],
-                                           float (&ml)[2], float (&l)[2], float (&lk)[2],
+                                           float (&ml)[2], const float (&li)[2],
+                                           const float (&lki)[2], float (&lo)[2], float (&lko)[2],
                                            float (&dq)[2], float (&bnd)[2], float (&al)[2],
                                            uint32_t& resc, float c2, float tau, float pbnd,
                                            const TileBound& wb, const int (&pos)[2],
@@ -582,14 +587,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   bf16x8 pbuf[2][NRB][NPS];
   float mlog[NRB], lsum[NRB], lsum_q[NRB];  // running max (log2 units), row sums
   float lcomp[NRB], lcomp_q[NRB];            // their compensations (fold_sum)
+  // HD = 256: the row sums and compensations in two sets, read by even
+  // tiles from [0] and odd tiles from [1], each writing the other; the walk
+  // ends on an odd tile, so the final sums are in [0]
+  float lsum2[2][NRB], lcomp2[2][NRB];
   // HD = 256, bf16 output: the output's normaliser is lsum + dq, dq the sum
   // over significant tiles of (rounded - fp32) tile sums; a tile is
   // significant when a lane's tile sum exceeds its bound sbnd
   float dq[NRB], sbnd[NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    mlog[rb] = kNegInf;
+    // a finite start (-FLT_MAX): the first max update needs no -inf guard,
+    // and a row that never sees a key keeps l = 0 and gets lse = -inf
+    mlog[rb] = -__FLT_MAX__;
     lsum[rb] = 0.f;     // fp32 sum of this lane's share of the keys' probabilities (LSE)
+    lsum2[0][rb] = lcomp2[0][rb] = lsum2[1][rb] = lcomp2[1][rb] = 0.f;
     lsum_q[rb] = 0.f;   // the same over the bf16-rounded ones (generic bf16 normaliser)
     lcomp[rb] = lcomp_q[rb] = 0.f;
     dq[rb] = sbnd[rb] = 0.f;
@@ -842,8 +854,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       const i32x4 dkr = desc_of(wk_), dvr = desc_of(wv_);
       tile_hd256<F32OUT, SL * TILE_B, ((SL + 3) % 4) * TILE_B, PB ^ 1, ((SL + 2) % 4) * TILE_B,
                  VBASE + ((SL + 1) % 4) * TILE_B, ((SL + 1) % 4) * TILE_B>(
-          acc, pbuf[0], pbuf[1], qreg, kpre, ka, va, mlog, lsum, lcomp, dq, sbnd, alpha, resc, c2,
-          kTau<F32OUT>, kPBound, tb, pos, dkr, dvr, wk_.off, wv_.off, m0b, dl);
+          acc, pbuf[0], pbuf[1], qreg, kpre, ka, va, mlog, lsum2[SL & 1], lcomp2[SL & 1],
+          lsum2[(SL & 1) ^ 1], lcomp2[(SL & 1) ^ 1], dq, sbnd, alpha, resc, c2, kTau<F32OUT>,
+          kPBound, tb, pos, dkr, dvr, wk_.off, wv_.off, m0b, dl);
       step(wk_, 0);
       step(wv_, 1);
     } else {
@@ -904,7 +917,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     // the rounded probabilities its numerator took (HD = 256: of the
     // significant tiles), fp32 output (hi + lo probabilities) by the fp32
     // sum
-    const float l_own = lsum[rb] - lcomp[rb];
+    const float l_own = ASM256 ? lsum2[0][rb] - lcomp2[0][rb] : lsum[rb] - lcomp[rb];
     const float lq_own = ASM256 ? l_own + dq[rb] : lsum_q[rb] - lcomp_q[rb];
     const float l_tot = l_own + __shfl_xor(l_own, 32);
     const float l_norm = F32OUT ? l_tot : lq_own + __shfl_xor(lq_own, 32);
@@ -916,16 +929,38 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     const int64_t obase = seg * p.seg_out_stride + ((int64_t)token[rb] * p.nq + head[rb]) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
+      if (F32OUT || p.store_f32) {
+        // the two lane halves hold adjacent 4-value groups of a row: each
+        // store writes 32 contiguous bytes per row
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d0 = db * 32 + i4 * 8 + 4 * h_e;
-        const f32x4 o = {acc[rb][db][4 * i4] * inv, acc[rb][db][4 * i4 + 1] * inv,
-                         acc[rb][db][4 * i4 + 2] * inv, acc[rb][db][4 * i4 + 3] * inv};
-        if (F32OUT || p.store_f32) {
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d0 = db * 32 + i4 * 8 + 4 * h_e;
+          const f32x4 o = {acc[rb][db][4 * i4] * inv, acc[rb][db][4 * i4 + 1] * inv,
+                           acc[rb][db][4 * i4 + 2] * inv, acc[rb][db][4 * i4 + 3] * inv};
           *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase + d0) = o;
-        } else {
-          const bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
-          *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.out) + obase + d0) = ob;
+        }
+      } else {
+        // bf16: groups i4 and i4 + 1 of both lane halves are exchanged
+        // (v_permlane32_swap) so that the lower half holds values 0..7 of
+        // group pair i4 and the upper half values 8..15: 16 bytes per lane,
+        // 32 contiguous bytes per row and store
+#pragma unroll
+        for (int i4 = 0; i4 < 4; i4 += 2) {
+          uint32_t a[2], b[2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const bf16x2 pa = {(__bf16)(acc[rb][db][4 * i4 + 2 * k] * inv),
+                               (__bf16)(acc[rb][db][4 * i4 + 2 * k + 1] * inv)};
+            const bf16x2 pb = {(__bf16)(acc[rb][db][4 * i4 + 4 + 2 * k] * inv),
+                               (__bf16)(acc[rb][db][4 * i4 + 4 + 2 * k + 1] * inv)};
+            a[k] = __builtin_bit_cast(uint32_t, pa);
+            b[k] = __builtin_bit_cast(uint32_t, pb);
+          }
+          const auto s0 = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
+          const int d0 = db * 32 + (i4 + h_e) * 8;
+          const i32x4 v = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+          *reinterpret_cast<i32x4*>(static_cast<uint16_t*>(p.out) + obase + d0) = v;
         }
       }
     }
