@@ -83,6 +83,9 @@ CONFIGS = {
     "128k": Workload("128k", 3, 32, 2, 256, 126973, 8, 2048, 2048, 3548, 16316),
     "1m": Workload("1m", 4, 32, 2, 256, 1044480, 8, 2048, 2048, 4096, 131072,
                    k_mult=4.0),
+    # 512k: the context the PCP page's Performance section names beside 1M
+    # (not in its table); the 4k chunk after 508k cached tokens
+    "512k": Workload("512k", 5, 32, 2, 256, 520192, 8, 2048, 2048, 4096, 65536),
 }
 
 
@@ -110,6 +113,10 @@ CONFIGS["tiny_rank1of2"] = rank_share(CONFIGS["tiny"], 2, 1)
 CONFIGS["32k_rank3of8"] = rank_share(CONFIGS["32k"], 8, 3)
 CONFIGS["128k_rank0of8"] = rank_share(CONFIGS["128k"], 8, 0)
 CONFIGS["128k_rank2of8"] = rank_share(CONFIGS["128k"], 8, 2)
+# long-context rank shares (a few hundred rows over a long cache: the split
+# walk's case)
+CONFIGS["512k_rank3of8"] = rank_share(CONFIGS["512k"], 8, 3)
+CONFIGS["1m_rank3of8"] = rank_share(CONFIGS["1m"], 8, 3)
 
 
 def custom(name="custom", **kw):
