@@ -17,16 +17,22 @@ Tiles run in pairs (K and V slots t mod 4).  One block, in order:
   3. O^T += V^T P^T of tile v-1: 32 MFMAs.  After each MFMA an even share
      (by issue cost) of tile v's online softmax is issued.  ASM blocks (bf16
      output): one FMA + exp2 per score against the running max as it
-     stands, the row sums, their compensated fold, the bf16 packing of the
-     probabilities into the next P.V operands, and a test that no lane's
-     probabilities sum past 2^tau.  F32 blocks (fp32 output): first the row
-     max (two in-lane max3 chains, one v_permlane32_swap exchange with lane
-     ^ 32) and the running-max vote, then the same.  The even tile of a
-     pair reads the odd tile's KPRE here.
-  4. ASM blocks, when the test fails (the first tile; a row's max grew by
-     more than tau): restore the row sums, compute the tile's scores again
-     from its K slot, mask them again, and run the F32 blocks' softmax
-     (vote, rescale factors, exact new max where voted).
+     stands, the row sums, their compensated fold (read from one register
+     set, written to the other: even and odd tiles alternate), the bf16
+     packing of the probabilities into the next P.V operands, and a test of
+     each lane's tile sum against a bound.  F32 blocks (fp32 output): first
+     the row max (two in-lane max3 chains, one v_permlane32_swap exchange
+     with lane ^ 32) and the running-max vote, then the same sums; P.V takes
+     each probability as two bf16 operands hi + lo (four MFMAs per step),
+     packed late because the register file holds one hi/lo set.  The even
+     tile of a pair reads the odd tile's KPRE here.
+  4. ASM blocks, when a lane's tile sum passes its bound: if some
+     probability may exceed 2^tau (the first tile; a row's max grew by more
+     than tau) compute the tile's scores again from its K slot, mask them
+     again, and run the F32 blocks' softmax (vote, rescale factors, exact
+     new max where voted); either way treat the tile as significant: add
+     the difference between its bf16-rounded and fp32 row sums to dq (the
+     output is normalised by l + dq) and raise the bound.
   5. Odd tile only (the end of the pair): wait for this wave's copies, meet
      the other waves at the pair's barrier, and read the next pair's first
      KPRE, left in flight: the scalar code between blocks hides its latency.
@@ -38,7 +44,9 @@ are dead outside the block.
 Hazards respected inside the block (gfx950): a VALU op never reads the
 result of a transcendental in the next slot; two wait states between a VALU
 write and v_permlane32_swap, and between an SGPR write and its use as a lane
-mask; MFMA results are read by VALU only after a later MFMA and an s_nop.
+mask; MFMA results are read by VALU only after a later MFMA and an s_nop;
+a v_dot2 result is read by another VALU op only after DOT_WAIT wait states
+(checked by check_dot_hazards on every block written).
 Code after the block must leave the last MFMAs' operands alone for a while
 (the compiler cannot see them); a CPU test checks the compiled kernel.
 

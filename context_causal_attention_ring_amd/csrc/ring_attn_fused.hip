@@ -42,10 +42,15 @@
 //    bound cuts skip the compare entirely.
 //  * Online softmax in log2 units with a lazy running max: a 32-row block
 //    of the accumulator is rescaled only when some row of it raised its max
-//    by more than kTau (a vote), so the common tile costs max, fma, exp2,
-//    add and a bf16 pack per score.  The softmax of tile v is issued between the
+//    by more than kTau (a vote), so the common tile costs fma, exp2, add and
+//    a bf16 pack per score.  The softmax of tile v is issued between the
 //    P.V MFMAs of tile v-1, which do not depend on it, in a hand-ordered
 //    block (one MFMA pair, one V operand read, a slice of softmax work).
+//  * P.V takes bf16 weights.  bf16 output is normalised by the fp32 row sum
+//    corrected, for every tile that holds a sizeable share of a row's
+//    weight, by the rounding of that tile's weights, so numerator and
+//    denominator weight its keys identically; fp32 output feeds P.V each
+//    weight as a bf16 pair hi + lo (two MFMAs per step).
 //  * Workgroup ids are remapped so that the workgroups resident on one XCD
 //    share a KV head and walk the same tiles, keeping the re-streamed K/V in
 //    that XCD's L2, with the KV head's row tiles dealt to its XCDs in turn,
