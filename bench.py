@@ -132,7 +132,8 @@ def setup(w, device, out_fp32=False):
 
 
 def cpu_baseline(w, t, budget_s=12.0):
-    """Time the fp64 oracle (as it stands) on a bounded sample of rows."""
+    """Time the fp64 oracle (as it stands) on a bounded sample of rows
+    (budget_s of oracle time; None: every real row)."""
     import numpy as np
     import oracle
     try:
@@ -145,7 +146,7 @@ def cpu_baseline(w, t, budget_s=12.0):
     rng = np.random.default_rng(0)
     order = rng.permutation(w.real_rows).tolist()
     done, flops, elapsed, blk = 0, 0, 0.0, 8
-    while done < len(order) and elapsed < budget_s:
+    while done < len(order) and (budget_s is None or elapsed < budget_s):
         rows = order[done:done + blk]
         t0 = time.perf_counter()
         oracle.attention_rows(*args, rows, w.scale, positions=w.positions)
@@ -183,7 +184,21 @@ def main():
                     help="rocprofv3 summary holding the measured HBM bytes per fused launch")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for counter calibration)")
+    ap.add_argument("--cpu-only", action="store_true",
+                    help="only time the oracle on the host (no GPU needed) and print its line")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle time for the CPU baseline's sample; 0: every real "
+                         "row of the workload")
     args = ap.parse_args()
+    budget = args.cpu_budget if args.cpu_budget > 0 else None
+
+    if args.cpu_only:
+        import workloads
+        w = workloads.CONFIGS[args.config]
+        line = {"config": {"workload": w.name}, "cpu_baseline": cpu_baseline(
+            w, workloads.generate(w), budget)}
+        print(json.dumps(line), flush=True)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build computes one rank's share of the ring "
@@ -331,7 +346,7 @@ def main():
         two["fused_time_reduction"] = round(1 - ms_per_step / two["ms_per_step"], 4)
         res["two_launch"] = two
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, t)
+        res["cpu_baseline"] = cpu_baseline(w, t, budget)
     print(json.dumps(res), flush=True)
     return 0
 
