@@ -11,7 +11,9 @@ Tiles run in pairs (K and V slots t mod 4).  One block, in order:
      the end.  Every two k-steps one LDS-DMA copy of the next tiles is
      issued (8 per block: the wave's rows of one K tile and one V tile), so
      the vector memory pipe drains them in the MFMAs' shadow rather than
-     stalling the wave.
+     stalling the wave.  The tile's key bound and the walkers' step to the
+     next tile (offsets, bound, tiles left per region) are scalar ops in
+     the same shadow.
   2. Only when the tile is cut by a key bound (a uniform flag): the scores
      of keys at or past each row's bound become -inf.
   3. O^T += V^T P^T of tile v-1: 32 MFMAs.  After each MFMA an even share
@@ -174,7 +176,26 @@ def bound_ops():
          "s_cselect_b32 %[lc], %[wlim], %[lc]"],
         ["s_cmp_ge_i32 %[vv], %[tt]", "s_cselect_b32 %[mflag], 1, %[mflag]",
          "s_cselect_b32 %[lm], 0, %[lm]", "s_cselect_b32 %[lc], -32, %[lc]"],
-    ]
+    ] + walker_ops()
+
+
+def walker_ops():
+    """The walkers' step to the next tile, scalar, in the QK^T MFMAs' shadow
+    after the bound ops have read this tile's bound: the bound walker's key
+    bound moves by dlim (-32 in a shard visit, +32 in the current tiles) and
+    each walker's count of tiles left in its region drops by one; tmin, the
+    smallest count, tells the code after the block whether a walker enters
+    its next region (tmin = 0).  The copy offsets move on after the block's
+    last copy (copy_step_ops)."""
+    return [["s_add_i32 %[wlim], %[wlim], %[dlim]", "s_sub_u32 %[lb], %[lb], 1",
+             "s_sub_u32 %[lk], %[lk], 1", "s_sub_u32 %[lv], %[lv], 1"],
+            ["s_min_u32 %[tmin], %[lb], %[lk]", "s_min_u32 %[tmin], %[tmin], %[lv]"]]
+
+
+def copy_step_ops():
+    """After the block's last copy: the K and V copy walkers' tile offsets
+    move on by one tile."""
+    return ["s_add_u32 %[offk], %[offk], %[tstr]", "s_add_u32 %[offv], %[offv], %[tstr]"]
 
 
 def qk_part(extra=()):
@@ -183,6 +204,7 @@ def qk_part(extra=()):
     # KPRE was read by the block before (or before the loop): wait for it.
     out = ["s_nop 1", "s_waitcnt lgkmcnt(0)"]
     bound = bound_ops()
+    assert len(bound) <= NKS // 2, "one group of scalar ops per even k-step"
     extra = list(extra)
     per = -(-len(extra) // NKS) if extra else 0
     for k in range(NKS):
@@ -204,6 +226,8 @@ def qk_part(extra=()):
             out.append(f"v_mfma_f32_32x32x16_bf16 {stile(rb)}, {kop(k)}, {qop(rb, k)}, {c}")
         if k % 2 == 1:  # one copy of the next tiles per two k-steps
             out += dma(k // 2)
+            if k == NKS - 1:
+                out += copy_step_ops()
         elif k // 2 < len(bound):
             out += bound[k // 2]
         out += extra[k * per:(k + 1) * per]

@@ -207,6 +207,11 @@ __device__ __forceinline__ float wave_max_pair(float x) {
 // slot); its lane offset is dl.ka / dl.kb (dl.va / dl.vb) for a = 0 / 1, and
 // b adds dl.rs16, 16 rows' stride, to the scalar offset.  The caller waits
 // for them (vmcnt) and synchronises before the slots are read.
+// It then steps the walkers to the next tile in the same shadow: offk and
+// offv by tstr (one tile), the bound walker's wlim by dlim, and the tiles
+// left in each walker's region (lb, lk, lv) by one; tmin returns the
+// smallest of these, and the caller enters the next region of each walker
+// whose count reached 0.
 #include "tile_hd256.inc"
 #define RA_TILE_STATE_OPERANDS                                                                  \
   [acc00] "+a"(acc[0][0]), [acc01] "+a"(acc[0][1]), [acc02] "+a"(acc[0][2]),                   \
@@ -220,7 +225,8 @@ __device__ __forceinline__ float wave_max_pair(float x) {
       [a0] "=&v"(a0), [b0] "=&v"(b0), [a1] "=&v"(a1), [b1] "=&v"(b1), [th0] "=&v"(th0),       \
       [th1] "=&v"(th1), [r0] "=&v"(r0), [r1] "=&v"(r1), [c0] "=&s"(c0), [c1] "=&s"(c1), [v0] "=&s"(v0), [v1] "=&s"(v1),        \
       [st] "=&s"(st), [mflag] "=&s"(mflag), [lc] "=&s"(lc), [lm] "=&s"(lm), [cr] "=&s"(cr),     \
-      [cc] "=&s"(cc), RA_TILE_HD256_KPRE_OPERANDS
+      [cc] "=&s"(cc), [offk] "+s"(offk), [offv] "+s"(offv), [wlim] "+s"(wlim), [lb] "+s"(lb), \
+      [lk] "+s"(lk), [lv] "+s"(lv), [tmin] "=&s"(tmin), RA_TILE_HD256_KPRE_OPERANDS
 // bf16 output: the rounded-minus-fp32 sums of the significant tiles, and
 // the tile-sum bound past which a tile is significant
 #define RA_TILE_LQ_OPERANDS                                                                     \
@@ -231,13 +237,13 @@ __device__ __forceinline__ float wave_max_pair(float x) {
       [va2] "v"(va[2]), [va3] "v"(va[3]), [c2] "s"(c2), [tau] "s"(tau), [pbnd] "s"(pbnd),       \
       [wk] "s"(wb.k), [li0] "v"(li[0]), [li1] "v"(li[1]), [lki0] "v"(lki[0]),                   \
       [lki1] "v"(lki[1]),                                                                      \
-      [np] "s"(wb.np), [wlim] "s"(wb.lim), [wm31] "s"(wb.wm31), [vv] "s"(wb.v), [tt] "s"(wb.t),  \
+      [np] "s"(wb.np), [dlim] "s"(dlim), [wm31] "s"(wb.wm31), [vv] "s"(wb.v), [tt] "s"(wb.t),  \
       [pos0] "v"(pos[0]), [pos1] "v"(pos[1]), [ninf] "v"(ninf), [ko0] "i"(KOFF),                \
       [ko1] "i"(KOFF + 256), [vo000] "i"(VOFF), [vo001] "i"(VOFF + 4096),                       \
       [vo010] "i"(VOFF + 256), [vo011] "i"(VOFF + 256 + 4096), [vo100] "i"(VOFF + 8192),        \
       [vo101] "i"(VOFF + 8192 + 4096), [vo110] "i"(VOFF + 8192 + 256),                          \
       [vo111] "i"(VOFF + 8192 + 256 + 4096), [kpo] "i"(KPO), [desck] "s"(desck),                \
-      [descv] "s"(descv), [offk] "s"(offk), [offv] "s"(offv), [m0b] "s"(m0b),                   \
+      [descv] "s"(descv), [tstr] "s"(tstr), [m0b] "s"(m0b),                                      \
       [rs16] "s"(dl.rs16), [dka] "v"(dl.ka), [dkb] "v"(dl.kb), [dva] "v"(dl.va),                \
       [dvb] "v"(dl.vb), [mk0] "i"(MK), [mk1] "i"(MK + 8192), [mk2] "i"(MK + 4096),              \
       [mk3] "i"(MK + 12288), [mv0] "i"(MV), [mv1] "i"(MV + 8192), [mv2] "i"(MV + 4096),         \
@@ -259,7 +265,6 @@ __device__ __forceinline__ void fold_sum(float& l, float& c, float a, float r) {
 
 struct TileBound {    // what the block derives the tile's key bound from (uniform)
   int k, np;          // the tile's region and P (k >= P: current tiles)
-  int lim;            // a visit's keys left from the tile, or its first key's position
   int wm31;           // smallest chunk position of the workgroup's rows - 31
   int v, t;           // the tile and the walk's length (v >= t: past the walk)
 };
@@ -279,9 +284,10 @@ __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], bf16x8 (&p0)[2][
                                            float (&dq)[2], float (&bnd)[2], float (&al)[2],
                                            uint32_t& resc, float c2, float tau, float pbnd,
                                            const TileBound& wb, const int (&pos)[2],
-                                           const i32x4& desck,
-                                           const i32x4& descv, uint32_t offk, uint32_t offv,
-                                           uint32_t m0b, const CopyLanes& dl) {
+                                           const i32x4& desck, const i32x4& descv,
+                                           uint32_t& offk, uint32_t& offv, int& wlim, int dlim,
+                                           int& lb, int& lk, int& lv, uint32_t tstr,
+                                           uint32_t& tmin, uint32_t m0b, const CopyLanes& dl) {
 #if defined(__HIP_DEVICE_COMPILE__)
   float a0, b0, a1, b1, th0, th1, r0, r1;
   uint32_t st, mflag, lc, lm, cr, cc, v0, v1;
@@ -454,12 +460,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
                             // current: chunk position of the tile's first key
     int left;               // tiles of the region from this one on
     int k;                  // region
+    int dlim;               // lim's step per tile: -kBKV in a shard visit, +kBKV after
   };
   // enter region k at its tile b; side 0: K, 1: V
   auto enter = [&](Walker& w, int k, int b, int side) RA_INLINE {
     uint64_t base;
     uint32_t size;
     w.k = k;
+    w.dlim = k < p.P ? -kBKV : kBKV;
     if (k < p.P) {
       int sh = p.ring_start - k;
       sh += (sh < 0) ? p.P : 0;
@@ -482,7 +490,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // one tile on; the region ends after `left` tiles
   auto step = [&](Walker& w, int side) RA_INLINE {
     w.off += tile_stride;
-    w.lim += w.k < p.P ? -kBKV : kBKV;
+    w.lim += w.dlim;
     if (__builtin_expect(--w.left == 0, 0)) enter(w, w.k + 1, 0, side);
   };
   // the walkers at this workgroup's first tile
@@ -848,22 +856,28 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       }
     }
     if constexpr (ASM256) {
-      // the block derives the key bound from these (scalar, in the shadow
-      // of its QK^T MFMAs)
-      const TileBound tb{wb_.k, p.P, wb_.lim, wg_min_pos - 31, v, T};
-      step(wb_, 0);
+      // the block derives the key bound from these and the bound walker's
+      // lim (scalar, in the shadow of its QK^T MFMAs), then steps the three
+      // walkers: lim, the copy offsets and the tiles left in each region
+      const TileBound tb{wb_.k, p.P, wg_min_pos - 31, v, T};
 
       // tile v's probabilities go to buffer v & 1; tile v-1's are read
       constexpr int PB = SL & 1;
       // this block's copies: K of tile v + 2 and V of tile v + 1
       const i32x4 dkr = desc_of(wk_), dvr = desc_of(wv_);
+      uint32_t tmin;
       tile_hd256<F32OUT, SL * TILE_B, ((SL + 3) % 4) * TILE_B, PB ^ 1, ((SL + 2) % 4) * TILE_B,
                  VBASE + ((SL + 1) % 4) * TILE_B, ((SL + 1) % 4) * TILE_B>(
           acc, pbuf[0], pbuf[1], qreg, kpre, ka, va, mlog, lsum2[SL & 1], lcomp2[SL & 1],
           lsum2[(SL & 1) ^ 1], lcomp2[(SL & 1) ^ 1], dq, sbnd, alpha, resc, c2, kTau<F32OUT>,
-          kPBound, tb, pos, dkr, dvr, wk_.off, wv_.off, m0b, dl);
-      step(wk_, 0);
-      step(wv_, 1);
+          kPBound, tb, pos, dkr, dvr, wk_.off, wv_.off, wb_.lim, wb_.dlim, wb_.left, wk_.left,
+          wv_.left, tile_stride, tmin, m0b, dl);
+      // a walker that has finished its region enters the next
+      if (__builtin_expect(tmin == 0, 0)) {
+        if (wb_.left == 0) enter(wb_, wb_.k + 1, 0, 0);
+        if (wk_.left == 0) enter(wk_, wk_.k + 1, 0, 0);
+        if (wv_.left == 0) enter(wv_, wv_.k + 1, 0, 1);
+      }
     } else {
       int lim[NRB];
       bool cut = bounds(wb_, lim);
