@@ -140,24 +140,28 @@ def kpre_reads():
     return [f"ds_read_b128 %[kp{k}], %[ka{k}] offset:%[kpo]" for k in range(2)]
 
 
-def dma(i):
-    """One 16-byte-per-lane LDS-DMA copy of this block's share of the next
-    tiles: i < 4 copies rows of a K tile, i >= 4 rows of a V tile.
+def dma_setup(i):
+    """M0 (the LDS destination) and the scalar offset of copy i, set right
+    after copy i - 1 went out (LDS-DMA reads M0 when issued, and needs one
+    wait state after an SALU write of M0, which the k-steps in between
+    give).  Copy i < 4 moves rows of a K tile, i >= 4 rows of a V tile.
     Instruction j = 2 a + b of wave w moves rows 2 w + 8 a + 16 b and the
     next one.  Rows 16 apart share their swizzle, so lane offset a
     (precomputed, %[d<kind>a] / %[d<kind>b]) serves both b; the 16 rows of
-    b = 1 go into the scalar offset next to the tile's first byte.  M0
-    holds the LDS destination."""
+    b = 1 go into the scalar offset next to the tile's first byte."""
+    kind, j = ("k", i) if i < 4 else ("v", i - 4)
+    out = [f"s_add_u32 m0, %[m0b], %[m{kind}{j}]"]
+    if j & 1:
+        out.append(f"s_add_u32 %[st], %[off{kind}], %[rs16]")
+    return out
+
+
+def dma_issue(i):
+    """Copy i (see dma_setup): 16 bytes per lane into LDS at M0."""
     kind, j = ("k", i) if i < 4 else ("v", i - 4)
     a, b = j >> 1, j & 1
-    out = [f"s_add_u32 m0, %[m0b], %[m{kind}{j}]"]
-    soff = f"%[off{kind}]"
-    if b:
-        out.append(f"s_add_u32 %[st], {soff}, %[rs16]")
-        soff = "%[st]"
-    return out + ["s_nop 0",
-                  f"buffer_load_dwordx4 %[d{kind}{'b' if a else 'a'}], %[desc{kind}], {soff} "
-                  "offen lds"]
+    soff = "%[st]" if b else f"%[off{kind}]"
+    return [f"buffer_load_dwordx4 %[d{kind}{'b' if a else 'a'}], %[desc{kind}], {soff} offen lds"]
 
 
 def bound_ops():
@@ -202,7 +206,7 @@ def qk_part(extra=()):
     """S^T = K Q^T with the block's copies and bound ops; `extra` VALU ops
     (independent of the scores) are spread over the k-steps, two per step."""
     # KPRE was read by the block before (or before the loop): wait for it.
-    out = ["s_nop 1", "s_waitcnt lgkmcnt(0)"]
+    out = ["s_nop 1", "s_waitcnt lgkmcnt(0)"] + dma_setup(0)
     bound = bound_ops()
     assert len(bound) <= NKS // 2, "one group of scalar ops per even k-step"
     extra = list(extra)
@@ -225,9 +229,11 @@ def qk_part(extra=()):
             c = "0" if k == 0 else stile(rb)
             out.append(f"v_mfma_f32_32x32x16_bf16 {stile(rb)}, {kop(k)}, {qop(rb, k)}, {c}")
         if k % 2 == 1:  # one copy of the next tiles per two k-steps
-            out += dma(k // 2)
+            out += dma_issue(k // 2)
             if k == NKS - 1:
                 out += copy_step_ops()
+            else:
+                out += dma_setup(k // 2 + 1)
         elif k // 2 < len(bound):
             out += bound[k // 2]
         out += extra[k * per:(k + 1) * per]
