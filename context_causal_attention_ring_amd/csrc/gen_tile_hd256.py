@@ -73,6 +73,13 @@ KPRE = 236         # K operands of k-steps 0 and 1 (pinned), read ahead: v[KPRE 
 RING0 = 244        # operand ring (clobbered): group j -> v[RING0 + 4j : RING0 + 4j + 3]
 KPRE_STEP = 2      # P.V step of an even tile after which the odd tile's KPRE is read
 
+# READ_NOTE: an LDS read issued right behind an MFMA costs the wave little;
+# issued after VALU work in an MFMA's shadow it stalls the next MFMA (a
+# loop of MFMAs with one transposing V read and five VALU issue units each
+# ran at 38 cycles per MFMA with the reads behind the MFMA, 43 with them
+# after the VALU ops, on gfx950).  Every LDS read of the block goes out
+# right behind an MFMA.
+
 # Issue cost of one instruction, in units of one full-rate VALU op (measured
 # on gfx950: v_exp_f32 is half rate; SALU and s_nop issue in about a cycle).
 COST = {"valu": 1.0, "trans": 2.0, "dot": 2.0, "salu": 0.5, "nop": 0.5}
@@ -211,23 +218,21 @@ def qk_part(extra=()):
     assert len(bound) <= NKS // 2, "one group of scalar ops per even k-step"
     extra = list(extra)
     per = -(-len(extra) // NKS) if extra else 0
+    pending = []  # LDS reads in flight, in issue order
     for k in range(NKS):
-        wait = None
-        if k + 2 < NKS:
-            out.append(kread(k + 2))
-            if k >= 2:
-                wait = 2
-        elif k == NKS - 2:
-            out += vreads(0)
-            wait = 3
-        else:
-            out += vreads(1)
-            wait = 4
-        if wait is not None:
-            out.append(f"s_waitcnt lgkmcnt({wait})")
+        if k >= 2:  # this step's K operand (read two steps ahead) must be in
+            out.append(f"s_waitcnt lgkmcnt({len(pending) - 1 - pending.index(k)})")
+            pending = pending[pending.index(k) + 1:]
         for rb in range(NRB):
             c = "0" if k == 0 else stile(rb)
             out.append(f"v_mfma_f32_32x32x16_bf16 {stile(rb)}, {kop(k)}, {qop(rb, k)}, {c}")
+            if rb == 0:  # LDS reads go out right behind an MFMA (see READ_NOTE)
+                if k + 2 < NKS:
+                    out.append(kread(k + 2))
+                    pending.append(k + 2)
+                else:
+                    out += vreads(k + 2 - NKS)
+                    pending += ["v", "v"]
         if k % 2 == 1:  # one copy of the next tiles per two k-steps
             out += dma_issue(k // 2)
             if k == NKS - 1:
@@ -549,7 +554,7 @@ def pv_part(pin, lazy=True):
         for rb in range(NRB):
             out.append(f"v_mfma_f32_32x32x16_bf16 %[acc{rb}{db}], {grp(vgroup(t))}, "
                        f"{pbop(pin, rb, ks)}, %[acc{rb}{db}]")
-            if rb == NRB - 1:
+            if rb == 0:  # LDS reads right behind the MFMA, before the VALU ops
                 if even and t == KPRE_STEP:
                     out += kpre_reads()
                 if t + 2 < NT:
@@ -612,7 +617,7 @@ def pv_part_f32(even):
             buf, rb = divmod(u, NRB)
             out.append(f"v_mfma_f32_32x32x16_bf16 %[acc{rb}{db}], {grp(vgroup(t))}, "
                        f"{pbop(buf, rb, ks)}, %[acc{rb}{db}]")
-            if u == 2 * NRB - 1:
+            if u == 0:  # LDS reads right behind the MFMA, before the VALU ops
                 if even and t == KPRE_STEP:
                     out += kpre_reads()
                 if t + 2 < NT:
