@@ -184,6 +184,9 @@ def main():
                     help="rocprofv3 summary holding the measured HBM bytes per fused launch")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for counter calibration)")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="time kv_cache_write and the attention as two launches (default with "
+                         "one segment: ring_attn_prefill_write, both in one launch)")
     ap.add_argument("--cpu-only", action="store_true",
                     help="only time the oracle on the host (no GPU needed) and print its line")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
@@ -234,7 +237,21 @@ def main():
     ws_bytes = ra.ra_split_workspace_bytes(dims, args.splits)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
 
+    # The step: the chunk's strided cache write and the attention.  With one
+    # segment they share one launch (ring_attn_prefill_write); a split walk
+    # (or --separate-write) runs kv_cache_write first.
+    fused_write = args.splits == 1 and not args.separate_write
+
     def step(ev=None):
+        if fused_write:
+            if ev is not None:
+                ev[0].record(stream)
+            ra.ring_attn_prefill_write(d["q"], d["k_cache"], d["v_cache"], d["k_cur"],
+                                       d["v_cur"], w.cache_len, w.P, layout, w.n_cur_real,
+                                       d["out"], d["lse"], dims)
+            if ev is not None:
+                ev[1].record(stream)
+            return
         ra.kv_cache_write(d["k_cur"], d["v_cur"], w.n_cur_real, d["k_cache"], d["v_cache"],
                           w.cache_len, w.P, layout, dims)
         if ev is not None:
@@ -329,7 +346,8 @@ def main():
                                f"kv_cache_write of the chunk",
                    "cache_len": w.cache_len, "P": w.P, "q_rows": w.q_rows,
                    "real_rows": w.real_rows, "nq": w.nq, "nkv": w.nkv, "hd": w.hd,
-                   "splits": args.splits, "flop_per_step": F},
+                   "splits": args.splits, "flop_per_step": F,
+                   "write": "in the fused launch" if fused_write else "kv_cache_write launch"},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "ms_per_chunk": round(ms_per_step, 4),
         "ms_per_step_cold_median": round(sorted(cold)[len(cold) // 2], 4),

@@ -33,6 +33,15 @@ struct FusedParams {
   int32_t store_f32;        // out is written in fp32 (out_f32, or a split launch's partials)
   int32_t regions;          // 1: cache (ring) only, 2: current only, 3: both
   float scale_log2e;        // softmax scale * log2(e)
+  // The strided cache write fused into the launch (write_tokens > 0): current
+  // token t < write_tokens goes to global position write_pos0 + t of
+  // wk_cache / wv_cache, each workgroup copying write_per_wg tokens.
+  uint16_t* wk_cache;
+  uint16_t* wv_cache;
+  int64_t write_pos0;
+  int32_t write_tokens;
+  int32_t write_per_wg;
+  int32_t write_chunks;     // 16-byte chunks per token row (NKV * HD / 8)
 };
 
 // Arguments of the log-sum-exp merge of two partial attentions.

@@ -51,6 +51,9 @@
 //    weight, by the rounding of that tile's weights, so numerator and
 //    denominator weight its keys identically; fp32 output feeds P.V each
 //    weight as a bf16 pair hi + lo (two MFMAs per step).
+//  * With the strided cache write fused in (ring_attn_prefill_write), each
+//    workgroup copies its share of the chunk's tokens into their cache
+//    slots after its epilogue; the walk never reads those slots.
 //  * Workgroup ids are remapped so that the workgroups resident on one XCD
 //    share a KV head and walk the same tiles, keeping the re-streamed K/V in
 //    that XCD's L2, with the KV head's row tiles dealt to its XCDs in turn,
@@ -986,6 +989,30 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     if (h_e == 0 && p.lse != nullptr)
       p.lse[((int64_t)seg * p.nq + head[rb]) * p.q_rows + token[rb]] =
           (mlog[rb] + __log2f(l_tot)) * kLn2;
+  }
+
+  // The fused strided write: this workgroup's tokens of the chunk go to their
+  // cache slots (position p = write_pos0 + t: shard (p / I) mod P, slot
+  // ((p / I) / P) * I + p mod I), 16 bytes a thread, K and V alike.  The
+  // walk reads positions below write_pos0 only, so no workgroup reads a slot
+  // written here.
+  if (p.write_tokens > 0) {
+    const int64_t t0 = (int64_t)logical * p.write_per_wg;
+    const int64_t t1 = min((int64_t)p.write_tokens, t0 + p.write_per_wg);
+    for (int64_t idx = t0 * p.write_chunks + threadIdx.x; idx < t1 * p.write_chunks;
+         idx += blockDim.x) {
+      const int64_t t = idx / p.write_chunks;
+      const int c = (int)(idx - t * p.write_chunks);
+      const int64_t pos = p.write_pos0 + t;
+      const int64_t unit = pos / p.interleave;
+      const int64_t sh = unit % p.P;
+      const int64_t slot = (unit / p.P) * p.interleave + (pos - unit * p.interleave);
+      const int64_t dst = (sh * p.shard_cap + slot) * p.write_chunks + c;
+      const i32x4 kx = reinterpret_cast<const i32x4*>(p.k_cur)[idx];
+      const i32x4 vx = reinterpret_cast<const i32x4*>(p.v_cur)[idx];
+      reinterpret_cast<i32x4*>(p.wk_cache)[dst] = kx;
+      reinterpret_cast<i32x4*>(p.wv_cache)[dst] = vx;
+    }
   }
 }
 

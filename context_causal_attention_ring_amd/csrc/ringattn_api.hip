@@ -140,10 +140,18 @@ void log_geometry(const ra::FusedParams& p, int hd) {
 // current, 3: both), with the walk of every row tile cut into `splits`
 // segments.  With splits > 1, out and lse receive the segments' partials
 // ([splits, C, NQ, HD] and [splits, NQ, C]).
+// The strided cache write a launch may carry (ring_attn_prefill_write).
+struct FusedWrite {
+  void* k_cache;
+  void* v_cache;
+  int32_t n_tokens;
+};
+
 int prefill_regions(const void* q, const void* k_cache, const void* v_cache, const void* k_cur,
                     const void* v_cur, int64_t cache_len, int32_t P,
                     ra_stripe_layout_t stripe_layout, int32_t regions, void* out, float* lse,
-                    const ra_dims_t* dims, void* stream, int32_t splits = 1) {
+                    const ra_dims_t* dims, void* stream, int32_t splits = 1,
+                    const FusedWrite* write = nullptr) {
   if (int rc = check_heads(dims)) return rc;
   if (int rc = check_layout(P, stripe_layout, cache_len)) return rc;
   const ra_dims_t& d = *dims;
@@ -281,6 +289,14 @@ int prefill_regions(const void* q, const void* k_cache, const void* v_cache, con
   p.scale_log2e = scale * 1.4426950408889634f;
   if ((int64_t)p.nb * P >= lim31)
     return fail(RA_ERR_UNSUPPORTED, "too many ring tiles");
+  if (write && write->n_tokens > 0) {
+    p.wk_cache = static_cast<uint16_t*>(write->k_cache);
+    p.wv_cache = static_cast<uint16_t*>(write->v_cache);
+    p.write_pos0 = cache_len;
+    p.write_tokens = write->n_tokens;
+    p.write_per_wg = (write->n_tokens + p.grid_real - 1) / p.grid_real;
+    p.write_chunks = (int32_t)(rowstride / 16);
+  }
 
   log_geometry(p, HD);
   hipError_t e = ra::launch_fused(p, HD, static_cast<hipStream_t>(stream));
@@ -299,6 +315,51 @@ int ring_attn_prefill(const void* q, const void* k_cache, const void* v_cache, c
                       const ra_dims_t* dims, void* stream) {
   return prefill_regions(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
                          RA_REGION_CACHE | RA_REGION_CURRENT, out, lse, dims, stream);
+}
+
+int ring_attn_prefill_write(const void* q, void* k_cache, void* v_cache, const void* k_cur,
+                            const void* v_cur, int64_t cache_len, int32_t P,
+                            ra_stripe_layout_t stripe_layout, int32_t n_tokens, void* out,
+                            float* lse, const ra_dims_t* dims, void* stream) {
+  if (int rc = check_heads(dims)) return rc;
+  if (int rc = check_layout(P, stripe_layout, cache_len)) return rc;
+  const ra_dims_t& d = *dims;
+  if (n_tokens < 0 || n_tokens > d.cur_len)
+    return fail(RA_ERR_INVALID_ARG, "n_tokens must be in [0, cur_len=%d]; got %d", d.cur_len,
+                n_tokens);
+  // the rows no launch computes: the write alone
+  if (d.real_rows == 0 || n_tokens == 0) {
+    if (d.real_rows == 0)
+      return kv_cache_write(k_cur, v_cur, n_tokens, k_cache, v_cache, cache_len, P,
+                            stripe_layout, dims, stream);
+    return ring_attn_prefill(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
+                             out, lse, dims, stream);
+  }
+  const int64_t end = cache_len + n_tokens;
+  const int64_t need = shard_len(end, P, stripe_layout.interleave, 0);
+  if (need > d.shard_cap)
+    return fail(RA_ERR_INVALID_ARG,
+                "writing positions [%lld, %lld) needs %lld slots in shard 0 but shard_cap is %lld",
+                (long long)cache_len, (long long)end, (long long)need, (long long)d.shard_cap);
+  if (!k_cache || !v_cache)
+    return fail(RA_ERR_INVALID_ARG, "k_cache and v_cache must not be NULL when n_tokens > 0");
+  // the caches are written: no other tensor may share their bytes
+  const int64_t row_bytes = (int64_t)d.num_kv_heads * d.head_dim * 2;
+  const int64_t cache_bytes = row_bytes * P * d.shard_cap;
+  if (overlaps(k_cache, cache_bytes, v_cache, cache_bytes))
+    return fail(RA_ERR_INVALID_ARG, "k_cache and v_cache overlap");
+  struct R { const void* p; int64_t n; };
+  const int64_t out_bytes = (int64_t)d.q_rows * d.num_q_heads * d.head_dim *
+                            (d.out_dtype == RA_DTYPE_FP32 ? 4 : 2);
+  const R others[] = {{q, (int64_t)d.q_rows * d.num_q_heads * d.head_dim * 2},
+                      {k_cur, row_bytes * d.cur_len}, {v_cur, row_bytes * d.cur_len},
+                      {out, out_bytes}, {lse, (int64_t)d.num_q_heads * d.q_rows * 4}};
+  for (const R& r : others)
+    if (overlaps(k_cache, cache_bytes, r.p, r.n) || overlaps(v_cache, cache_bytes, r.p, r.n))
+      return fail(RA_ERR_INVALID_ARG, "a cache tensor overlaps q, k_cur, v_cur, out or lse");
+  const FusedWrite w{k_cache, v_cache, n_tokens};
+  return prefill_regions(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
+                         RA_REGION_CACHE | RA_REGION_CURRENT, out, lse, dims, stream, 1, &w);
 }
 
 int ring_attn_partial(const void* q, const void* k_cache, const void* v_cache, const void* k_cur,

@@ -133,6 +133,28 @@ int ring_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
                       int32_t P, ra_stripe_layout_t stripe_layout, void* out,
                       float* lse, const ra_dims_t* dims, void* stream);
 
+/*
+ * ring_attn_prefill_write -- ring_attn_prefill and kv_cache_write of the
+ * same chunk in one launch: the pages pair the fused attention launch with
+ * a strided write of the chunk's K/V into the striped cache (Summary
+ * section; Testing section: the write is bit-exact).  Arguments as
+ * ring_attn_prefill, the caches writable, plus
+ *   n_tokens  current tokens 0 .. n_tokens-1 to write, 0 <= n_tokens <=
+ *             dims->cur_len; token t goes to global position cache_len + t
+ *             exactly as kv_cache_write puts it
+ * The walk reads cache positions below cache_len only and the write touches
+ * positions from cache_len on, so out, lse and the caches equal those of
+ * kv_cache_write and ring_attn_prefill called one after the other, bit for
+ * bit.  Every written slot must be < shard_cap; the caches must not overlap
+ * q, k_cur, v_cur, out or lse, nor each other (RA_ERR_INVALID_ARG).  One
+ * launch, never split.  With real_rows == 0 only the write runs; with
+ * n_tokens == 0 only the attention.
+ */
+int ring_attn_prefill_write(const void* q, void* k_cache, void* v_cache, const void* k_cur,
+                            const void* v_cur, int64_t cache_len, int32_t P,
+                            ra_stripe_layout_t stripe_layout, int32_t n_tokens, void* out,
+                            float* lse, const ra_dims_t* dims, void* stream);
+
 /* Largest number of segments a split launch may cut each row's walk into. */
 #define RA_MAX_SPLITS 64
 

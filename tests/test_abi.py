@@ -226,6 +226,37 @@ def test_write_zero_tokens_is_a_no_op():
     assert call_write(dims(), n=0) == 0
 
 
+def call_prefill_write(d, n=128, cache_len=512, P=2, layout=(1, 0), ptrs=None,
+                       out=FAKE + 0x8000000, lse=None):
+    q, kc, vc, kcur, vcur = ptrs or (FAKE, FAKE + 0x1000000, FAKE + 0x2000000,
+                                     FAKE + 0x3000000, FAKE + 0x4000000)
+    return ra.lib().ring_attn_prefill_write(q, kc, vc, kcur, vcur, cache_len, P,
+                                            ra.StripeLayout(*layout), n, out, lse,
+                                            ctypes.byref(d), None)
+
+
+BAD_PREFILL_WRITE = [
+    (dict(d=dims(), n=-1), 1, "n_tokens"),
+    (dict(d=dims(), n=129), 1, "n_tokens"),                       # k_cur holds cur_len=128
+    (dict(d=dims(shard_cap=319)), 1, "shard_cap"),               # the write needs 320 slots
+    (dict(d=dims(), ptrs=(FAKE, 0, FAKE + 0x2000000, FAKE + 0x3000000, FAKE + 0x4000000)),
+     1, "NULL"),
+    (dict(d=dims(), out=FAKE + 0x1000010), 1, "overlaps"),        # out inside k_cache
+    (dict(d=dims(), lse=FAKE + 0x2000000), 1, "overlaps"),        # lse inside v_cache
+    (dict(d=dims(), ptrs=(FAKE + 0x1000000, FAKE + 0x1000000, FAKE + 0x2000000,
+                          FAKE + 0x3000000, FAKE + 0x4000000)), 1, "overlaps"),  # q = k_cache
+    (dict(d=dims(num_q_heads=6, num_kv_heads=4)), 1, "multiple"),
+    (dict(d=dims(), layout=(1, 2)), 1, "ring_start"),
+    (dict(d=dims(scale=-1.0)), 1, "scale"),                       # the attention's own checks
+]
+
+
+@pytest.mark.parametrize("kw,code,msg", BAD_PREFILL_WRITE)
+def test_prefill_write_rejects_bad_arguments(kw, code, msg):
+    assert call_prefill_write(**kw) == code
+    assert msg in ra.lib().ra_last_error().decode()
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ra, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(ra, "_lib", None)
