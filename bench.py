@@ -185,8 +185,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for counter calibration)")
     ap.add_argument("--separate-write", action="store_true",
-                    help="time kv_cache_write and the attention as two launches (default with "
-                         "one segment: ring_attn_prefill_write, both in one launch)")
+                    help="time kv_cache_write as its own launch before the attention "
+                         "(default without a split: the write inside the attention launch)")
     ap.add_argument("--cpu-only", action="store_true",
                     help="only time the oracle on the host (no GPU needed) and print its line")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
@@ -237,18 +237,21 @@ def main():
     ws_bytes = ra.ra_split_workspace_bytes(dims, args.splits)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
 
-    # The step: the chunk's strided cache write and the attention.  With one
-    # segment they share one launch (ring_attn_prefill_write); a split walk
-    # (or --separate-write) runs kv_cache_write first.
+    # The step: the chunk's strided cache write and the attention.  Without a
+    # split the write runs inside the attention launch (ring_attn_prefill_write);
+    # a split walk, whose segments all end together, keeps kv_cache_write as
+    # its own launch before it (measured: the copy at the end of every
+    # segment costs the split launch more than the separate launch does), as
+    # does --separate-write.
     fused_write = args.splits == 1 and not args.separate_write
 
     def step(ev=None):
         if fused_write:
             if ev is not None:
                 ev[0].record(stream)
-            ra.ring_attn_prefill_write(d["q"], d["k_cache"], d["v_cache"], d["k_cur"],
-                                       d["v_cur"], w.cache_len, w.P, layout, w.n_cur_real,
-                                       d["out"], d["lse"], dims)
+            ra.ring_attn_prefill_split_write(d["q"], d["k_cache"], d["v_cache"], d["k_cur"],
+                                             d["v_cur"], w.cache_len, w.P, layout, args.splits,
+                                             ws, w.n_cur_real, d["out"], d["lse"], dims)
             if ev is not None:
                 ev[1].record(stream)
             return

@@ -18,13 +18,14 @@ __all__ = ["StripeLayout", "Dims", "RingAttnError", "lib", "ring_attn_prefill",
            "RA_REGION_CACHE", "RA_REGION_CURRENT", "ring_attn_prefill_split",
            "ra_split_workspace_bytes", "ra_split_suggest", "RA_MAX_SPLITS", "load",
            "SYNC_LIB_PATH", "ring_attn_prefill_split_noalloc", "RA_NOALLOC_SCRATCH_BYTES",
-           "ring_attn_prefill_write"]
+           "ring_attn_prefill_write", "ring_attn_prefill_split_write"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn.so")
 # The checking build (every tile of the fused kernel fenced by a wait and a
 # barrier); tests compare it bit for bit with the product library.
 SYNC_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn_sync.so")
 EXPORTED_SYMBOLS = ("ring_attn_prefill", "ring_attn_prefill_write", "ring_attn_prefill_split",
+                    "ring_attn_prefill_split_write",
                     "ra_split_workspace_bytes",
                     "ring_attn_prefill_split_noalloc",
                     "ra_split_suggest",
@@ -74,6 +75,9 @@ def load(path):
     L.ring_attn_prefill_write.argtypes = [vp, vp, vp, vp, vp, i64, i32, StripeLayout, i32, vp,
                                           vp, ctypes.POINTER(Dims), vp]
     L.ring_attn_prefill_write.restype = ctypes.c_int
+    L.ring_attn_prefill_split_write.argtypes = [vp, vp, vp, vp, vp, i64, i32, StripeLayout, i32,
+                                                vp, i64, i32, vp, vp, ctypes.POINTER(Dims), vp]
+    L.ring_attn_prefill_split_write.restype = ctypes.c_int
     L.ring_attn_prefill_split.argtypes = [vp, vp, vp, vp, vp, i64, i32, StripeLayout, i32,
                                           vp, i64, vp, vp, ctypes.POINTER(Dims), vp]
     L.ring_attn_prefill_split.restype = ctypes.c_int
@@ -156,6 +160,19 @@ def ring_attn_prefill_write(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, str
                                          _ptr(v_cur), cache_len, P, stripe_layout, n_tokens,
                                          _ptr(out), _ptr(lse), ctypes.byref(dims),
                                          _stream(stream)))
+
+
+def ring_attn_prefill_split_write(q, k_cache, v_cache, k_cur, v_cur, cache_len, P,
+                                  stripe_layout, splits, workspace, n_tokens, out, lse, dims,
+                                  stream=None):
+    """Same arguments as the C entry point, with torch tensors for buffers
+    (``workspace`` as in ring_attn_prefill_split)."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().ring_attn_prefill_split_write(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                               _ptr(k_cur), _ptr(v_cur), cache_len, P,
+                                               stripe_layout, splits, _ptr(workspace), nbytes,
+                                               n_tokens, _ptr(out), _ptr(lse),
+                                               ctypes.byref(dims), _stream(stream)))
 
 
 def ra_split_suggest(dims, num_cus):

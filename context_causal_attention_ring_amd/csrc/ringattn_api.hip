@@ -305,6 +305,110 @@ int prefill_regions(const void* q, const void* k_cache, const void* v_cache, con
   return RA_OK;
 }
 
+
+// ring_attn_prefill_split, with the strided write in the launch when
+// `write` is given (its arguments checked by the caller).
+int split_impl(const void* q, const void* k_cache, const void* v_cache, const void* k_cur,
+               const void* v_cur, int64_t cache_len, int32_t P, ra_stripe_layout_t stripe_layout,
+               int32_t splits, void* workspace, int64_t workspace_bytes, void* out, float* lse,
+               const ra_dims_t* dims, void* stream, const FusedWrite* write) {
+  int64_t need = 0;
+  if (int rc = ra_split_workspace_bytes(dims, splits, &need)) return rc;
+  if (splits == 1)
+    return prefill_regions(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
+                           RA_REGION_CACHE | RA_REGION_CURRENT, out, lse, dims, stream, 1, write);
+  const ra_dims_t& d = *dims;
+  if (d.real_rows > 0 && !out) return fail(RA_ERR_INVALID_ARG, "out must not be NULL");
+  if (!workspace) return fail(RA_ERR_INVALID_ARG, "workspace must not be NULL when splits > 1");
+  if (!aligned16(workspace))
+    return fail(RA_ERR_INVALID_ARG, "every tensor pointer must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(RA_ERR_INVALID_ARG, "workspace_bytes %lld is below the %lld bytes splits=%d needs",
+                (long long)workspace_bytes, (long long)need, splits);
+  // the workspace must not overlap the caller's tensors
+  const int64_t C = d.q_rows, NQ = d.num_q_heads, HD = d.head_dim, NKV = d.num_kv_heads;
+  struct R { const void* p; int64_t n; };
+  // (the caches in full when the launch writes them)
+  const int64_t cache_bytes = (cache_len > 0 || write) ? (int64_t)P * d.shard_cap * NKV * HD * 2 : 0;
+  const R others[] = {{q, C * NQ * HD * 2}, {k_cache, cache_bytes}, {v_cache, cache_bytes},
+                      {k_cur, (int64_t)d.cur_len * NKV * HD * 2}, {v_cur, (int64_t)d.cur_len * NKV * HD * 2},
+                      {out, C * NQ * HD * (d.out_dtype == RA_DTYPE_FP32 ? 4 : 2)}, {lse, NQ * C * 4}};
+  for (const R& r : others)
+    if (overlaps(workspace, need, r.p, r.n))
+      return fail(RA_ERR_INVALID_ARG, "workspace overlaps another tensor");
+  char* ws = static_cast<char*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(ws + split_part_bytes(d, splits));
+  if (int rc = prefill_regions(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
+                               RA_REGION_CACHE | RA_REGION_CURRENT, ws, part_lse, dims, stream,
+                               splits, write))
+    return rc;
+  if (d.real_rows == 0) return RA_OK;
+  ra::MergeSplitsParams m{};
+  m.part_o = ws;
+  m.part_lse = part_lse;
+  m.out = out;
+  m.lse = lse;
+  m.splits = splits;
+  m.q_rows = d.q_rows;
+  m.real_rows = d.real_rows;
+  m.nq = d.num_q_heads;
+  m.hd = d.head_dim;
+  m.parts_f32 = 1;
+  m.out_f32 = d.out_dtype == RA_DTYPE_FP32;
+  hipError_t e = ra::launch_merge_splits(m, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(RA_ERR_HIP, "split merge launch failed: %s", hipGetErrorString(e));
+  return RA_OK;
+}
+
+// The strided write's own checks (those of kv_cache_write, plus what a
+// launch that reads and writes the caches at once needs), then the
+// attention launch, split or not, carrying the write.
+int prefill_write_impl(const void* q, void* k_cache, void* v_cache, const void* k_cur,
+                       const void* v_cur, int64_t cache_len, int32_t P,
+                       ra_stripe_layout_t stripe_layout, int32_t splits, void* workspace,
+                       int64_t workspace_bytes, int32_t n_tokens, void* out, float* lse,
+                       const ra_dims_t* dims, void* stream) {
+  if (int rc = check_heads(dims)) return rc;
+  if (int rc = check_layout(P, stripe_layout, cache_len)) return rc;
+  const ra_dims_t& d = *dims;
+  if (n_tokens < 0 || n_tokens > d.cur_len)
+    return fail(RA_ERR_INVALID_ARG, "n_tokens must be in [0, cur_len=%d]; got %d", d.cur_len,
+                n_tokens);
+  // no rows to compute: the write alone; nothing to write: the attention alone
+  if (d.real_rows == 0)
+    return kv_cache_write(k_cur, v_cur, n_tokens, k_cache, v_cache, cache_len, P, stripe_layout,
+                          dims, stream);
+  if (n_tokens == 0)
+    return split_impl(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout, splits,
+                      workspace, workspace_bytes, out, lse, dims, stream, nullptr);
+  const int64_t end = cache_len + n_tokens;
+  const int64_t need = shard_len(end, P, stripe_layout.interleave, 0);
+  if (need > d.shard_cap)
+    return fail(RA_ERR_INVALID_ARG,
+                "writing positions [%lld, %lld) needs %lld slots in shard 0 but shard_cap is %lld",
+                (long long)cache_len, (long long)end, (long long)need, (long long)d.shard_cap);
+  if (!k_cache || !v_cache)
+    return fail(RA_ERR_INVALID_ARG, "k_cache and v_cache must not be NULL when n_tokens > 0");
+  // the caches are written: no other tensor may share their bytes
+  const int64_t row_bytes = (int64_t)d.num_kv_heads * d.head_dim * 2;
+  const int64_t cache_bytes = row_bytes * P * d.shard_cap;
+  if (overlaps(k_cache, cache_bytes, v_cache, cache_bytes))
+    return fail(RA_ERR_INVALID_ARG, "k_cache and v_cache overlap");
+  const int64_t out_bytes = (int64_t)d.q_rows * d.num_q_heads * d.head_dim *
+                            (d.out_dtype == RA_DTYPE_FP32 ? 4 : 2);
+  struct R { const void* p; int64_t n; };
+  const R others[] = {{q, (int64_t)d.q_rows * d.num_q_heads * d.head_dim * 2},
+                      {k_cur, row_bytes * d.cur_len}, {v_cur, row_bytes * d.cur_len},
+                      {out, out_bytes}, {lse, (int64_t)d.num_q_heads * d.q_rows * 4}};
+  for (const R& r : others)
+    if (overlaps(k_cache, cache_bytes, r.p, r.n) || overlaps(v_cache, cache_bytes, r.p, r.n))
+      return fail(RA_ERR_INVALID_ARG, "a cache tensor overlaps q, k_cur, v_cur, out or lse");
+  const FusedWrite w{k_cache, v_cache, n_tokens};
+  return split_impl(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout, splits,
+                    workspace, workspace_bytes, out, lse, dims, stream, &w);
+}
+
 }  // namespace
 
 extern "C" {
@@ -321,45 +425,17 @@ int ring_attn_prefill_write(const void* q, void* k_cache, void* v_cache, const v
                             const void* v_cur, int64_t cache_len, int32_t P,
                             ra_stripe_layout_t stripe_layout, int32_t n_tokens, void* out,
                             float* lse, const ra_dims_t* dims, void* stream) {
-  if (int rc = check_heads(dims)) return rc;
-  if (int rc = check_layout(P, stripe_layout, cache_len)) return rc;
-  const ra_dims_t& d = *dims;
-  if (n_tokens < 0 || n_tokens > d.cur_len)
-    return fail(RA_ERR_INVALID_ARG, "n_tokens must be in [0, cur_len=%d]; got %d", d.cur_len,
-                n_tokens);
-  // the rows no launch computes: the write alone
-  if (d.real_rows == 0 || n_tokens == 0) {
-    if (d.real_rows == 0)
-      return kv_cache_write(k_cur, v_cur, n_tokens, k_cache, v_cache, cache_len, P,
-                            stripe_layout, dims, stream);
-    return ring_attn_prefill(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
-                             out, lse, dims, stream);
-  }
-  const int64_t end = cache_len + n_tokens;
-  const int64_t need = shard_len(end, P, stripe_layout.interleave, 0);
-  if (need > d.shard_cap)
-    return fail(RA_ERR_INVALID_ARG,
-                "writing positions [%lld, %lld) needs %lld slots in shard 0 but shard_cap is %lld",
-                (long long)cache_len, (long long)end, (long long)need, (long long)d.shard_cap);
-  if (!k_cache || !v_cache)
-    return fail(RA_ERR_INVALID_ARG, "k_cache and v_cache must not be NULL when n_tokens > 0");
-  // the caches are written: no other tensor may share their bytes
-  const int64_t row_bytes = (int64_t)d.num_kv_heads * d.head_dim * 2;
-  const int64_t cache_bytes = row_bytes * P * d.shard_cap;
-  if (overlaps(k_cache, cache_bytes, v_cache, cache_bytes))
-    return fail(RA_ERR_INVALID_ARG, "k_cache and v_cache overlap");
-  struct R { const void* p; int64_t n; };
-  const int64_t out_bytes = (int64_t)d.q_rows * d.num_q_heads * d.head_dim *
-                            (d.out_dtype == RA_DTYPE_FP32 ? 4 : 2);
-  const R others[] = {{q, (int64_t)d.q_rows * d.num_q_heads * d.head_dim * 2},
-                      {k_cur, row_bytes * d.cur_len}, {v_cur, row_bytes * d.cur_len},
-                      {out, out_bytes}, {lse, (int64_t)d.num_q_heads * d.q_rows * 4}};
-  for (const R& r : others)
-    if (overlaps(k_cache, cache_bytes, r.p, r.n) || overlaps(v_cache, cache_bytes, r.p, r.n))
-      return fail(RA_ERR_INVALID_ARG, "a cache tensor overlaps q, k_cur, v_cur, out or lse");
-  const FusedWrite w{k_cache, v_cache, n_tokens};
-  return prefill_regions(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
-                         RA_REGION_CACHE | RA_REGION_CURRENT, out, lse, dims, stream, 1, &w);
+  return prefill_write_impl(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout, 1,
+                            nullptr, 0, n_tokens, out, lse, dims, stream);
+}
+
+int ring_attn_prefill_split_write(const void* q, void* k_cache, void* v_cache, const void* k_cur,
+                                  const void* v_cur, int64_t cache_len, int32_t P,
+                                  ra_stripe_layout_t stripe_layout, int32_t splits,
+                                  void* workspace, int64_t workspace_bytes, int32_t n_tokens,
+                                  void* out, float* lse, const ra_dims_t* dims, void* stream) {
+  return prefill_write_impl(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
+                            splits, workspace, workspace_bytes, n_tokens, out, lse, dims, stream);
 }
 
 int ring_attn_partial(const void* q, const void* k_cache, const void* v_cache, const void* k_cur,
@@ -418,52 +494,8 @@ int ring_attn_prefill_split(const void* q, const void* k_cache, const void* v_ca
                             ra_stripe_layout_t stripe_layout, int32_t splits, void* workspace,
                             int64_t workspace_bytes, void* out, float* lse,
                             const ra_dims_t* dims, void* stream) {
-  int64_t need = 0;
-  if (int rc = ra_split_workspace_bytes(dims, splits, &need)) return rc;
-  if (splits == 1)
-    return ring_attn_prefill(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
-                             out, lse, dims, stream);
-  const ra_dims_t& d = *dims;
-  if (!workspace) return fail(RA_ERR_INVALID_ARG, "workspace must not be NULL when splits > 1");
-  if (!aligned16(workspace))
-    return fail(RA_ERR_INVALID_ARG, "every tensor pointer must be 16-byte aligned");
-  if (workspace_bytes < need)
-    return fail(RA_ERR_INVALID_ARG, "workspace_bytes %lld is below the %lld bytes splits=%d needs",
-                (long long)workspace_bytes, (long long)need, splits);
-  // the workspace must not overlap the caller's tensors
-  const int64_t C = d.q_rows, NQ = d.num_q_heads, HD = d.head_dim, NKV = d.num_kv_heads;
-  struct R { const void* p; int64_t n; };
-  const R others[] = {{q, C * NQ * HD * 2}, {k_cache, cache_len > 0 ? (int64_t)P * d.shard_cap * NKV * HD * 2 : 0},
-                      {v_cache, cache_len > 0 ? (int64_t)P * d.shard_cap * NKV * HD * 2 : 0},
-                      {k_cur, (int64_t)d.cur_len * NKV * HD * 2}, {v_cur, (int64_t)d.cur_len * NKV * HD * 2},
-                      {out, C * NQ * HD * (d.out_dtype == RA_DTYPE_FP32 ? 4 : 2)}, {lse, NQ * C * 4}};
-  for (const R& r : others)
-    if (overlaps(workspace, need, r.p, r.n))
-      return fail(RA_ERR_INVALID_ARG, "workspace overlaps another tensor");
-  char* ws = static_cast<char*>(workspace);
-  float* part_lse = reinterpret_cast<float*>(ws + split_part_bytes(d, splits));
-  if (int rc = prefill_regions(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout,
-                               RA_REGION_CACHE | RA_REGION_CURRENT, ws, part_lse, dims, stream,
-                               splits))
-    return rc;
-  if (d.real_rows == 0) return RA_OK;
-  if (!out) return fail(RA_ERR_INVALID_ARG, "out must not be NULL");
-  ra::MergeSplitsParams m{};
-  m.part_o = ws;
-  m.part_lse = part_lse;
-  m.out = out;
-  m.lse = lse;
-  m.splits = splits;
-  m.q_rows = d.q_rows;
-  m.real_rows = d.real_rows;
-  m.nq = d.num_q_heads;
-  m.hd = d.head_dim;
-  m.parts_f32 = 1;
-  m.out_f32 = d.out_dtype == RA_DTYPE_FP32;
-  hipError_t e = ra::launch_merge_splits(m, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess)
-    return fail(RA_ERR_HIP, "split merge launch failed: %s", hipGetErrorString(e));
-  return RA_OK;
+  return split_impl(q, k_cache, v_cache, k_cur, v_cur, cache_len, P, stripe_layout, splits,
+                    workspace, workspace_bytes, out, lse, dims, stream, nullptr);
 }
 
 }  // extern "C"

@@ -182,6 +182,22 @@ int ring_attn_prefill_split(const void* q, const void* k_cache, const void* v_ca
                             void* workspace, int64_t workspace_bytes, void* out, float* lse,
                             const ra_dims_t* dims, void* stream);
 
+/*
+ * ring_attn_prefill_split_write -- ring_attn_prefill_split with the
+ * strided cache write of ring_attn_prefill_write in the same launch (the
+ * split walk's segments share the copy of the chunk's tokens); the merge
+ * follows as its own launch.  Arguments: those of ring_attn_prefill_split,
+ * the caches writable, plus n_tokens as in ring_attn_prefill_write, whose
+ * checks also apply (the workspace must not overlap the caches either).
+ * splits == 1 is ring_attn_prefill_write.  Result: that of kv_cache_write
+ * followed by ring_attn_prefill_split, bit for bit.
+ */
+int ring_attn_prefill_split_write(const void* q, void* k_cache, void* v_cache, const void* k_cur,
+                                  const void* v_cur, int64_t cache_len, int32_t P,
+                                  ra_stripe_layout_t stripe_layout, int32_t splits,
+                                  void* workspace, int64_t workspace_bytes, int32_t n_tokens,
+                                  void* out, float* lse, const ra_dims_t* dims, void* stream);
+
 /* Bytes of the workspace ring_attn_prefill_split_noalloc keeps in the
  * library's own device memory (one copy per GPU, held until the process
  * ends): 72 MiB, e.g. splits = 4 over a 512-row rank share at NQ = 32,

@@ -257,6 +257,22 @@ def test_prefill_write_rejects_bad_arguments(kw, code, msg):
     assert msg in ra.lib().ra_last_error().decode()
 
 
+def test_split_write_checks_the_write_and_the_workspace():
+    d = dims()
+    q, kc, vc, kcur, vcur = FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000, FAKE + 0x4000000
+    need = ra.ra_split_workspace_bytes(d, 4)
+    L = ra.lib()
+
+    def call(n=128, ws=FAKE + 0x9000000, nbytes=need):
+        return L.ring_attn_prefill_split_write(q, kc, vc, kcur, vcur, 512, 2, ra.StripeLayout(1, 0),
+                                               4, ws, nbytes, n, FAKE + 0x8000000, None,
+                                               ctypes.byref(d), None)
+    assert call(n=129) == 1 and "n_tokens" in L.ra_last_error().decode()
+    assert call(ws=kc) == 1 and "workspace overlaps" in L.ra_last_error().decode()
+    assert call(nbytes=need - 16) == 1 and "workspace_bytes" in L.ra_last_error().decode()
+    assert call(ws=0) == 1 and "workspace must not be NULL" in L.ra_last_error().decode()
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ra, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(ra, "_lib", None)

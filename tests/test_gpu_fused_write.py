@@ -108,3 +108,54 @@ def test_fused_write_without_real_rows_still_writes():
                                                bits(case.t["v_cur"]), n, w.cache_len, w.P,
                                                w.interleave)
     assert np.array_equal(bits(kc), kc_ref) and np.array_equal(bits(vc), vc_ref)
+
+
+def split_run(case, n_tokens, splits, fused):
+    """The split walk with the write inside its launch (fused) or as its own
+    launch before it, on fresh device copies."""
+    w = case.w
+    case.to_device()
+    d = case.d
+    C, NQ, HD = w.q_rows, w.nq, w.hd
+    out = torch.full((C, NQ, HD), SENTINEL, device="cuda", dtype=torch.bfloat16)
+    lse = torch.full((NQ, C), SENTINEL, device="cuda", dtype=torch.float32)
+    dims = ra.make_dims(d["q"], d["k_cur"], w.shard_cap, real_rows=w.real_rows,
+                        head_rows=w.head_rows, scale=w.scale, head_pos=w.head_pos,
+                        tail_pos=w.tail_start)
+    layout = ra.StripeLayout(w.interleave, 0)
+    ws = torch.empty(ra.ra_split_workspace_bytes(dims, splits), dtype=torch.uint8, device="cuda")
+    print(f"[gpu] split {'write' if fused else 'then prefill'} {w.name} splits={splits} "
+          f"n_tokens={n_tokens}", flush=True)
+    if fused:
+        ra.ring_attn_prefill_split_write(d["q"], d["k_cache"], d["v_cache"], d["k_cur"],
+                                         d["v_cur"], w.cache_len, w.P, layout, splits, ws,
+                                         n_tokens, out, lse, dims)
+    else:
+        ra.kv_cache_write(d["k_cur"], d["v_cur"], n_tokens, d["k_cache"], d["v_cache"],
+                          w.cache_len, w.P, layout, dims)
+        ra.ring_attn_prefill_split(d["q"], d["k_cache"], d["v_cache"], d["k_cur"], d["v_cur"],
+                                   w.cache_len, w.P, layout, splits, ws, out, lse, dims)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu(), d["k_cache"].cpu(), d["v_cache"].cpu()
+
+
+SPLIT_CASES = [
+    (workloads.CONFIGS["32k_rank3of8"], 4),
+    (small("w-split", nq=8, nkv=2, hd=256, cache_len=700, P=3, real_rows=180, interleave=4), 3),
+    (workloads.CONFIGS["tiny"], 16),
+]
+
+
+@pytest.mark.parametrize("w,splits", SPLIT_CASES, ids=[f"{w.name}-s{s}" for w, s in SPLIT_CASES])
+def test_split_write_matches_write_then_split(w, splits):
+    n_tokens = w.n_cur_real
+    case = Case(w)
+    out, lse, kc, vc = split_run(case, n_tokens, splits, fused=True)
+    out2, lse2, _, _ = split_run(case, n_tokens, splits, fused=False)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+    kc_ref, vc_ref = oracle.kv_cache_write_ref(bits(case.kc), bits(case.vc), bits(case.t["k_cur"]),
+                                               bits(case.t["v_cur"]), n_tokens, w.cache_len, w.P,
+                                               w.interleave)
+    assert np.array_equal(bits(kc), kc_ref) and np.array_equal(bits(vc), vc_ref)
+    compare(case, out, lse, sample_rows(w, 8, seed=w.seed + 11), TOL_BF16)
