@@ -1,0 +1,85 @@
+"""Seeded random configurations on the GPU against the oracle, every real
+row: head dims, GQA groups, shard counts, stripe units, first shards, cache
+lengths (none, short, unaligned), head/tail pieces at arbitrary chunk
+positions, pad rows, pad current tokens, split counts and both output
+dtypes, drawn together so that combinations the hand-written cases do not
+name are covered too."""
+import numpy as np
+import pytest
+import torch
+
+import context_causal_attention_ring_amd as ra
+import oracle
+import workloads
+from helpers import Case
+from test_gpu_parity import (SENTINEL, TOL_BF16, TOL_F32, check_pads_untouched, compare,
+                             run_split)
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 24
+
+
+def draw(i):
+    """Configuration i, a pure function of i (numpy's seeded generator)."""
+    g = np.random.default_rng(1000 + i)
+    hd = int(g.choice([64, 128, 256]))
+    nkv = int(g.choice([1, 2, 3, 4]))
+    group = int(g.choice([1, 2, 3, 4, 8, 16]))
+    while nkv * group > 16:
+        group //= 2
+    P = int(g.integers(1, 10))
+    interleave = int(g.choice([1, 1, 1, 2, 7, 16]))
+    cache_len = 0 if g.random() < 0.2 else int(g.integers(1, 2500))
+    head_rows = int(g.integers(0, 120))
+    tail_rows = int(g.integers(0 if head_rows else 1, 120))
+    head_pos = int(g.integers(0, 200))
+    tail_pos = head_pos + head_rows + int(g.integers(0, 200))
+    q_rows = head_rows + tail_rows
+    # pads only at the end of the rows: a partly real tail needs a full head
+    real_rows = int(g.integers(0, q_rows + 1)) if g.random() < 0.5 else q_rows
+    if real_rows > head_rows:
+        real_rows = max(real_rows, head_rows)
+    last = -1
+    if real_rows:
+        last = head_pos + min(real_rows, head_rows) - 1 if head_rows else -1
+        if real_rows > head_rows:
+            last = max(last, tail_pos + real_rows - head_rows - 1)
+    cur_len = max(last + 1, 1) + int(g.integers(0, 40))
+    cur_real = max(last + 1, 0) + int(g.integers(0, cur_len - max(last + 1, 0) + 1))
+    cap = max(oracle.shard_lengths(cache_len, P, interleave) + [1])
+    w = workloads.custom(f"rand{i}", seed=2000 + i, nq=nkv * group, nkv=nkv, hd=hd,
+                         cache_len=cache_len, P=P, head_rows=head_rows, tail_rows=tail_rows,
+                         real_rows=real_rows, shard_cap=cap, interleave=interleave,
+                         head_pos=head_pos, tail_pos=tail_pos, cur_len=cur_len,
+                         cur_real=cur_real)
+    splits = int(g.choice([1, 1, 1, 2, 3, 5]))
+    fp32 = bool(g.random() < 0.3)
+    ring_start = int(g.integers(0, P))
+    return w, splits, fp32, ring_start
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_configuration_matches_oracle(i):
+    w, splits, fp32, ring_start = draw(i)
+    print(f"[gpu] random config {i}: NQ={w.nq} NKV={w.nkv} HD={w.hd} L={w.cache_len} P={w.P} "
+          f"I={w.interleave} start={ring_start} head={w.head_rows}@{w.head_pos} "
+          f"tail={w.tail_rows}@{w.tail_start} real={w.real_rows} cur={w.n_cur}/{w.n_cur_real} "
+          f"splits={splits} fp32={fp32}", flush=True)
+    case = Case(w).to_device()
+    out, lse = run_split(case, splits, out_fp32=fp32, ring_start=ring_start)
+    if w.real_rows:
+        compare(case, out, lse, list(range(w.real_rows)), TOL_F32 if fp32 else TOL_BF16)
+    check_pads_untouched(case, out, lse)
+
+
+def test_random_configurations_are_varied():
+    """The draw covers what it claims (a check of the generator, on the CPU
+    side of the same file)."""
+    ws = [draw(i) for i in range(N_CASES)]
+    assert {w.hd for w, *_ in ws} == {64, 128, 256}
+    assert any(w.cache_len == 0 for w, *_ in ws) and any(w.cache_len % 32 for w, *_ in ws)
+    assert any(s > 1 for _, s, _, _ in ws) and any(f for _, _, f, _ in ws)
+    assert any(w.real_rows < w.q_rows for w, *_ in ws)
+    assert any(w.interleave > 1 for w, *_ in ws) and any(r > 0 for *_, r in ws)
+    assert any(w.n_cur_real < w.n_cur for w, *_ in ws)
