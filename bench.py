@@ -51,7 +51,7 @@ def alg_bytes(w, with_write):
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "ring_attn_fused_32k_hbm_traffic.md")
 FUSED_SOURCES = [os.path.join(ROOT, "context_causal_attention_ring_amd", "csrc", f)
-                 for f in ("ring_attn_fused.hip", "tile_hd256.inc")]
+                 for f in ("ring_attn_fused.hip", "tile_hd256.inc", "tile_hd128.inc")]
 
 
 def peak_sclk_mhz():
@@ -172,6 +172,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="32k", help="workload name (default: 32k)")
+    ap.add_argument("--head-dim", type=int, default=0, choices=(0, 64, 128, 256),
+                    help="run the workload's shape at this head dim (0: the workload's own)")
     ap.add_argument("--splits", type=int, default=0,
                     help="cut each row's key walk into this many segments (partials merged by "
                          "LSE); 0 (default): the library's suggestion for this GPU")
@@ -228,7 +230,8 @@ def main():
         return 0
 
     w = workloads.CONFIGS[args.config]
-    with_write = True
+    if args.head_dim and args.head_dim != w.hd:
+        w = workloads.with_fields(w, name=f"{w.name}_hd{args.head_dim}", hd=args.head_dim)
     t, d, layout, dims = setup(w, dev, args.out_fp32)
     stream = torch.cuda.current_stream()
     if args.splits == 0:
@@ -356,7 +359,7 @@ def main():
         "ms_per_step_cold_median": round(sorted(cold)[len(cold) // 2], 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "ring_attn_fused_kernel<256>",
+                     "traffic": traffic, "kernel": f"ring_attn_fused_kernel<{w.hd}>",
                      "kernel_ms_avg": round(kern_ms_avg, 4),
                      "kernel_ms_median": round(kern_ms_median, 4),
                      "kernel_ms_min": round(kern_sorted[0], 4)},

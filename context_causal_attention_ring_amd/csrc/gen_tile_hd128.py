@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Writes tile_hd128.inc: the instruction block of one step of the fused
+ring + current attention kernel at HD = 128 with bf16 output (a wave owns
+two 32-row blocks; the accumulator O^T is 2 x 4 tiles of 32 x 32 fp32 in
+AGPRs).
+
+A 32-key tile at HD = 128 takes 32 MFMAs per wave (16 for S^T = K Q^T, 16
+for O^T += V^T P^T), half as many as at HD = 256, while its online softmax
+is the same 32 scores per lane.  Hidden behind the P.V MFMAs alone, as the
+HD = 256 block does, the softmax would need about twice the VALU issue
+slots those MFMAs leave.  So the block works on three tiles at once: block
+u computes the scores of tile u, the softmax of tile u-1 and the P.V of
+tile u-2, and spreads the softmax over all 32 MFMAs (the same softmax work
+per MFMA as the HD = 256 block's P.V half).  The scores live in two
+buffers by tile parity, and the common softmax writes its exponentials to
+temporaries, so tile u-1's raw scores are still there for its slow path:
+no second S^T = K Q^T is needed.
+
+Tiles run in pairs (K and V slots t mod 4).  Block u (E = u mod 2):
+  1. 16 MFMAs S^T = K Q^T of tile u into score buffer E.  The first two K
+     operands were read into KPRE ahead, the others are read from LDS two
+     k-steps ahead.  One LDS-DMA copy per two k-steps: the wave's rows of K
+     tile u + 2 and of V tile u (two instructions each).
+  2. 16 MFMAs O^T += V^T P^T of tile u-2 (probability buffer E).  The even
+     block reads the odd tile's KPRE here.
+  Behind every one of the 32 MFMAs goes an even share (by issue cost) of
+  tile u-1's common-case softmax: scores of buffer 1 - E against the
+  running max as it stands, exponentials into temporaries, the row sums and
+  their compensated fold, the bf16 probabilities into buffer 1 - E, and a
+  test of each lane's tile sum against its bound.  The scalar key bound of
+  tile u and the walkers' step to the next tile share the same shadow.
+  3. When a lane's tile sum passed its bound: if some probability may exceed
+     2^tau, the full softmax (running-max vote, rescale factors, exact new
+     max where voted) on tile u-1's intact scores; either way the tile is
+     significant (its bf16-rounded minus fp32 row sums go to dq, the bound
+     rises).
+  4. When tile u is cut by a key bound: its scores at or past each row's
+     bound become -inf (the next block's softmax reads them).
+  5. Odd u (the end of the pair): wait for this wave's copies, meet the
+     other waves at the pair's barrier, read the next tile's KPRE and leave
+     it in flight.
+
+The walk runs two blocks more than it has tiles (their scores are masked),
+so the last tile's P.V comes out of the final block.
+
+Usage: python gen_tile_hd128.py            (rewrites the .inc)
+       python gen_tile_hd128.py --check    (exit 1 if the .inc is stale)
+"""
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+import gen_tile_hd256 as base  # noqa: E402  (softmax, bound, walker and hazard helpers)
+
+OUT = os.path.join(HERE, "tile_hd128.inc")
+
+NKS = 8            # 16-wide k-steps of QK^T (HD / 16)
+NDB = 4            # 32-wide d blocks of the output (HD / 32)
+NPS = 2            # 16-key steps of P.V per 32-key tile
+NT = NPS * NDB     # P.V steps; each issues one MFMA per row block
+NRB = base.NRB     # 32-row blocks per wave
+NM = 2 * NRB * NKS  # MFMAs per block (QK^T and P.V alike: NKS = NT)
+Q0 = 44            # Q^T operands (pinned): row block rb, k-step k -> v[Q0 + 32 rb + 4 k : +3]
+S0 = (108, 140)    # score buffers (pinned): buffer b, row block rb, key slot i -> v[S0[b] + 16 rb + i]
+T0 = 204           # exponentials (clobbered): row block rb, key slot i -> v[T0 + 4 rb + i % 4]
+PB = base.PB       # bf16 probabilities (pinned), two buffers, as at HD = 256
+KPRE = base.KPRE   # K operands of k-steps 0 and 1 (pinned), read ahead
+RING0 = base.RING0  # operand ring (clobbered)
+KPRE_STEP = 2      # P.V step of an even block after which the next tile's KPRE is read
+ROW_B = 256        # bytes of one K or V row in LDS (HD = 128 bf16)
+
+assert NT == NKS and Q0 + 4 * NKS * NRB <= S0[0] and S0[1] + 32 <= PB[0]
+assert PB[1] + 16 <= T0 and T0 + 4 * NRB <= KPRE
+
+
+def sreg(buf):
+    """Score register of buffer buf as a function (rb, i) -> name."""
+    return lambda rb, i: f"v{S0[buf] + 16 * rb + i}"
+
+
+def treg(rb, i):
+    """Exponential of key slot i of row block rb: four rotating registers
+    per row block (a pair is packed two slots after its second member is
+    written, so slot i's register is free again by slot i + 4)."""
+    return f"v{T0 + 4 * rb + i % 4}"
+
+
+def stile(buf, rb):
+    b = S0[buf] + 16 * rb
+    return f"v[{b}:{b + 15}]"
+
+
+def qop(rb, k):
+    b = Q0 + 4 * NKS * rb + 4 * k
+    return f"v[{b}:{b + 3}]"
+
+
+# K step k uses ring group k % 3 and V step t group (t + NKS) % 3: the
+# first two V operands, read during the last two K steps, go to the groups
+# those steps do not use.
+def kgroup(k):
+    return k % 3
+
+
+def vgroup(t):
+    return (t + NKS) % 3
+
+
+def kread(k):
+    return f"ds_read_b128 {base.grp(kgroup(k))}, %[ka{k}] offset:%[ko]"
+
+
+def kop(k):
+    """K operand of k-step k: the first two were read ahead into KPRE."""
+    return f"%[kp{k}]" if k < 2 else base.grp(kgroup(k))
+
+
+def vreads(t):
+    """Two transposing reads (keys 0-7 and 8-15 of the step) of V operand t."""
+    ks, db = divmod(t, NDB)
+    return [f"ds_read_b64_tr_b16 {base.grp(vgroup(t), h)}, %[va{db}] offset:%[vo{ks}{h}]"
+            for h in (0, 1)]
+
+
+def dma_setup(i):
+    """M0 (the LDS destination) and the scalar offset of copy i, set right
+    after copy i - 1 went out (LDS-DMA reads M0 when issued, and needs one
+    wait state after an SALU write of M0, which the k-steps in between
+    give).  Copies 0, 1 move rows of the K tile, 2, 3 rows of the V tile.
+    Copy b of wave w moves rows 4 w + 16 b .. + 3 (a KiB).  Rows 16 apart
+    share their swizzle, so one precomputed lane offset (%[dk] / %[dv])
+    serves both; the 16 rows of b = 1 go into the scalar offset next to
+    the tile's first byte."""
+    kind, b = ("k", i) if i < 2 else ("v", i - 2)
+    out = [f"s_add_u32 m0, %[m0b], %[m{kind}{b}]"]
+    if b:
+        out.append(f"s_add_u32 %[st], %[off{kind}], %[rs16]")
+    return out
+
+
+def dma_issue(i):
+    """Copy i (see dma_setup): 16 bytes per lane into LDS at M0."""
+    kind, b = ("k", i) if i < 2 else ("v", i - 2)
+    soff = "%[st]" if b else f"%[off{kind}]"
+    return [f"buffer_load_dwordx4 %[d{kind}], %[desc{kind}], {soff} offen lds"]
+
+
+def softmax_common(sr, pout):
+    """Tile u-1's common-case softmax (see base.softmax_ops_stale) on score
+    buffer sr, exponentials into the temporaries.  Its scores are a block
+    old, so the wait for score MFMAs the HD = 256 list opens with is
+    dropped."""
+    ops = base.softmax_ops_stale(pout, src=sreg(sr), dst=treg)
+    assert ops[0] == ("nop", "s_nop 4")
+    return ops[1:]
+
+
+def block(E):
+    """Block u with u mod 2 = E."""
+    sw, sr = E, 1 - E    # scores written (tile u) / read by the softmax (tile u-1)
+    pin, pout = E, 1 - E  # probabilities read by P.V (tile u-2) / written (tile u-1)
+    even = E == 0
+    gaps, per = base.assign(softmax_common(sr, pout), NM)
+    # scalar groups: the key bound of tile u, then the walkers' step; each
+    # group keeps its compares next to the selects that read SCC
+    bound = base.bound_ops()
+    nbound = 0
+    out = ["s_nop 1", "s_waitcnt lgkmcnt(0)"] + dma_setup(0)
+    pending = []  # LDS reads in flight, in issue order
+    m = 0
+    for k in range(NKS):
+        if k >= 2:  # this step's K operand (read two steps ahead) must be in
+            out.append(f"s_waitcnt lgkmcnt({len(pending) - 1 - pending.index(k)})")
+            pending = pending[pending.index(k) + 1:]
+        for rb in range(NRB):
+            c = "0" if k == 0 else stile(sw, rb)
+            out.append(f"v_mfma_f32_32x32x16_bf16 {stile(sw, rb)}, {kop(k)}, {qop(rb, k)}, {c}")
+            if rb == 0:  # LDS reads go out right behind an MFMA (see base.READ_NOTE)
+                if k + 2 < NKS:
+                    out.append(kread(k + 2))
+                    pending.append(k + 2)
+                else:
+                    out += vreads(k + 2 - NKS)
+                    pending += ["v", "v"]
+            out += gaps[m]
+            m += 1
+        if k % 2 == 1:  # one copy of the next tiles per two k-steps
+            out += dma_issue(k // 2)
+            out += base.copy_step_ops() if k == NKS - 1 else dma_setup(k // 2 + 1)
+        elif nbound < len(bound):
+            out += bound[nbound]
+            nbound += 1
+    for t in range(NT):
+        ks, db = divmod(t, NDB)
+        wait = 2 if t + 1 < NT else 0
+        if even and t == KPRE_STEP + 1:  # the KPRE reads went out before step t+1's V reads
+            wait = 4
+        out.append(f"s_waitcnt lgkmcnt({wait})")
+        for rb in range(NRB):
+            out.append(f"v_mfma_f32_32x32x16_bf16 %[acc{rb}{db}], {base.grp(vgroup(t))}, "
+                       f"{base.pbop(pin, rb, ks)}, %[acc{rb}{db}]")
+            if rb == 0:
+                if even and t == KPRE_STEP:
+                    out += base.kpre_reads()
+                if t + 2 < NT:
+                    out += vreads(t + 2)
+            out += gaps[m]
+            m += 1
+        if t % 2 == 0 and nbound < len(bound):
+            out += bound[nbound]
+            nbound += 1
+    assert m == NM and nbound == len(bound)
+    tail = [] if even else ["s_waitcnt vmcnt(0)", "s_barrier"] + base.kpre_reads()
+    # Common path: no lane's tile sum passed its bound and tile u is not cut.
+    out += ["s_cmp_lg_u64 %[any], 0", "s_cbranch_scc1 8f", "10:",
+            "s_cmp_lg_u32 %[mflag], 0", "s_cbranch_scc1 7f", "11:"] + tail + ["s_branch 9f"]
+    # tile u cut by a key bound: mask its scores, for the next block
+    out += ["7:"] + base.mask_body(sreg(sw)) + ["s_branch 11b"]
+    # Some lane's tile sum passed its bound: if some probability may
+    # exceed 2^tau, the full softmax on the intact scores (5); either way
+    # the tile is significant.  Then back to the mask test.
+    out += ["8:"] + [f"v_cmp_gt_f32_e64 %[c{rb}], %[r{rb}], %[pbnd]" for rb in range(NRB)]
+    out += ["s_nop 1", "s_or_b64 %[any], %[c0], %[c1]", "s_cmp_lg_u64 %[any], 0",
+            "s_cbranch_scc1 5f"]
+    out += base.sig_ops(pout) + ["s_branch 10b"]
+    out += ["5:"] + [text for _, text in base.softmax_ops(pout, src=sreg(sr))]
+    out += [f"v_mul_f32 %[dq{rb}], %[dq{rb}], %[al{rb}]" for rb in range(NRB)]
+    out += base.sig_ops(pout) + ["s_branch 10b", "9:"]
+    return out, per
+
+
+def offset_operands():
+    """The block's LDS offsets (immediates, from the slot offsets KOFF, VOFF,
+    MK, MV of the asm statement's scope) and the copy lane offsets: K
+    k-step s at ka[s] + ko; V step (ks, db), half h at va[db] + vo<ks><h>
+    (16 rows per ks, 8 rows per h); copy b to the rows 16 b past the wave's
+    first."""
+    ops = ['[ko] "i"(KOFF)']
+    ops += [f'[vo{ks}{h}] "i"(VOFF + {16 * ROW_B * ks + 8 * ROW_B * h})'
+            for ks in range(NPS) for h in (0, 1)]
+    ops += [f'[mk{b}] "i"(MK + {16 * ROW_B * b})' for b in (0, 1)]
+    ops += [f'[mv{b}] "i"(MV + {16 * ROW_B * b})' for b in (0, 1)]
+    ops += ['[dk] "v"(dl.ka)', '[dv] "v"(dl.va)']
+    return ops
+
+
+def render():
+    out = ["// Generated by gen_tile_hd128.py -- edit the generator, not this file.",
+           "// One step of the HD = 128 tile loop (bf16 output): S^T = K Q^T of tile u,",
+           "// the online softmax of tile u-1 and O^T += V^T P^T of tile u-2, the",
+           "// softmax spread over all 32 MFMAs.  Variant E<e> is block u with",
+           "// u mod 2 = e: it writes score buffer e, reads score buffer 1 - e,",
+           "// reads probability buffer e and writes buffer 1 - e.  Operands are",
+           "// bound by the asm statement in ring_attn_fused.hip."]
+    for E in (0, 1):
+        body, per = block(E)
+        out.append(f"// Block E{E}: about {per:.1f} full-rate VALU issue slots of softmax work"
+                   " per MFMA.")
+        base.check_dot_hazards(body)
+        out += base.macro(f"RA_TILE_HD128_E{E}", body)
+    q = [f'[q{rb}_{k}] "{{{qop(rb, k)}}}"(q[{rb}][{k}])' for rb in range(NRB) for k in range(NKS)]
+    out += base.operand_list("RA_TILE_HD128_Q_OPERANDS", q)
+    kp = [f'[kp{k}] "+{{v[{KPRE + 4 * k}:{KPRE + 4 * k + 3}]}}"(kpre[{k}])' for k in range(2)]
+    out += base.operand_list("RA_TILE_HD128_KPRE_OPERANDS", kp)
+    acc = [f'[acc{rb}{db}] "+a"(acc[{rb}][{db}])' for rb in range(NRB) for db in range(NDB)]
+    out += base.operand_list("RA_TILE_HD128_ACC_OPERANDS", acc)
+    out += base.operand_list("RA_TILE_HD128_OFFSET_OPERANDS", offset_operands())
+    # score buffers: the one written (tile u) is an output, the one the
+    # softmax reads (tile u-1) is rewritten by the slow path
+    for buf in (0, 1):
+        regs = [(stile(buf, rb), f"sc[{buf}][{rb}]") for rb in range(NRB)]
+        out += base.operand_list(f"RA_TILE_HD128_S_OUT{buf}", [f'"=&{{{r}}}"({c})' for r, c in regs])
+        out += base.operand_list(f"RA_TILE_HD128_S_RW{buf}", [f'"+{{{r}}}"({c})' for r, c in regs])
+    for buf in (0, 1):
+        regs = [(base.pbop(buf, rb, ks), f"p{buf}[{rb}][{ks}]") for rb in range(NRB)
+                for ks in range(NPS)]
+        out += base.operand_list(f"RA_TILE_HD128_PB_IN{buf}", [f'"{{{r}}}"({c})' for r, c in regs])
+        out += base.operand_list(f"RA_TILE_HD128_PB_OUT{buf}", [f'"=&{{{r}}}"({c})' for r, c in regs])
+    clob = [f'"v{r}"' for r in list(range(T0, T0 + 4 * NRB)) + list(range(RING0, RING0 + 12))]
+    out += base.operand_list("RA_TILE_HD128_CLOBBERS", clob)
+    return "\n".join(out) + "\n"
+
+
+def main():
+    text = render()
+    if "--check" in sys.argv:
+        cur = open(OUT).read() if os.path.exists(OUT) else ""
+        if cur != text:
+            print(f"{OUT} is stale: run {os.path.basename(__file__)}", file=sys.stderr)
+            return 1
+        return 0
+    with open(OUT, "w") as f:
+        f.write(text)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -324,16 +324,17 @@ def pack_f32(rb, j, direct):
             ("valu", f"v_perm_b32 {hi}, %[b0], %[a0], %[psel]")]
 
 
-def mask_part():
-    """Keys at or past the row's bound -> -inf, only when the flag is set.
+def mask_part(src=s):
+    """Keys at or past the row's bound -> -inf, only when the flag is set
+    (src: the score registers, (rb, i) -> name).
     The bound of row block rb is lc (a visit's keys left, lm = 0) or
     pos_rb + lc (current tiles, lm = 1: lc = 1 - first key's position).
     Lane half h holds keys 8 (i / 4) + 4 h + i % 4 of the tile; with lim =
     bound - 4 h, key slot i is kept iff 8 (i / 4) + i % 4 < lim."""
-    return ["s_cmp_eq_u32 %[mflag], 0", "s_cbranch_scc1 1f"] + mask_body() + ["1:"]
+    return ["s_cmp_eq_u32 %[mflag], 0", "s_cbranch_scc1 1f"] + mask_body(src) + ["1:"]
 
 
-def mask_body():
+def mask_body(src=s):
     """mask_part without its test: the per-row bounds, then the compares."""
     out = ["v_mbcnt_lo_u32_b32 %[a0], -1, 0", "v_mbcnt_hi_u32_b32 %[a0], -1, %[a0]",
            "v_lshrrev_b32 %[a0], 5, %[a0]", "v_lshlrev_b32 %[a0], 2, %[a0]",  # 4 h
@@ -347,13 +348,14 @@ def mask_body():
             c = 8 * (i // 4) + i % 4
             out.append(f"v_sub_u32 %[a0], {c}, %[th{rb}]")    # < 0 iff kept
             out.append("v_ashrrev_i32 %[a0], 31, %[a0]")      # all ones iff kept
-            out.append(f"v_bfi_b32 {s(rb, i)}, %[a0], {s(rb, i)}, %[ninf]")
+            out.append(f"v_bfi_b32 {src(rb, i)}, %[a0], {src(rb, i)}, %[ninf]")
     return out
 
 
-def softmax_ops(pout, pack=True):
+def softmax_ops(pout, pack=True, src=s):
     """The online softmax of tile v as (kind, text) in dependency order
-    (pack: the bf16 packing of the probabilities into buffer pout)."""
+    (pack: the bf16 packing of the probabilities into buffer pout; src: the
+    score registers, (rb, i) -> name, overwritten by the probabilities)."""
     ops = [("nop", "s_nop 4")]  # the last score MFMAs' results (after one more MFMA)
     for rb in range(NRB):  # threshold for the lazy rescale: mlog + tau
         ops.append(("valu", f"v_add_f32 %[th{rb}], %[tau], %[ml{rb}]"))
@@ -364,10 +366,10 @@ def softmax_ops(pout, pack=True):
             for name, c in (("a", ca), ("b", cb)):
                 if c is None:
                     continue
-                src = [s(rb, i) for i in c]
+                regs = [src(rb, i) for i in c]
                 if len(c) == 2:
-                    src = [f"%[{name}{rb}]"] + src
-                ops.append(("valu", f"v_max3_f32 %[{name}{rb}], {', '.join(src)}"))
+                    regs = [f"%[{name}{rb}]"] + regs
+                ops.append(("valu", f"v_max3_f32 %[{name}{rb}], {', '.join(regs)}"))
     # The two halves of a row live in lanes l and l ^ 32: the in-lane max
     # goes into both swap operands, the halves are exchanged, max taken.
     for rb in range(NRB):
@@ -416,23 +418,23 @@ def softmax_ops(pout, pack=True):
     for rb in range(NRB):
         st = []
         for i in range(16):
-            st.append(("valu", f"v_fma_f32 {s(rb, i)}, {s(rb, i)}, %[c2], -%[a{rb}]"))
+            st.append(("valu", f"v_fma_f32 {src(rb, i)}, {src(rb, i)}, %[c2], -%[a{rb}]"))
             if i == 2:
-                st.append(("valu", f"v_add_f32 %[r{rb}], {s(rb, 0)}, {s(rb, 1)}"))
+                st.append(("valu", f"v_add_f32 %[r{rb}], {src(rb, 0)}, {src(rb, 1)}"))
             elif i > 2:
-                st.append(("valu", f"v_add_f32 %[r{rb}], %[r{rb}], {s(rb, i - 1)}"))
+                st.append(("valu", f"v_add_f32 %[r{rb}], %[r{rb}], {src(rb, i - 1)}"))
             if pack and i >= 2 and i % 2 == 0:
                 j = i // 2 - 1
-                st.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, j)}, {s(rb, 2 * j)}, "
-                                   f"{s(rb, 2 * j + 1)}"))
-            st.append(("trans", f"v_exp_f32 {s(rb, i)}, {s(rb, i)}"))
+                st.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, j)}, {src(rb, 2 * j)}, "
+                                   f"{src(rb, 2 * j + 1)}"))
+            st.append(("trans", f"v_exp_f32 {src(rb, i)}, {src(rb, i)}"))
         streams.append(st)
     for k in range(max(len(x) for x in streams)):
         for st in streams:
             if k < len(st):
                 ops.append(st[k])
     for rb in range(NRB):
-        ops.append(("valu", f"v_add_f32 %[r{rb}], %[r{rb}], {s(rb, 15)}"))
+        ops.append(("valu", f"v_add_f32 %[r{rb}], %[r{rb}], {src(rb, 15)}"))
     # l = l * alpha + r, compensated (Kahan): lk keeps what the rounding of
     # each fold dropped, so millions of tiny tile sums do not drift.  The
     # sums are read from li / lki and written to lo / lko (two register
@@ -450,12 +452,12 @@ def softmax_ops(pout, pack=True):
         ops.append(("valu", f"v_sub_f32 %[lko{rb}], %[lko{rb}], %[b{rb}]"))
     if pack:
         for rb in range(NRB):
-            ops.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, 7)}, {s(rb, 14)}, "
-                                f"{s(rb, 15)}"))
+            ops.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, 7)}, {src(rb, 14)}, "
+                                f"{src(rb, 15)}"))
     return ops
 
 
-def softmax_ops_stale(pout):
+def softmax_ops_stale(pout, src=s, dst=s):
     """The common case of tile v's online softmax (bf16 output): every score
     is taken against the running max as it stands (it starts at -FLT_MAX,
     so a row that has seen no key gets +inf probabilities and the slow
@@ -463,22 +465,24 @@ def softmax_ops_stale(pout):
     and lo = li + r compensated (alpha = 1).  Valid while every
     probability is at most 2^tau, which r <= 2^tau (pbnd) proves: otherwise
     (a row's max grew by more than tau, or the first tile) the block's
-    slow path recomputes the tile with softmax_ops, from li as it was."""
+    slow path recomputes the tile with softmax_ops, from li as it was.
+    src holds the scores, dst gets the probabilities ((rb, i) -> name); with
+    dst = src they replace the scores."""
     ops = [("nop", "s_nop 4"), ("salu", "s_mov_b32 %[resc], 0")]
     streams = []
     for rb in range(NRB):
         st = []
         for i in range(16):
-            st.append(("valu", f"v_fma_f32 {s(rb, i)}, {s(rb, i)}, %[c2], -%[ml{rb}]"))
+            st.append(("valu", f"v_fma_f32 {dst(rb, i)}, {src(rb, i)}, %[c2], -%[ml{rb}]"))
             if i == 2:
-                st.append(("valu", f"v_add_f32 %[r{rb}], {s(rb, 0)}, {s(rb, 1)}"))
+                st.append(("valu", f"v_add_f32 %[r{rb}], {dst(rb, 0)}, {dst(rb, 1)}"))
             elif i > 2:
-                st.append(("valu", f"v_add_f32 %[r{rb}], %[r{rb}], {s(rb, i - 1)}"))
+                st.append(("valu", f"v_add_f32 %[r{rb}], %[r{rb}], {dst(rb, i - 1)}"))
             if i >= 2 and i % 2 == 0:
                 j = i // 2 - 1
-                st.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, j)}, {s(rb, 2 * j)}, "
-                                   f"{s(rb, 2 * j + 1)}"))
-            st.append(("trans", f"v_exp_f32 {s(rb, i)}, {s(rb, i)}"))
+                st.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, j)}, {dst(rb, 2 * j)}, "
+                                   f"{dst(rb, 2 * j + 1)}"))
+            st.append(("trans", f"v_exp_f32 {dst(rb, i)}, {dst(rb, i)}"))
         streams.append(st)
     main = []
     for k in range(max(len(x) for x in streams)):
@@ -487,7 +491,7 @@ def softmax_ops_stale(pout):
                 main.append(st[k])
     ops += main
     for rb in range(NRB):
-        ops.append(("valu", f"v_add_f32 %[r{rb}], %[r{rb}], {s(rb, 15)}"))
+        ops.append(("valu", f"v_add_f32 %[r{rb}], %[r{rb}], {dst(rb, 15)}"))
     for rb in range(NRB):  # y = r - lki; lo = li + y; lko = (lo - li) - y
         ops.append(("valu", f"v_sub_f32 %[a{rb}], %[r{rb}], %[lki{rb}]"))
     for rb in range(NRB):
@@ -497,7 +501,7 @@ def softmax_ops_stale(pout):
     for rb in range(NRB):
         ops.append(("valu", f"v_sub_f32 %[lko{rb}], %[lko{rb}], %[a{rb}]"))
     for rb in range(NRB):
-        ops.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, 7)}, {s(rb, 14)}, {s(rb, 15)}"))
+        ops.append(("valu", f"v_cvt_pk_bf16_f32 {pbreg(pout, rb, 7)}, {dst(rb, 14)}, {dst(rb, 15)}"))
     # some probability of the lane may exceed 2^tau, or the tile is
     # significant: bnd <= 2^tau (see sig_ops)
     for rb in range(NRB):
@@ -649,6 +653,24 @@ def operand_list(name, items):
     return out
 
 
+ROW_B = 512  # bytes of one K or V row in LDS (HD = 256 bf16)
+
+
+def offset_operands():
+    """The block's LDS offsets (immediates, from the slot offsets KOFF, VOFF,
+    MK, MV of the asm statement's scope) and the copy lane offsets: K
+    k-step s at ka[s % 8] + ko<s / 8>; V step (ks, db), half h at va[db %
+    4] + vo<ks><db / 4><h> (16 rows per ks, 8 rows per h, d blocks 4..7 at
+    +256); copy j = 2 a + b to the rows 8 a + 16 b past the wave's first."""
+    ops = ['[ko0] "i"(KOFF)', '[ko1] "i"(KOFF + 256)']
+    ops += [f'[vo{ks}{hi}{h}] "i"(VOFF + {16 * ROW_B * ks + 256 * hi + 8 * ROW_B * h})'
+            for ks in range(NPS) for hi in (0, 1) for h in (0, 1)]
+    ops += [f'[mk{j}] "i"(MK + {ROW_B * (8 * (j >> 1) + 16 * (j & 1))})' for j in range(4)]
+    ops += [f'[mv{j}] "i"(MV + {ROW_B * (8 * (j >> 1) + 16 * (j & 1))})' for j in range(4)]
+    ops += ['[dka] "v"(dl.ka)', '[dkb] "v"(dl.kb)', '[dva] "v"(dl.va)', '[dvb] "v"(dl.vb)']
+    return ops
+
+
 def render():
     out = ["// Generated by gen_tile_hd256.py -- edit the generator, not this file.",
            "// One 32-key tile at HD = 256: S^T = K Q^T, the optional key-bound mask,",
@@ -677,6 +699,9 @@ def render():
     out += operand_list("RA_TILE_HD256_Q_OPERANDS", q)
     kp = [f'[kp{k}] "+{{v[{KPRE + 4 * k}:{KPRE + 4 * k + 3}]}}"(kpre[{k}])' for k in range(2)]
     out += operand_list("RA_TILE_HD256_KPRE_OPERANDS", kp)
+    acc = [f'[acc{rb}{db}] "+a"(acc[{rb}][{db}])' for rb in range(NRB) for db in range(NDB)]
+    out += operand_list("RA_TILE_HD256_ACC_OPERANDS", acc)
+    out += operand_list("RA_TILE_HD256_OFFSET_OPERANDS", offset_operands())
     # probability buffers: p0 at PB[0], p1 at PB[1].  bf16 output: one is
     # read (the previous tile's), the other written; fp32 output: hi in p0,
     # lo in p1, both read and rewritten.

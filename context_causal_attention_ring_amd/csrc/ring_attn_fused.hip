@@ -217,19 +217,14 @@ __device__ __forceinline__ float wave_max_pair(float x) {
 // whose count reached 0.
 #include "tile_hd256.inc"
 #define RA_TILE_STATE_OPERANDS                                                                  \
-  [acc00] "+a"(acc[0][0]), [acc01] "+a"(acc[0][1]), [acc02] "+a"(acc[0][2]),                   \
-      [acc03] "+a"(acc[0][3]), [acc04] "+a"(acc[0][4]), [acc05] "+a"(acc[0][5]),               \
-      [acc06] "+a"(acc[0][6]), [acc07] "+a"(acc[0][7]), [acc10] "+a"(acc[1][0]),               \
-      [acc11] "+a"(acc[1][1]), [acc12] "+a"(acc[1][2]), [acc13] "+a"(acc[1][3]),               \
-      [acc14] "+a"(acc[1][4]), [acc15] "+a"(acc[1][5]), [acc16] "+a"(acc[1][6]),               \
-      [acc17] "+a"(acc[1][7]), [ml0] "+v"(ml[0]), [ml1] "+v"(ml[1]), [lo0] "=&v"(lo[0]),       \
-      [lo1] "=&v"(lo[1]), [lko0] "=&v"(lko[0]), [lko1] "=&v"(lko[1]), [al0] "=&v"(al[0]),      \
-      [al1] "=&v"(al[1]), [resc] "=&s"(resc), [any] "=&s"(any),                                                    \
-      [a0] "=&v"(a0), [b0] "=&v"(b0), [a1] "=&v"(a1), [b1] "=&v"(b1), [th0] "=&v"(th0),       \
-      [th1] "=&v"(th1), [r0] "=&v"(r0), [r1] "=&v"(r1), [c0] "=&s"(c0), [c1] "=&s"(c1), [v0] "=&s"(v0), [v1] "=&s"(v1),        \
-      [st] "=&s"(st), [mflag] "=&s"(mflag), [lc] "=&s"(lc), [lm] "=&s"(lm), [cr] "=&s"(cr),     \
-      [cc] "=&s"(cc), [offk] "+s"(offk), [offv] "+s"(offv), [wlim] "+s"(wlim), [lb] "+s"(lb), \
-      [lk] "+s"(lk), [lv] "+s"(lv), [tmin] "=&s"(tmin), RA_TILE_HD256_KPRE_OPERANDS
+  [ml0] "+v"(ml[0]), [ml1] "+v"(ml[1]), [lo0] "=&v"(lo[0]), [lo1] "=&v"(lo[1]),                 \
+      [lko0] "=&v"(lko[0]), [lko1] "=&v"(lko[1]), [al0] "=&v"(al[0]), [al1] "=&v"(al[1]),      \
+      [resc] "=&s"(resc), [any] "=&s"(any), [a0] "=&v"(a0), [b0] "=&v"(b0), [a1] "=&v"(a1),    \
+      [b1] "=&v"(b1), [th0] "=&v"(th0), [th1] "=&v"(th1), [r0] "=&v"(r0), [r1] "=&v"(r1),      \
+      [c0] "=&s"(c0), [c1] "=&s"(c1), [v0] "=&s"(v0), [v1] "=&s"(v1), [st] "=&s"(st),          \
+      [mflag] "=&s"(mflag), [lc] "=&s"(lc), [lm] "=&s"(lm), [cr] "=&s"(cr), [cc] "=&s"(cc),     \
+      [offk] "+s"(offk), [offv] "+s"(offv), [wlim] "+s"(wlim), [lb] "+s"(lb), [lk] "+s"(lk),    \
+      [lv] "+s"(lv), [tmin] "=&s"(tmin)
 // bf16 output: the rounded-minus-fp32 sums of the significant tiles, and
 // the tile-sum bound past which a tile is significant
 #define RA_TILE_LQ_OPERANDS                                                                     \
@@ -239,18 +234,10 @@ __device__ __forceinline__ float wave_max_pair(float x) {
       [ka5] "v"(ka[5]), [ka6] "v"(ka[6]), [ka7] "v"(ka[7]), [va0] "v"(va[0]), [va1] "v"(va[1]), \
       [va2] "v"(va[2]), [va3] "v"(va[3]), [c2] "s"(c2), [tau] "s"(tau), [pbnd] "s"(pbnd),       \
       [wk] "s"(wb.k), [li0] "v"(li[0]), [li1] "v"(li[1]), [lki0] "v"(lki[0]),                   \
-      [lki1] "v"(lki[1]),                                                                      \
-      [np] "s"(wb.np), [dlim] "s"(dlim), [wm31] "s"(wb.wm31), [vv] "s"(wb.v), [tt] "s"(wb.t),  \
-      [pos0] "v"(pos[0]), [pos1] "v"(pos[1]), [ninf] "v"(ninf), [ko0] "i"(KOFF),                \
-      [ko1] "i"(KOFF + 256), [vo000] "i"(VOFF), [vo001] "i"(VOFF + 4096),                       \
-      [vo010] "i"(VOFF + 256), [vo011] "i"(VOFF + 256 + 4096), [vo100] "i"(VOFF + 8192),        \
-      [vo101] "i"(VOFF + 8192 + 4096), [vo110] "i"(VOFF + 8192 + 256),                          \
-      [vo111] "i"(VOFF + 8192 + 256 + 4096), [kpo] "i"(KPO), [desck] "s"(desck),                \
-      [descv] "s"(descv), [tstr] "s"(tstr), [m0b] "s"(m0b),                                      \
-      [rs16] "s"(dl.rs16), [dka] "v"(dl.ka), [dkb] "v"(dl.kb), [dva] "v"(dl.va),                \
-      [dvb] "v"(dl.vb), [mk0] "i"(MK), [mk1] "i"(MK + 8192), [mk2] "i"(MK + 4096),              \
-      [mk3] "i"(MK + 12288), [mv0] "i"(MV), [mv1] "i"(MV + 8192), [mv2] "i"(MV + 4096),         \
-      [mv3] "i"(MV + 12288)
+      [lki1] "v"(lki[1]), [np] "s"(wb.np), [dlim] "s"(dlim), [wm31] "s"(wb.wm31),               \
+      [vv] "s"(wb.v), [tt] "s"(wb.t), [pos0] "v"(pos[0]), [pos1] "v"(pos[1]),                   \
+      [ninf] "v"(ninf), [kpo] "i"(KPO), [desck] "s"(desck), [descv] "s"(descv),                 \
+      [tstr] "s"(tstr), [m0b] "s"(m0b), [rs16] "s"(dl.rs16)
 // l <- l * a + r, compensated (Kahan summation): c holds the part of the
 // sum that earlier folds rounded away (negated), and the fold adds it back,
 // so a row sum over millions of keys whose tile sums are tiny against it
@@ -301,28 +288,100 @@ __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], bf16x8 (&p0)[2][
   const uint32_t psel = 0x07060302u;   // v_perm: the upper halves of two words
   if constexpr (PIN == 0 && !F32) {
     asm volatile(RA_TILE_HD256_ASM_P0
-                 : RA_TILE_STATE_OPERANDS, RA_TILE_LQ_OPERANDS, RA_TILE_HD256_PB_OUT1
+                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_ACC_OPERANDS, RA_TILE_HD256_KPRE_OPERANDS,
+                   RA_TILE_LQ_OPERANDS, RA_TILE_HD256_PB_OUT1
                  : RA_TILE_HD256_Q_OPERANDS, RA_TILE_HD256_PB_IN0, RA_TILE_INPUT_OPERANDS,
-                   [one2] "s"(one2)
+                   RA_TILE_HD256_OFFSET_OPERANDS, [one2] "s"(one2)
                  : RA_TILE_HD256_CLOBBERS, "memory", "scc", "m0");
   } else if constexpr (!F32) {
     asm volatile(RA_TILE_HD256_ASM_P1
-                 : RA_TILE_STATE_OPERANDS, RA_TILE_LQ_OPERANDS, RA_TILE_HD256_PB_OUT0
+                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_ACC_OPERANDS, RA_TILE_HD256_KPRE_OPERANDS,
+                   RA_TILE_LQ_OPERANDS, RA_TILE_HD256_PB_OUT0
                  : RA_TILE_HD256_Q_OPERANDS, RA_TILE_HD256_PB_IN1, RA_TILE_INPUT_OPERANDS,
-                   [one2] "s"(one2)
+                   RA_TILE_HD256_OFFSET_OPERANDS, [one2] "s"(one2)
                  : RA_TILE_HD256_CLOBBERS, "memory", "scc", "m0");
   } else if constexpr (PIN == 0) {
     asm volatile(RA_TILE_HD256_F32_P0
-                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_PB_RW0, RA_TILE_HD256_PB_RW1
-                 : RA_TILE_HD256_Q_OPERANDS, RA_TILE_INPUT_OPERANDS, [hmask] "s"(hmask),
+                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_ACC_OPERANDS, RA_TILE_HD256_KPRE_OPERANDS,
+                   RA_TILE_HD256_PB_RW0, RA_TILE_HD256_PB_RW1
+                 : RA_TILE_HD256_Q_OPERANDS, RA_TILE_INPUT_OPERANDS, RA_TILE_HD256_OFFSET_OPERANDS,
+                   [hmask] "s"(hmask),
                    [psel] "s"(psel)
                  : RA_TILE_HD256_CLOBBERS, "memory", "scc", "m0");
   } else {
     asm volatile(RA_TILE_HD256_F32_P1
-                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_PB_RW0, RA_TILE_HD256_PB_RW1
-                 : RA_TILE_HD256_Q_OPERANDS, RA_TILE_INPUT_OPERANDS, [hmask] "s"(hmask),
+                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD256_ACC_OPERANDS, RA_TILE_HD256_KPRE_OPERANDS,
+                   RA_TILE_HD256_PB_RW0, RA_TILE_HD256_PB_RW1
+                 : RA_TILE_HD256_Q_OPERANDS, RA_TILE_INPUT_OPERANDS, RA_TILE_HD256_OFFSET_OPERANDS,
+                   [hmask] "s"(hmask),
                    [psel] "s"(psel)
                  : RA_TILE_HD256_CLOBBERS, "memory", "scc", "m0");
+  }
+#endif
+}
+
+// One step of the HD = 128 tile loop, bf16 output (generated: tile_hd128.inc;
+// this binds its operands).  Block u computes S^T = K Q^T of tile u (K slot
+// at KOFF, first two operands in kpre) into score buffer sc[E], E = u mod 2;
+// runs the online softmax of tile u-1 on sc[1 - E] (its raw scores stay:
+// the exponentials go to temporaries) into probability buffer 1 - E, with
+// the slow path and the significant-tile correction of the HD = 256 block;
+// and accumulates O^T += V^T P^T of tile u-2 (V slot at VOFF, probability
+// buffer E).  The softmax is spread over all 32 MFMAs.  When tile u is cut
+// by a key bound its scores are masked at the end of the block, for the
+// next one.  Copies: the wave's rows of K tile u + 2 (to MK) and V tile u
+// (to MV), two instructions each; copy b of wave w moves rows 4 w + 16 b
+// and the next three, lane offset dl.ka / dl.va, and b = 1 adds dl.rs16 to
+// the scalar offset.  The even block reads tile u + 1's kpre from KPO
+// during its P.V; the odd block ends the pair (copies waited for, barrier)
+// and leaves the next kpre in flight.  The walkers step as in the HD = 256
+// block.  On return ml, lo / lko, al and resc are those of tile u-1's
+// softmax.
+//   ka[j]  LDS address of this lane's K row at chunk (2j + h) ^ swizzle;
+//          k-step s reads ka[s] + KOFF
+//   va[d]  LDS address of this lane's transposed V read for d block d;
+//          step (ks, db) reads va[db] + VOFF + 4096 ks, and + 2048 for keys
+//          8..15
+// Q is pinned to v[44:107], the score buffers to v[108:171], the
+// probability buffers to v[172:203] and kpre to v[236:243]; the
+// exponentials use v[204:211] and the operand ring v[244:255] (clobbered).
+#include "tile_hd128.inc"
+template <uint32_t KOFF, uint32_t VOFF, int E, uint32_t MK, uint32_t MV, uint32_t KPO>
+__device__ __forceinline__ void tile_hd128(f32x16 (&acc)[2][4], f32x16 (&sc)[2][2],
+                                           bf16x8 (&p0)[2][2], bf16x8 (&p1)[2][2],
+                                           const bf16x8 (&q)[2][8], bf16x8 (&kpre)[2],
+                                           const uint32_t (&ka)[8], const uint32_t (&va)[4],
+                                           float (&ml)[2], const float (&li)[2],
+                                           const float (&lki)[2], float (&lo)[2], float (&lko)[2],
+                                           float (&dq)[2], float (&bnd)[2], float (&al)[2],
+                                           uint32_t& resc, float c2, float tau, float pbnd,
+                                           const TileBound& wb, const int (&pos)[2],
+                                           const i32x4& desck, const i32x4& descv,
+                                           uint32_t& offk, uint32_t& offv, int& wlim, int dlim,
+                                           int& lb, int& lk, int& lv, uint32_t tstr,
+                                           uint32_t& tmin, uint32_t m0b, const CopyLanes& dl) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  float a0, b0, a1, b1, th0, th1, r0, r1;
+  uint32_t st, mflag, lc, lm, cr, cc, v0, v1;
+  uint64_t c0, c1, any;
+  const float ninf = kNegInf;
+  const uint32_t one2 = 0x3F803F80u;  // bf16 pair (1, 1): v_dot2 sums a packed pair
+  if constexpr (E == 0) {
+    asm volatile(RA_TILE_HD128_E0
+                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD128_ACC_OPERANDS, RA_TILE_HD128_KPRE_OPERANDS,
+                   RA_TILE_LQ_OPERANDS, RA_TILE_HD128_PB_OUT1, RA_TILE_HD128_S_OUT0,
+                   RA_TILE_HD128_S_RW1
+                 : RA_TILE_HD128_Q_OPERANDS, RA_TILE_HD128_PB_IN0, RA_TILE_INPUT_OPERANDS,
+                   RA_TILE_HD128_OFFSET_OPERANDS, [one2] "s"(one2)
+                 : RA_TILE_HD128_CLOBBERS, "memory", "scc", "m0");
+  } else {
+    asm volatile(RA_TILE_HD128_E1
+                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD128_ACC_OPERANDS, RA_TILE_HD128_KPRE_OPERANDS,
+                   RA_TILE_LQ_OPERANDS, RA_TILE_HD128_PB_OUT0, RA_TILE_HD128_S_OUT1,
+                   RA_TILE_HD128_S_RW0
+                 : RA_TILE_HD128_Q_OPERANDS, RA_TILE_HD128_PB_IN1, RA_TILE_INPUT_OPERANDS,
+                   RA_TILE_HD128_OFFSET_OPERANDS, [one2] "s"(one2)
+                 : RA_TILE_HD128_CLOBBERS, "memory", "scc", "m0");
   }
 #endif
 }
@@ -343,7 +402,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   constexpr uint32_t TILE_B = TILE * 2;   // bytes of one K or V tile
   constexpr int DPW = kBKV * CPR / (64 * kWaves);  // DMA instructions per wave per tile
   static_assert(DPW >= 1 && DPW * 64 * kWaves == kBKV * CPR, "tile must split over the waves");
-  constexpr bool ASM256 = D == 256 && NRB == 2 && NKB == 1;  // hand-scheduled tile body
+  // hand-scheduled tile bodies: HD = 256 (both output types), HD = 128 (bf16
+  // output; fp32 output at HD = 128 runs the compiler-scheduled loop)
+  constexpr bool ASM256 = D == 256 && NRB == 2 && NKB == 1;
+  constexpr bool ASM128 = D == 128 && !F32OUT && NRB == 2 && NKB == 1;
+  constexpr bool ASMBLK = ASM256 || ASM128;
   // LDS: K slots 0..3 then V slots 0..3 (tile t in slot t mod 4).  Slot
   // offsets are compile-time constants because the tile loop is unrolled
   // over the four slots.
@@ -543,22 +606,24 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
             w.off + (uint32_t)R * rowstride);
     }
   };
-  // The copies issued from the HD = 256 tile block split the rows another
-  // way: instruction 2 a + b of wave w moves rows R = 2 w + 8 a + 16 b and
-  // R + 1.  Rows 16 apart share their swizzle, so two lane offsets per
-  // operand (a = 0, 1) carry the swizzle and R's rows for b = 0; the 16 more
-  // rows of b = 1 go into the scalar offset (the sum, which the descriptor
-  // bounds, is the same).
+  // The copies issued from the hand-scheduled tile blocks split the rows
+  // another way.  HD = 256: instruction 2 a + b of wave w moves rows R =
+  // 2 w + 8 a + 16 b and R + 1; HD = 128: instruction b moves rows R = 4 w +
+  // 16 b .. R + 3.  Rows 16 apart share their swizzle, so one lane offset
+  // per operand and a (two at HD = 256) carries the swizzle and R's rows
+  // for b = 0; the 16 more rows of b = 1 go into the scalar offset (the sum,
+  // which the descriptor bounds, is the same).
   CopyLanes dl;
+  const int dl_r0 = (D == 128 ? 4 : 2) * wave;  // the wave's first copied row
   {
-    const int r0 = 2 * wave, r1 = 2 * wave + 8;
+    const int r0 = dl_r0, r1 = D == 128 ? dl_r0 : dl_r0 + 8;
     dl.ka = (dma_kbase ^ (uint32_t)(swz_k(r0, CPR) << 4)) + (uint32_t)r0 * rowstride;
     dl.kb = (dma_kbase ^ (uint32_t)(swz_k(r1, CPR) << 4)) + (uint32_t)r1 * rowstride;
     dl.va = (dma_vbase ^ (uint32_t)(swz_v(r0, CPR) << 4)) + (uint32_t)r0 * rowstride;
     dl.vb = (dma_vbase ^ (uint32_t)(swz_v(r1, CPR) << 4)) + (uint32_t)r1 * rowstride;
     dl.rs16 = 16 * rowstride;
   }
-  const uint32_t m0b = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)wave * 2u * D * 2u);
+  const uint32_t m0b = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)dl_r0 * D * 2u);
 
   // K operand reads: lane reads row 32 kb + lr, chunk 2s + h.  (2s + h) ^ swz
   // = 2s ^ x with x = h ^ swz < 16, so steps s and s + 8 differ by 256 bytes
@@ -611,6 +676,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // over significant tiles of (rounded - fp32) tile sums; a tile is
   // significant when a lane's tile sum exceeds its bound sbnd
   float dq[NRB], sbnd[NRB];
+  // HD = 128: the raw scores of the last two tiles, by tile parity.  Buffer
+  // 1 starts at -inf: the first block's softmax (of tile -1) then yields
+  // zero probabilities.
+  f32x16 sc[2][NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sc[0][rb][i] = 0.f;
+      sc[1][rb][i] = kNegInf;
+    }
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     // a finite start (-FLT_MAX): the first max update needs no -inf guard,
@@ -799,9 +875,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     step(wk_, 0);
     issue_k(wk_, kslot(1));
     step(wk_, 0);  // K copies run two tiles ahead ...
-    issue_v(zero, vslot(3));
-    issue_v(wv_, vslot(0));
-    step(wv_, 1);  // ... V copies one
+    if constexpr (ASM128) {
+      // ... and block u copies V tile u: tiles -2 and -1 (the P.V of the
+      // first two blocks) read zeros
+      issue_v(zero, vslot(2));
+      issue_v(zero, vslot(3));
+    } else {
+      issue_v(zero, vslot(3));
+      issue_v(wv_, vslot(0));
+      step(wv_, 1);  // ... V copies one
+    }
   }
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
@@ -810,11 +893,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       pb[rb][ks] = pbl[rb][ks] = pbuf[0][rb][ks] = pbuf[1][rb][ks] = bf16x8{};
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
   __syncthreads();
-  // HD = 256: the first two K operands of tile 0 (each block reads them for
-  // the tile after it).
+  // Hand-scheduled blocks: the first two K operands of tile 0 (each block
+  // reads them for the tile after it).
   bf16x8 kpre[2];
 #if defined(__HIP_DEVICE_COMPILE__)
-  if constexpr (ASM256)
+  if constexpr (ASMBLK)
     asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
                  : "={v[236:239]}"(kpre[0]), "={v[240:243]}"(kpre[1])
                  : "v"(ka[0]), "v"(ka[1])
@@ -846,7 +929,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
 #endif
-    if constexpr (SL % 2 == 0 && !ASM256) {  // start of a pair: the copies of the next pair
+    if constexpr (SL % 2 == 0 && !ASMBLK) {  // start of a pair: the copies of the next pair
       if (v + 2 <= T) {
         issue_k(wk_, kslot((SL + 2) % 4));
         step(wk_, 0);
@@ -881,6 +964,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
         if (wk_.left == 0) enter(wk_, wk_.k + 1, 0, 0);
         if (wv_.left == 0) enter(wv_, wv_.k + 1, 0, 1);
       }
+    } else if constexpr (ASM128) {
+      // block v: scores of tile v, softmax of tile v-1, P.V of tile v-2
+      const TileBound tb{wb_.k, p.P, wg_min_pos - 31, v, T};
+      // this block's copies: K of tile v + 2 and V of tile v
+      const i32x4 dkr = desc_of(wk_), dvr = desc_of(wv_);
+      uint32_t tmin;
+      tile_hd128<SL * TILE_B, ((SL + 2) % 4) * TILE_B, SL & 1, ((SL + 2) % 4) * TILE_B,
+                 VBASE + SL * TILE_B, ((SL + 1) % 4) * TILE_B>(
+          acc, sc, pbuf[0], pbuf[1], qreg, kpre, ka, va, mlog, lsum2[SL & 1], lcomp2[SL & 1],
+          lsum2[(SL & 1) ^ 1], lcomp2[(SL & 1) ^ 1], dq, sbnd, alpha, resc, c2, kTau<F32OUT>,
+          kPBound, tb, pos, dkr, dvr, wk_.off, wv_.off, wb_.lim, wb_.dlim, wb_.left, wk_.left,
+          wv_.left, tile_stride, tmin, m0b, dl);
+      if (__builtin_expect(tmin == 0, 0)) {
+        if (wb_.left == 0) enter(wb_, wb_.k + 1, 0, 0);
+        if (wk_.left == 0) enter(wk_, wk_.k + 1, 0, 0);
+        if (wv_.left == 0) enter(wv_, wv_.k + 1, 0, 1);
+      }
     } else {
       int lim[NRB];
       bool cut = bounds(wb_, lim);
@@ -900,28 +1000,31 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     __syncthreads();
 #endif
     if constexpr (SL % 2 == 1) {  // end of a pair
-      if constexpr (!ASM256) {  // (the HD = 256 block waits and synchronises itself)
+      if constexpr (!ASMBLK) {  // (the hand-scheduled blocks wait and synchronise themselves)
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
         __syncthreads();
       }
     }
   };
-  // Tiles 0 .. T (pass T is the P.V of the last tile), four per trip so that
-  // the slot offsets are constants.
+  // Tiles 0 .. T (pass T is the P.V of the last tile; at HD = 128 passes
+  // T and T + 1 are the softmax and the P.V of the last tile), four per
+  // trip so that the slot offsets are constants.  The walk ends on an odd
+  // pass, so the final row sums are in set 0.
+  const int v_last = ASM128 ? T + 1 : T;
   for (int v = 0;;) {
     body(std::integral_constant<int, 0>{}, v);
     body(std::integral_constant<int, 1>{}, v + 1);
-    if ((v += 2) > T) break;
+    if ((v += 2) > v_last) break;
     body(std::integral_constant<int, 2>{}, v);
     body(std::integral_constant<int, 3>{}, v + 1);
-    if ((v += 2) > T) break;
+    if ((v += 2) > v_last) break;
   }
 
 #if defined(__HIP_DEVICE_COMPILE__)
   // the last P.V MFMAs (inline asm, unseen by the compiler's hazard checks)
   // may still be writing acc, which is read below
   // (and the last block's KPRE reads may still be landing)
-  if constexpr (ASM256) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+  if constexpr (ASMBLK) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15" ::: "memory");
 #endif
 
   // Epilogue: out = acc / l, lse = ln 2 * (m + log2 l).  The lane's rows
@@ -939,8 +1042,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     // the rounded probabilities its numerator took (HD = 256: of the
     // significant tiles), fp32 output (hi + lo probabilities) by the fp32
     // sum
-    const float l_own = ASM256 ? lsum2[0][rb] - lcomp2[0][rb] : lsum[rb] - lcomp[rb];
-    const float lq_own = ASM256 ? l_own + dq[rb] : lsum_q[rb] - lcomp_q[rb];
+    const float l_own = ASMBLK ? lsum2[0][rb] - lcomp2[0][rb] : lsum[rb] - lcomp[rb];
+    const float lq_own = ASMBLK ? l_own + dq[rb] : lsum_q[rb] - lcomp_q[rb];
     const float l_tot = l_own + __shfl_xor(l_own, 32);
     const float l_norm = F32OUT ? l_tot : lq_own + __shfl_xor(lq_own, 32);
     if (!row_ok[rb]) continue;

@@ -280,12 +280,14 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         ra.lib()
 
 
-def test_generated_tile_block_is_current():
-    """The HD = 256 tile block is generated; the committed include must be
-    what its generator writes (else the kernel runs a stale schedule)."""
+@pytest.mark.parametrize("hd", [256, 128])
+def test_generated_tile_block_is_current(hd):
+    """The HD = 256 and HD = 128 tile blocks are generated; each committed
+    include must be what its generator writes (else the kernel runs a stale
+    schedule)."""
     import subprocess
     import sys
-    gen = os.path.join(ROOT, "context_causal_attention_ring_amd", "csrc", "gen_tile_hd256.py")
+    gen = os.path.join(ROOT, "context_causal_attention_ring_amd", "csrc", f"gen_tile_hd{hd}.py")
     res = subprocess.run([sys.executable, gen, "--check"], capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
 
