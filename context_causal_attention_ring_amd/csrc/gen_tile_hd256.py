@@ -524,14 +524,20 @@ def qk_again():
     return out + ["s_nop 15", "s_nop 15"]  # the scores are read by VALU next
 
 
-def assign(ops, ngaps):
-    """Split the ops into ngaps consecutive groups of even cumulative cost."""
+def assign(ops, ngaps, weights=None):
+    """Split the ops into ngaps consecutive groups of even cumulative cost
+    (or of cost in proportion to weights, one per gap)."""
     total = sum(COST[k] for k, _ in ops)
     per = total / ngaps
+    w = weights or [1.0] * ngaps
+    bounds, run = [], 0.0
+    for x in w:  # cumulative cost at the end of each gap
+        run += x
+        bounds.append(total * run / sum(w))
     gaps = [[] for _ in range(ngaps)]
     acc, g = 0.0, 0
     for kind, text in ops:
-        while g < ngaps - 1 and acc + COST[kind] / 2 > per * (g + 1):
+        while g < ngaps - 1 and acc + COST[kind] / 2 > bounds[g]:
             g += 1
         gaps[g].append(text)
         acc += COST[kind]
