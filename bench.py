@@ -51,7 +51,8 @@ def alg_bytes(w, with_write):
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "ring_attn_fused_32k_hbm_traffic.md")
 FUSED_SOURCES = [os.path.join(ROOT, "context_causal_attention_ring_amd", "csrc", f)
-                 for f in ("ring_attn_fused.hip", "tile_hd256.inc", "tile_hd128.inc")]
+                 for f in ("ring_attn_fused.hip", "tile_hd256.inc", "tile_hd128.inc",
+                           "tile_hd64.inc")]
 
 
 def peak_sclk_mhz():

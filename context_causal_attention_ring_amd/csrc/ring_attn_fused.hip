@@ -320,71 +320,75 @@ __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], bf16x8 (&p0)[2][
 #endif
 }
 
-// One step of the HD = 128 tile loop, bf16 output (generated: tile_hd128.inc;
-// this binds its operands).  Block u computes S^T = K Q^T of tile u (K slot
-// at KOFF, first two operands in kpre) into score buffer sc[E], E = u mod 2;
-// runs the online softmax of tile u-1 on sc[1 - E] (its raw scores stay:
-// the exponentials go to temporaries) into probability buffer 1 - E, with
-// the slow path and the significant-tile correction of the HD = 256 block;
-// and accumulates O^T += V^T P^T of tile u-2 (V slot at VOFF, probability
-// buffer E).  The softmax is spread over all 32 MFMAs.  When tile u is cut
-// by a key bound its scores are masked at the end of the block, for the
-// next one.  Copies: the wave's rows of K tile u + 2 (to MK) and V tile u
-// (to MV), two instructions each; copy b of wave w moves rows 4 w + 16 b
-// and the next three, lane offset dl.ka / dl.va, and b = 1 adds dl.rs16 to
-// the scalar offset.  The even block reads tile u + 1's kpre from KPO
-// during its P.V; the odd block ends the pair (copies waited for, barrier)
-// and leaves the next kpre in flight.  The walkers step as in the HD = 256
-// block.  On return ml, lo / lko, al and resc are those of tile u-1's
-// softmax.
+// One step of the HD = 128 or HD = 64 tile loop, bf16 output (generated by
+// gen_tile_pipe.py: tile_hd128.inc, tile_hd64.inc; this binds their
+// operands).  Block u computes S^T = K Q^T of tile u (K slot at KOFF, first
+// two operands in kpre) into score buffer sc[E], E = u mod 2; runs the
+// online softmax of tile u-1 on sc[1 - E] (its raw scores stay: the
+// exponentials go to temporaries) into probability buffer 1 - E, with the
+// slow path and the significant-tile correction of the HD = 256 block; and
+// accumulates O^T += V^T P^T of tile u-2 (V slot at VOFF, probability
+// buffer E).  The softmax is spread over all the block's MFMAs.  When tile
+// u is cut by a key bound its scores are masked at the end of the block,
+// for the next one.  Copies: the wave's rows of K tile u + 2 (to MK) and V
+// tile u (to MV), D / 64 instructions each; copy b of wave w moves the 1024
+// / (2 D) rows from row (1024 / (2 D)) w + 16 b on, lane offset dl.ka /
+// dl.va, and b = 1 adds dl.rs16 to the scalar offset.  The even block reads
+// tile u + 1's kpre from KPO during its P.V; the odd block ends the pair
+// (copies waited for, barrier) and leaves the next kpre in flight.  The
+// walkers step as in the HD = 256 block.  On return ml, lo / lko, al and
+// resc are those of tile u-1's softmax.
 //   ka[j]  LDS address of this lane's K row at chunk (2j + h) ^ swizzle;
 //          k-step s reads ka[s] + KOFF
 //   va[d]  LDS address of this lane's transposed V read for d block d;
-//          step (ks, db) reads va[db] + VOFF + 4096 ks, and + 2048 for keys
+//          step (ks, db) reads va[db] + VOFF + 32 D ks, and + 16 D for keys
 //          8..15
-// Q is pinned to v[44:107], the score buffers to v[108:171], the
+// Q is pinned to v[44:44 + D / 2), the score buffers to v[108:171], the
 // probability buffers to v[172:203] and kpre to v[236:243]; the
 // exponentials use v[204:211] and the operand ring v[244:255] (clobbered).
 #include "tile_hd128.inc"
-template <uint32_t KOFF, uint32_t VOFF, int E, uint32_t MK, uint32_t MV, uint32_t KPO>
-__device__ __forceinline__ void tile_hd128(f32x16 (&acc)[2][4], f32x16 (&sc)[2][2],
-                                           bf16x8 (&p0)[2][2], bf16x8 (&p1)[2][2],
-                                           const bf16x8 (&q)[2][8], bf16x8 (&kpre)[2],
-                                           const uint32_t (&ka)[8], const uint32_t (&va)[4],
-                                           float (&ml)[2], const float (&li)[2],
-                                           const float (&lki)[2], float (&lo)[2], float (&lko)[2],
-                                           float (&dq)[2], float (&bnd)[2], float (&al)[2],
-                                           uint32_t& resc, float c2, float tau, float pbnd,
-                                           const TileBound& wb, const int (&pos)[2],
-                                           const i32x4& desck, const i32x4& descv,
-                                           uint32_t& offk, uint32_t& offv, int& wlim, int dlim,
-                                           int& lb, int& lk, int& lv, uint32_t tstr,
-                                           uint32_t& tmin, uint32_t m0b, const CopyLanes& dl) {
+#include "tile_hd64.inc"
+#define RA_TILE_PIPE_ASM(HD, E, SOUT, SRW, POUT, PIN)                                          \
+  asm volatile(RA_TILE_HD##HD##_E##E                                                            \
+               : RA_TILE_STATE_OPERANDS, RA_TILE_HD##HD##_ACC_OPERANDS,                         \
+                 RA_TILE_HD##HD##_KPRE_OPERANDS, RA_TILE_LQ_OPERANDS, RA_TILE_HD##HD##_##POUT,  \
+                 RA_TILE_HD##HD##_##SOUT, RA_TILE_HD##HD##_##SRW                                \
+               : RA_TILE_HD##HD##_Q_OPERANDS, RA_TILE_HD##HD##_##PIN, RA_TILE_INPUT_OPERANDS,   \
+                 RA_TILE_HD##HD##_OFFSET_OPERANDS, [one2] "s"(one2)                             \
+               : RA_TILE_HD##HD##_CLOBBERS, "memory", "scc", "m0")
+template <int D, uint32_t KOFF, uint32_t VOFF, int E, uint32_t MK, uint32_t MV, uint32_t KPO>
+__device__ __forceinline__ void tile_pipe(f32x16 (&acc)[2][D / 32], f32x16 (&sc)[2][2],
+                                          bf16x8 (&p0)[2][2], bf16x8 (&p1)[2][2],
+                                          const bf16x8 (&q)[2][D / 16], bf16x8 (&kpre)[2],
+                                          const uint32_t (&ka)[8], const uint32_t (&va)[4],
+                                          float (&ml)[2], const float (&li)[2],
+                                          const float (&lki)[2], float (&lo)[2], float (&lko)[2],
+                                          float (&dq)[2], float (&bnd)[2], float (&al)[2],
+                                          uint32_t& resc, float c2, float tau, float pbnd,
+                                          const TileBound& wb, const int (&pos)[2],
+                                          const i32x4& desck, const i32x4& descv,
+                                          uint32_t& offk, uint32_t& offv, int& wlim, int dlim,
+                                          int& lb, int& lk, int& lv, uint32_t tstr,
+                                          uint32_t& tmin, uint32_t m0b, const CopyLanes& dl) {
+  static_assert(D == 128 || D == 64, "three-tile blocks exist for HD 128 and 64");
 #if defined(__HIP_DEVICE_COMPILE__)
   float a0, b0, a1, b1, th0, th1, r0, r1;
   uint32_t st, mflag, lc, lm, cr, cc, v0, v1;
   uint64_t c0, c1, any;
   const float ninf = kNegInf;
   const uint32_t one2 = 0x3F803F80u;  // bf16 pair (1, 1): v_dot2 sums a packed pair
-  if constexpr (E == 0) {
-    asm volatile(RA_TILE_HD128_E0
-                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD128_ACC_OPERANDS, RA_TILE_HD128_KPRE_OPERANDS,
-                   RA_TILE_LQ_OPERANDS, RA_TILE_HD128_PB_OUT1, RA_TILE_HD128_S_OUT0,
-                   RA_TILE_HD128_S_RW1
-                 : RA_TILE_HD128_Q_OPERANDS, RA_TILE_HD128_PB_IN0, RA_TILE_INPUT_OPERANDS,
-                   RA_TILE_HD128_OFFSET_OPERANDS, [one2] "s"(one2)
-                 : RA_TILE_HD128_CLOBBERS, "memory", "scc", "m0");
+  if constexpr (D == 128 && E == 0) {
+    RA_TILE_PIPE_ASM(128, 0, S_OUT0, S_RW1, PB_OUT1, PB_IN0);
+  } else if constexpr (D == 128) {
+    RA_TILE_PIPE_ASM(128, 1, S_OUT1, S_RW0, PB_OUT0, PB_IN1);
+  } else if constexpr (E == 0) {
+    RA_TILE_PIPE_ASM(64, 0, S_OUT0, S_RW1, PB_OUT1, PB_IN0);
   } else {
-    asm volatile(RA_TILE_HD128_E1
-                 : RA_TILE_STATE_OPERANDS, RA_TILE_HD128_ACC_OPERANDS, RA_TILE_HD128_KPRE_OPERANDS,
-                   RA_TILE_LQ_OPERANDS, RA_TILE_HD128_PB_OUT0, RA_TILE_HD128_S_OUT1,
-                   RA_TILE_HD128_S_RW0
-                 : RA_TILE_HD128_Q_OPERANDS, RA_TILE_HD128_PB_IN1, RA_TILE_INPUT_OPERANDS,
-                   RA_TILE_HD128_OFFSET_OPERANDS, [one2] "s"(one2)
-                 : RA_TILE_HD128_CLOBBERS, "memory", "scc", "m0");
+    RA_TILE_PIPE_ASM(64, 1, S_OUT1, S_RW0, PB_OUT0, PB_IN1);
   }
 #endif
 }
+#undef RA_TILE_PIPE_ASM
 #undef RA_TILE_STATE_OPERANDS
 #undef RA_TILE_LQ_OPERANDS
 #undef RA_TILE_INPUT_OPERANDS
@@ -402,11 +406,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   constexpr uint32_t TILE_B = TILE * 2;   // bytes of one K or V tile
   constexpr int DPW = kBKV * CPR / (64 * kWaves);  // DMA instructions per wave per tile
   static_assert(DPW >= 1 && DPW * 64 * kWaves == kBKV * CPR, "tile must split over the waves");
-  // hand-scheduled tile bodies: HD = 256 (both output types), HD = 128 (bf16
-  // output; fp32 output at HD = 128 runs the compiler-scheduled loop)
+  // hand-scheduled tile bodies: HD = 256 (both output types), the
+  // three-tile blocks at HD = 128 and 64 (bf16 output; fp32 output there
+  // runs the compiler-scheduled loop)
   constexpr bool ASM256 = D == 256 && NRB == 2 && NKB == 1;
-  constexpr bool ASM128 = D == 128 && !F32OUT && NRB == 2 && NKB == 1;
-  constexpr bool ASMBLK = ASM256 || ASM128;
+  constexpr bool ASMPIPE = (D == 128 || D == 64) && !F32OUT && NRB == 2 && NKB == 1;
+  constexpr bool ASMBLK = ASM256 || ASMPIPE;
   // LDS: K slots 0..3 then V slots 0..3 (tile t in slot t mod 4).  Slot
   // offsets are compile-time constants because the tile loop is unrolled
   // over the four slots.
@@ -608,15 +613,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   };
   // The copies issued from the hand-scheduled tile blocks split the rows
   // another way.  HD = 256: instruction 2 a + b of wave w moves rows R =
-  // 2 w + 8 a + 16 b and R + 1; HD = 128: instruction b moves rows R = 4 w +
-  // 16 b .. R + 3.  Rows 16 apart share their swizzle, so one lane offset
-  // per operand and a (two at HD = 256) carries the swizzle and R's rows
-  // for b = 0; the 16 more rows of b = 1 go into the scalar offset (the sum,
-  // which the descriptor bounds, is the same).
+  // 2 w + 8 a + 16 b and R + 1; HD = 128 and 64: instruction b moves the
+  // RPI rows from R = RPI w + 16 b on.  Rows 16 apart share their swizzle,
+  // so one lane offset per operand and a (two at HD = 256) carries the
+  // swizzle and R's rows for b = 0; the 16 more rows of b = 1 go into the
+  // scalar offset (the sum, which the descriptor bounds, is the same).
   CopyLanes dl;
-  const int dl_r0 = (D == 128 ? 4 : 2) * wave;  // the wave's first copied row
+  const int dl_r0 = RPI * wave;  // the wave's first copied row
   {
-    const int r0 = dl_r0, r1 = D == 128 ? dl_r0 : dl_r0 + 8;
+    const int r0 = dl_r0, r1 = D == 256 ? dl_r0 + 8 : dl_r0;
     dl.ka = (dma_kbase ^ (uint32_t)(swz_k(r0, CPR) << 4)) + (uint32_t)r0 * rowstride;
     dl.kb = (dma_kbase ^ (uint32_t)(swz_k(r1, CPR) << 4)) + (uint32_t)r1 * rowstride;
     dl.va = (dma_vbase ^ (uint32_t)(swz_v(r0, CPR) << 4)) + (uint32_t)r0 * rowstride;
@@ -676,7 +681,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // over significant tiles of (rounded - fp32) tile sums; a tile is
   // significant when a lane's tile sum exceeds its bound sbnd
   float dq[NRB], sbnd[NRB];
-  // HD = 128: the raw scores of the last two tiles, by tile parity.  Buffer
+  // HD = 128 and 64: the raw scores of the last two tiles, by tile parity.  Buffer
   // 1 starts at -inf: the first block's softmax (of tile -1) then yields
   // zero probabilities.
   f32x16 sc[2][NRB];
@@ -875,7 +880,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     step(wk_, 0);
     issue_k(wk_, kslot(1));
     step(wk_, 0);  // K copies run two tiles ahead ...
-    if constexpr (ASM128) {
+    if constexpr (ASMPIPE) {
       // ... and block u copies V tile u: tiles -2 and -1 (the P.V of the
       // first two blocks) read zeros
       issue_v(zero, vslot(2));
@@ -964,14 +969,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
         if (wk_.left == 0) enter(wk_, wk_.k + 1, 0, 0);
         if (wv_.left == 0) enter(wv_, wv_.k + 1, 0, 1);
       }
-    } else if constexpr (ASM128) {
+    } else if constexpr (ASMPIPE) {
       // block v: scores of tile v, softmax of tile v-1, P.V of tile v-2
       const TileBound tb{wb_.k, p.P, wg_min_pos - 31, v, T};
       // this block's copies: K of tile v + 2 and V of tile v
       const i32x4 dkr = desc_of(wk_), dvr = desc_of(wv_);
       uint32_t tmin;
-      tile_hd128<SL * TILE_B, ((SL + 2) % 4) * TILE_B, SL & 1, ((SL + 2) % 4) * TILE_B,
-                 VBASE + SL * TILE_B, ((SL + 1) % 4) * TILE_B>(
+      tile_pipe<D, SL * TILE_B, ((SL + 2) % 4) * TILE_B, SL & 1, ((SL + 2) % 4) * TILE_B,
+                VBASE + SL * TILE_B, ((SL + 1) % 4) * TILE_B>(
           acc, sc, pbuf[0], pbuf[1], qreg, kpre, ka, va, mlog, lsum2[SL & 1], lcomp2[SL & 1],
           lsum2[(SL & 1) ^ 1], lcomp2[(SL & 1) ^ 1], dq, sbnd, alpha, resc, c2, kTau<F32OUT>,
           kPBound, tb, pos, dkr, dvr, wk_.off, wv_.off, wb_.lim, wb_.dlim, wb_.left, wk_.left,
@@ -1006,11 +1011,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       }
     }
   };
-  // Tiles 0 .. T (pass T is the P.V of the last tile; at HD = 128 passes
-  // T and T + 1 are the softmax and the P.V of the last tile), four per
-  // trip so that the slot offsets are constants.  The walk ends on an odd
-  // pass, so the final row sums are in set 0.
-  const int v_last = ASM128 ? T + 1 : T;
+  // Tiles 0 .. T (pass T is the P.V of the last tile; with the three-tile
+  // blocks passes T and T + 1 are the softmax and the P.V of the last
+  // tile), four per trip so that the slot offsets are constants.  The walk
+  // ends on an odd pass, so the final row sums are in set 0.
+  const int v_last = ASMPIPE ? T + 1 : T;
   for (int v = 0;;) {
     body(std::integral_constant<int, 0>{}, v);
     body(std::integral_constant<int, 1>{}, v + 1);

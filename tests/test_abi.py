@@ -280,14 +280,14 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         ra.lib()
 
 
-@pytest.mark.parametrize("hd", [256, 128])
-def test_generated_tile_block_is_current(hd):
-    """The HD = 256 and HD = 128 tile blocks are generated; each committed
-    include must be what its generator writes (else the kernel runs a stale
-    schedule)."""
+@pytest.mark.parametrize("gen", ["gen_tile_hd256.py", "gen_tile_pipe.py"])
+def test_generated_tile_block_is_current(gen):
+    """The tile blocks (HD = 256; the three-tile blocks at HD = 128 and 64)
+    are generated; each committed include must be what its generator writes
+    (else the kernel runs a stale schedule)."""
     import subprocess
     import sys
-    gen = os.path.join(ROOT, "context_causal_attention_ring_amd", "csrc", f"gen_tile_hd{hd}.py")
+    gen = os.path.join(ROOT, "context_causal_attention_ring_amd", "csrc", gen)
     res = subprocess.run([sys.executable, gen, "--check"], capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
 

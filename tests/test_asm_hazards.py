@@ -1,6 +1,6 @@
 """Static checks of the compiled fused kernel around its hand-scheduled blocks.
 
-The HD = 256 and HD = 128 tile blocks are single inline-asm statements,
+The HD = 256, 128 and 64 tile blocks are single inline-asm statements,
 so the compiler's hazard checks do not see the MFMAs inside them.  An MFMA
 reads its A and B
 operands while it runs and writes its result at the end, so compiler code
@@ -118,9 +118,10 @@ def hazards_after(lines, at, mfmas):
 def test_no_compiler_code_races_the_last_mfmas_of_a_tile_block(extra):
     with tempfile.TemporaryDirectory() as tmp:
         asm = open(build.assemble(out=os.path.join(tmp, "fused.s"), extra=extra)).read()
-    # HD = 256 with bf16 and fp32 output, HD = 128 with bf16 output
-    kernels = re.findall(r"^(_ZN2ra\S*fused_kernel(?:ILi256\S*|ILi128ELb0\S*)):", asm, re.M)
-    assert len(kernels) == 3
+    # HD = 256 with bf16 and fp32 output, HD = 128 and 64 with bf16 output
+    kernels = re.findall(r"^(_ZN2ra\S*fused_kernel(?:ILi256\S*|ILi128ELb0\S*|ILi64ELb0\S*)):",
+                         asm, re.M)
+    assert len(kernels) == 4
     for name in kernels:
         body = asm[asm.index(name + ":"):asm.index(".Lfunc_end", asm.index(name + ":"))]
         lines = body.splitlines()

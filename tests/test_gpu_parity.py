@@ -265,14 +265,14 @@ def test_negative_control():
     assert d_bad >= 10 * max(d_ok, 1e-4)
 
 
-@pytest.mark.parametrize("hd", [256, 128])
+@pytest.mark.parametrize("hd", [256, 128, 64])
 def test_running_max_jumps_mid_walk(hd):
     """Every row's running max jumps by about 6 (natural units, > 8 in log2)
     on the third tile of the first shard visit, which the shard's end cuts
     (shards of 87-88 tokens, token round-robin: slots 0-63, tokens below
     512, fill the first two tiles): the tile blocks' slow path after the
     first tile, on a masked tile (HD = 256: scores recomputed and masked
-    again; HD = 128: the masked scores kept from the block before).  q
+    again; HD = 128 and 64: the masked scores kept from the block before).  q
     carries 4 in dimension 0 and cached keys before token 512 carry -24
     there (scores lowered by 6), later ones 0; the rows stay as spread as
     the plain workload (exact in bf16)."""
@@ -326,15 +326,16 @@ def test_parity_full_size(name, n_random):
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("hd", [128, 64])
 @pytest.mark.parametrize("name,n_random", [("32k", None), ("128k_rank2of8", None),
                                            ("1m", 64)])
-def test_parity_hd128_full_size(name, n_random):
-    """The configurations' shapes at HD = 128 (the hand-scheduled three-tile
-    block): every real row at 32k and on a 128k rank share, sampled rows
-    over the 1M walk (peaky keys, about 2000 tiles per row: drift of the
-    running sums and the significant-tile correction)."""
+def test_parity_pipe_full_size(name, n_random, hd):
+    """The configurations' shapes at HD = 128 and 64 (the hand-scheduled
+    three-tile blocks): every real row at 32k and on a 128k rank share,
+    sampled rows over the 1M walk (peaky keys, about 2000 tiles per row:
+    drift of the running sums and the significant-tile correction)."""
     base = workloads.CONFIGS[name]
-    w = workloads.with_fields(base, name=f"{name}-hd128", hd=128)
+    w = workloads.with_fields(base, name=f"{name}-hd{hd}", hd=hd)
     case = Case(w).to_device()
     out, lse = run(case)
     rows = list(range(w.real_rows)) if n_random is None else sample_rows(w, n_random, seed=w.seed)
