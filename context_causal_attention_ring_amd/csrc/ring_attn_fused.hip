@@ -21,7 +21,10 @@
 //    (the key order inside a 16-key step is permuted identically on both
 //    operands, which leaves the contraction unchanged).  The fp32
 //    accumulator (64 rows x HD) lives in the AGPRs; at HD = 256 each tile is
-//    one hand-scheduled asm block (tile_hd256.inc, see tile_hd256 below).
+//    one hand-scheduled asm block (tile_hd256.inc, see tile_hd256 below),
+//    and at HD = 128 and 64 with bf16 output one asm block per step works
+//    on three tiles: the scores of tile u, the softmax of tile u-1 and the
+//    P.V of tile u-2 (tile_hd128.inc, tile_hd64.inc, see tile_pipe below).
 //  * K/V tiles of 32 keys go HBM -> LDS by buffer_load ... lds (no register
 //    staging) into four K and four V slots (tile t in slot t mod 4).  Tiles
 //    run in pairs with one wait and one barrier per pair; while a pair is
@@ -45,7 +48,9 @@
 //    by more than kTau (a vote), so the common tile costs fma, exp2, add and
 //    a bf16 pack per score.  The softmax of tile v is issued between the
 //    P.V MFMAs of tile v-1, which do not depend on it, in a hand-ordered
-//    block (one MFMA pair, one V operand read, a slice of softmax work).
+//    block (one MFMA pair, one V operand read, a slice of softmax work); in
+//    the three-tile blocks between all the MFMAs of the next step, whose
+//    score MFMAs write the other of two score buffers.
 //  * P.V takes bf16 weights.  bf16 output is normalised by the fp32 row sum
 //    corrected, for every tile that holds a sizeable share of a row's
 //    weight, by the rounding of that tile's weights, so numerator and
@@ -85,10 +90,11 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // P.V as a bf16 pair hi + lo that holds it to about 2^-16.
 template <bool F32OUT>
 constexpr float kTau = 8.0f;
-// With bf16 output the HD = 256 block first takes each tile's scores against
+// With bf16 output the tile blocks first take each tile's scores against
 // the running max as it stands; a lane whose 16 probabilities sum to more
 // than 2^kTau may hold one above 2^kTau, and then the block recomputes the
-// tile with the max updated.
+// tile with the max updated (at HD = 256 from its K slot, in the three-tile
+// blocks from the scores they kept).
 constexpr float kPBound = 256.0f;  // 2^kTau<false>
 
 // Chunk swizzles (16-byte chunks within a tile row).  K rows are read 32 at
@@ -668,22 +674,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // bf16 probabilities of the previous tile (B operands of P.V); with fp32
   // output pb holds each probability's bf16 part and pbl the rest, rounded
   bf16x8 pb[NRB][NPS], pbl[NRB][NPS];
-  // HD = 256 body: bf16 output double-buffers the probabilities by tile
-  // parity; fp32 output keeps hi in pbuf[0] and lo in pbuf[1]
+  // hand-scheduled blocks: bf16 output double-buffers the probabilities by
+  // tile parity; fp32 output (HD = 256) keeps hi in pbuf[0] and lo in pbuf[1]
   bf16x8 pbuf[2][NRB][NPS];
   float mlog[NRB], lsum[NRB], lsum_q[NRB];  // running max (log2 units), row sums
   float lcomp[NRB], lcomp_q[NRB];            // their compensations (fold_sum)
-  // HD = 256: the row sums and compensations in two sets, read by even
-  // tiles from [0] and odd tiles from [1], each writing the other; the walk
-  // ends on an odd tile, so the final sums are in [0]
+  // hand-scheduled blocks: the row sums and compensations in two sets, read
+  // by the softmax of even tiles from [0] (HD = 256; [1] in the three-tile
+  // blocks) and of odd tiles from the other, each writing the set it does
+  // not read; the final sums end in [0] either way
   float lsum2[2][NRB], lcomp2[2][NRB];
-  // HD = 256, bf16 output: the output's normaliser is lsum + dq, dq the sum
-  // over significant tiles of (rounded - fp32) tile sums; a tile is
-  // significant when a lane's tile sum exceeds its bound sbnd
+  // hand-scheduled blocks, bf16 output: the output's normaliser is lsum +
+  // dq, dq the sum over significant tiles of (rounded - fp32) tile sums; a
+  // tile is significant when a lane's tile sum exceeds its bound sbnd
   float dq[NRB], sbnd[NRB];
-  // HD = 128 and 64: the raw scores of the last two tiles, by tile parity.  Buffer
-  // 1 starts at -inf: the first block's softmax (of tile -1) then yields
-  // zero probabilities.
+  // Three-tile blocks: the raw scores of the last two tiles, by tile parity.
+  // Buffer 1 starts at -inf: the first block's softmax (of tile -1) then
+  // yields zero probabilities.
   f32x16 sc[2][NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
@@ -1044,9 +1051,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
     head[rb] = g * p.group + (row - token[rb] * p.group);
     row_ok[rb] = token[rb] < p.real_rows;
     // the LSE takes the fp32 sum; bf16 output is normalised by the sum of
-    // the rounded probabilities its numerator took (HD = 256: of the
-    // significant tiles), fp32 output (hi + lo probabilities) by the fp32
-    // sum
+    // the rounded probabilities its numerator took (hand-scheduled blocks:
+    // of the significant tiles), fp32 output (hi + lo probabilities) by the
+    // fp32 sum
     const float l_own = ASMBLK ? lsum2[0][rb] - lcomp2[0][rb] : lsum[rb] - lcomp[rb];
     const float lq_own = ASMBLK ? l_own + dq[rb] : lsum_q[rb] - lcomp_q[rb];
     const float l_tot = l_own + __shfl_xor(l_own, 32);
