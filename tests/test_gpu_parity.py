@@ -550,7 +550,10 @@ def run_split(case, splits, out_fp32=False, ring_start=0):
 
 SPLIT_CASES = [(workloads.CONFIGS["tiny"], 3), (FULL_CASES[1], 2), (FULL_CASES[2], 7),
                (RANK_CASES[2], 5), (small("split-nocache", cache_len=0, P=1), 4),
-               (small("split-many", cache_len=1000, P=3), 64), (FULL_CASES[-1], 7)]
+               (small("split-many", cache_len=1000, P=3), 64), (FULL_CASES[-1], 7),
+               # the HD = 64 three-tile block with empty and one-tile segments
+               (small("split-nocache-hd64", hd=64, cache_len=0, P=1), 4),
+               (small("split-many-hd64", hd=64, cache_len=1000, P=3), 64)]
 
 
 @pytest.mark.parametrize("w,splits", SPLIT_CASES, ids=lambda x: getattr(x, "name", str(x)))
