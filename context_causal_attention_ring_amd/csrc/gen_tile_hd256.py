@@ -171,36 +171,37 @@ def dma_issue(i):
     return [f"buffer_load_dwordx4 %[d{kind}{'b' if a else 'a'}], %[desc{kind}], {soff} offen lds"]
 
 
+def walk_ops():
+    """The tile's scalar bookkeeping, one group in the shadow of the QK^T
+    MFMAs: the bound walker's key bound wlim moves on to the next tile by
+    dlim (-32 in a shard visit, +32 in the current tiles); nm, the tiles
+    left before the next one a key bound cuts (set by the code around the
+    block whenever the bound walker enters a region), and tn, the tiles left
+    before some walker enters its next region, drop by one.  This tile is
+    cut when nm has gone negative (mask_test); the code after the block
+    takes the walkers into their next regions when tn reaches 0.  The copy
+    offsets move on after the block's last copy (copy_step_ops)."""
+    return ["s_add_i32 %[wlim], %[wlim], %[dlim]", "s_sub_i32 %[nm], %[nm], 1",
+            "s_sub_u32 %[tn], %[tn], 1"]
+
+
+def mask_test(label):
+    """Branch to label when a key bound cuts this tile (after walk_ops)."""
+    return ["s_cmp_lt_i32 %[nm], 0", f"s_cbranch_scc1 {label}"]
+
+
 def bound_ops():
-    """The tile's key bound, all scalar, in the shadow of the QK^T MFMAs, as
-    groups that keep each compare next to the selects that read it: lm = 1
-    for the current tiles (region wk >= P); mflag when a visit's keys end
-    inside the tile (wlim < 32), on the causal diagonal (wlim > wm31 =
-    smallest row position - 31) or past the walk (vv >= tt); lc = wlim in a
-    visit, 1 - wlim for the current tiles, -32 past the walk."""
-    return [
-        ["s_cmp_ge_i32 %[wk], %[np]", "s_cselect_b32 %[lm], 1, 0"],
-        ["s_cmp_lt_i32 %[wlim], 32", "s_cselect_b32 %[cr], 1, 0"],
-        ["s_cmp_gt_i32 %[wlim], %[wm31]", "s_cselect_b32 %[cc], 1, 0"],
-        ["s_sub_i32 %[lc], 1, %[wlim]"],
-        ["s_cmp_eq_u32 %[lm], 0", "s_cselect_b32 %[mflag], %[cr], %[cc]",
-         "s_cselect_b32 %[lc], %[wlim], %[lc]"],
-        ["s_cmp_ge_i32 %[vv], %[tt]", "s_cselect_b32 %[mflag], 1, %[mflag]",
-         "s_cselect_b32 %[lm], 0, %[lm]", "s_cselect_b32 %[lc], -32, %[lc]"],
-    ] + walker_ops()
-
-
-def walker_ops():
-    """The walkers' step to the next tile, scalar, in the QK^T MFMAs' shadow
-    after the bound ops have read this tile's bound: the bound walker's key
-    bound moves by dlim (-32 in a shard visit, +32 in the current tiles) and
-    each walker's count of tiles left in its region drops by one; tmin, the
-    smallest count, tells the code after the block whether a walker enters
-    its next region (tmin = 0).  The copy offsets move on after the block's
-    last copy (copy_step_ops)."""
-    return [["s_add_i32 %[wlim], %[wlim], %[dlim]", "s_sub_u32 %[lb], %[lb], 1",
-             "s_sub_u32 %[lk], %[lk], 1", "s_sub_u32 %[lv], %[lv], 1"],
-            ["s_min_u32 %[tmin], %[lb], %[lk]", "s_min_u32 %[tmin], %[tmin], %[lv]"]]
+    """The cut tile's key bound, all scalar, on the mask's own path (wlim
+    has already moved on by dlim): lm = 1 for the current tiles (region wk
+    >= P), lc = the bound, wt = this tile's wlim: lc = wt in a visit (keys
+    left), 1 - wt for the current tiles (wt = the tile's first position),
+    -32 past the walk (vv >= tt, with lm = 0: every key masked)."""
+    return ["s_sub_i32 %[wt], %[wlim], %[dlim]",
+            "s_cmp_ge_i32 %[wk], %[np]", "s_cselect_b32 %[lm], 1, 0",
+            "s_sub_i32 %[lc], 1, %[wt]",
+            "s_cmp_eq_u32 %[lm], 0", "s_cselect_b32 %[lc], %[wt], %[lc]",
+            "s_cmp_ge_i32 %[vv], %[tt]", "s_cselect_b32 %[lm], 0, %[lm]",
+            "s_cselect_b32 %[lc], -32, %[lc]"]
 
 
 def copy_step_ops():
@@ -210,11 +211,12 @@ def copy_step_ops():
 
 
 def qk_part(extra=()):
-    """S^T = K Q^T with the block's copies and bound ops; `extra` VALU ops
-    (independent of the scores) are spread over the k-steps, two per step."""
+    """S^T = K Q^T with the block's copies and scalar bookkeeping; `extra`
+    VALU ops (independent of the scores) are spread over the k-steps, two
+    per step."""
     # KPRE was read by the block before (or before the loop): wait for it.
     out = ["s_nop 1", "s_waitcnt lgkmcnt(0)"] + dma_setup(0)
-    bound = bound_ops()
+    bound = [walk_ops()]
     assert len(bound) <= NKS // 2, "one group of scalar ops per even k-step"
     extra = list(extra)
     per = -(-len(extra) // NKS) if extra else 0
@@ -331,12 +333,14 @@ def mask_part(src=s):
     pos_rb + lc (current tiles, lm = 1: lc = 1 - first key's position).
     Lane half h holds keys 8 (i / 4) + 4 h + i % 4 of the tile; with lim =
     bound - 4 h, key slot i is kept iff 8 (i / 4) + i % 4 < lim."""
-    return ["s_cmp_eq_u32 %[mflag], 0", "s_cbranch_scc1 1f"] + mask_body(src) + ["1:"]
+    return ["s_cmp_ge_i32 %[nm], 0", "s_cbranch_scc1 1f"] + mask_body(src) + ["1:"]
 
 
 def mask_body(src=s):
-    """mask_part without its test: the per-row bounds, then the compares."""
-    out = ["v_mbcnt_lo_u32_b32 %[a0], -1, 0", "v_mbcnt_hi_u32_b32 %[a0], -1, %[a0]",
+    """mask_part without its test: the tile's bound (bound_ops), the per-row
+    bounds, then the compares."""
+    out = bound_ops()
+    out += ["v_mbcnt_lo_u32_b32 %[a0], -1, 0", "v_mbcnt_hi_u32_b32 %[a0], -1, %[a0]",
            "v_lshrrev_b32 %[a0], 5, %[a0]", "v_lshlrev_b32 %[a0], 2, %[a0]",  # 4 h
            "s_cmp_eq_u32 %[lm], 0", "s_cbranch_scc0 2f"]
     out += [f"v_sub_u32 %[th{rb}], %[lc], %[a0]" for rb in range(NRB)] + ["s_branch 3f", "2:"]
@@ -693,7 +697,7 @@ def render():
             if lazy:
                 pv, per = pv_part(pin, True)
                 # the mask (rare) is out of line, branched to
-                body = qk_part() + ["s_cmp_lg_u32 %[mflag], 0", "s_cbranch_scc1 7f", "6:"] + pv
+                body = qk_part() + mask_test("7f") + ["6:"] + pv
             else:
                 pv, per = pv_part_f32(pin == 1)
                 body = qk_part() + mask_part() + pv

@@ -27,8 +27,8 @@ Tiles run in pairs (K and V slots t mod 4).  Block u (E = u mod 2):
   buffer 1 - E against the running max as it stands, exponentials into
   temporaries, the row sums and their compensated fold, the bf16
   probabilities into buffer 1 - E, and a test of each lane's tile sum
-  against its bound.  The scalar key bound of tile u and the walkers' step
-  to the next tile share the same shadow.
+  against its bound.  The walkers' step to the next tile shares the same
+  shadow.
   3. When a lane's tile sum passed its bound: if some probability may exceed
      2^tau, the full softmax (running-max vote, rescale factors, exact new
      max where voted) on tile u-1's intact scores; either way the tile is
@@ -51,7 +51,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
-import gen_tile_hd256 as base  # noqa: E402  (softmax, bound, walker and hazard helpers)
+import gen_tile_hd256 as base  # noqa: E402  (softmax, mask, walker and hazard helpers)
 
 NPS = 2            # 16-key steps of P.V per 32-key tile
 NRB = base.NRB     # 32-row blocks per wave
@@ -63,9 +63,8 @@ KPRE = base.KPRE   # K operands of k-steps 0 and 1 (pinned), read ahead
 RING0 = base.RING0  # operand ring (clobbered)
 KPRE_STEP = 2      # P.V step of an even block after which the next tile's KPRE is read
 # Softmax share of an MFMA gap in the S^T half relative to the P.V half: the
-# S^T half also carries the copies and the scalar bound and walker ops
-# (HD = 128: 0.7 measured 0.2-1.5 % faster than an even split on gfx950,
-# 1.3 slower).
+# S^T half also carries the copies and the walkers' scalar step (HD = 128:
+# 0.7 measured 0.2-1.5 % faster than an even split on gfx950, 1.3 slower).
 QK_WEIGHT = {128: 0.7, 64: 0.7}
 
 
@@ -184,10 +183,9 @@ def block(g, E):
     half = g.nm // 2
     gaps, per = base.assign(softmax_common(sr, pout), g.nm,
                             [g.qk_weight] * half + [1.0] * half)
-    # scalar groups: the key bound of tile u, then the walkers' step (each
-    # group keeps its compares next to the selects that read SCC), one
-    # group after every stride-th step of the block's 2 nks steps
-    bound = base.bound_ops()
+    # scalar groups (here the one of base.walk_ops), one after every
+    # stride-th step of the block's 2 nks steps
+    bound = [base.walk_ops()]
     stride = 2 * g.nks // len(bound)
     assert stride * len(bound) == 2 * g.nks
     out = ["s_nop 1", "s_waitcnt lgkmcnt(0)"] + dma_setup(g, 0)
@@ -244,8 +242,8 @@ def block(g, E):
     assert m == g.nm and step == 2 * g.nks
     tail = [] if even else ["s_waitcnt vmcnt(0)", "s_barrier"] + base.kpre_reads()
     # Common path: no lane's tile sum passed its bound and tile u is not cut.
-    out += ["s_cmp_lg_u64 %[any], 0", "s_cbranch_scc1 8f", "10:",
-            "s_cmp_lg_u32 %[mflag], 0", "s_cbranch_scc1 7f", "11:"] + tail + ["s_branch 9f"]
+    out += ["s_cmp_lg_u64 %[any], 0", "s_cbranch_scc1 8f", "10:"] + base.mask_test("7f")
+    out += ["11:"] + tail + ["s_branch 9f"]
     # tile u cut by a key bound: mask its scores, for the next block
     out += ["7:"] + base.mask_body(sreg(sw)) + ["s_branch 11b"]
     # Some lane's tile sum passed its bound: if some probability may

@@ -217,10 +217,11 @@ __device__ __forceinline__ float wave_max_pair(float x) {
 // b adds dl.rs16, 16 rows' stride, to the scalar offset.  The caller waits
 // for them (vmcnt) and synchronises before the slots are read.
 // It then steps the walkers to the next tile in the same shadow: offk and
-// offv by tstr (one tile), the bound walker's wlim by dlim, and the tiles
-// left in each walker's region (lb, lk, lv) by one; tmin returns the
-// smallest of these, and the caller enters the next region of each walker
-// whose count reached 0.
+// offv by tstr (one tile), the bound walker's wlim by dlim, and the two
+// counters the caller keeps by one: nm, the tiles before the next one a key
+// bound cuts (this tile is cut when nm was 0 or below: the mask above), and
+// tn, the tiles before some walker enters its next region (at 0 the caller
+// takes the walkers there).
 #include "tile_hd256.inc"
 #define RA_TILE_STATE_OPERANDS                                                                  \
   [ml0] "+v"(ml[0]), [ml1] "+v"(ml[1]), [lo0] "=&v"(lo[0]), [lo1] "=&v"(lo[1]),                 \
@@ -228,9 +229,8 @@ __device__ __forceinline__ float wave_max_pair(float x) {
       [resc] "=&s"(resc), [any] "=&s"(any), [a0] "=&v"(a0), [b0] "=&v"(b0), [a1] "=&v"(a1),    \
       [b1] "=&v"(b1), [th0] "=&v"(th0), [th1] "=&v"(th1), [r0] "=&v"(r0), [r1] "=&v"(r1),      \
       [c0] "=&s"(c0), [c1] "=&s"(c1), [v0] "=&s"(v0), [v1] "=&s"(v1), [st] "=&s"(st),          \
-      [mflag] "=&s"(mflag), [lc] "=&s"(lc), [lm] "=&s"(lm), [cr] "=&s"(cr), [cc] "=&s"(cc),     \
-      [offk] "+s"(offk), [offv] "+s"(offv), [wlim] "+s"(wlim), [lb] "+s"(lb), [lk] "+s"(lk),    \
-      [lv] "+s"(lv), [tmin] "=&s"(tmin)
+      [lc] "=&s"(lc), [lm] "=&s"(lm), [wt] "=&s"(wt), [offk] "+s"(offk), [offv] "+s"(offv),   \
+      [wlim] "+s"(wlim), [nm] "+s"(nm), [tn] "+s"(tn)
 // bf16 output: the rounded-minus-fp32 sums of the significant tiles, and
 // the tile-sum bound past which a tile is significant
 #define RA_TILE_LQ_OPERANDS                                                                     \
@@ -240,8 +240,8 @@ __device__ __forceinline__ float wave_max_pair(float x) {
       [ka5] "v"(ka[5]), [ka6] "v"(ka[6]), [ka7] "v"(ka[7]), [va0] "v"(va[0]), [va1] "v"(va[1]), \
       [va2] "v"(va[2]), [va3] "v"(va[3]), [c2] "s"(c2), [tau] "s"(tau), [pbnd] "s"(pbnd),       \
       [wk] "s"(wb.k), [li0] "v"(li[0]), [li1] "v"(li[1]), [lki0] "v"(lki[0]),                   \
-      [lki1] "v"(lki[1]), [np] "s"(wb.np), [dlim] "s"(dlim), [wm31] "s"(wb.wm31),               \
-      [vv] "s"(wb.v), [tt] "s"(wb.t), [pos0] "v"(pos[0]), [pos1] "v"(pos[1]),                   \
+      [lki1] "v"(lki[1]), [np] "s"(wb.np), [dlim] "s"(dlim), [vv] "s"(wb.v), [tt] "s"(wb.t),   \
+      [pos0] "v"(pos[0]), [pos1] "v"(pos[1]),                                                  \
       [ninf] "v"(ninf), [kpo] "i"(KPO), [desck] "s"(desck), [descv] "s"(descv),                 \
       [tstr] "s"(tstr), [m0b] "s"(m0b), [rs16] "s"(dl.rs16)
 // l <- l * a + r, compensated (Kahan summation): c holds the part of the
@@ -259,9 +259,8 @@ __device__ __forceinline__ void fold_sum(float& l, float& c, float a, float r) {
   l = t;
 }
 
-struct TileBound {    // what the block derives the tile's key bound from (uniform)
+struct TileBound {    // what a cut tile's key bound comes from (uniform)
   int k, np;          // the tile's region and P (k >= P: current tiles)
-  int wm31;           // smallest chunk position of the workgroup's rows - 31
   int v, t;           // the tile and the walk's length (v >= t: past the walk)
 };
 
@@ -282,11 +281,11 @@ __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], bf16x8 (&p0)[2][
                                            const TileBound& wb, const int (&pos)[2],
                                            const i32x4& desck, const i32x4& descv,
                                            uint32_t& offk, uint32_t& offv, int& wlim, int dlim,
-                                           int& lb, int& lk, int& lv, uint32_t tstr,
-                                           uint32_t& tmin, uint32_t m0b, const CopyLanes& dl) {
+                                           int& nm, uint32_t& tn, uint32_t tstr, uint32_t m0b,
+                                           const CopyLanes& dl) {
 #if defined(__HIP_DEVICE_COMPILE__)
   float a0, b0, a1, b1, th0, th1, r0, r1;
-  uint32_t st, mflag, lc, lm, cr, cc, v0, v1;
+  uint32_t st, lc, lm, wt, v0, v1;
   uint64_t c0, c1, any;
   const float ninf = kNegInf;
   const uint32_t one2 = 0x3F803F80u;   // bf16 pair (1, 1): v_dot2 sums a packed pair
@@ -374,12 +373,12 @@ __device__ __forceinline__ void tile_pipe(f32x16 (&acc)[2][D / 32], f32x16 (&sc)
                                           const TileBound& wb, const int (&pos)[2],
                                           const i32x4& desck, const i32x4& descv,
                                           uint32_t& offk, uint32_t& offv, int& wlim, int dlim,
-                                          int& lb, int& lk, int& lv, uint32_t tstr,
-                                          uint32_t& tmin, uint32_t m0b, const CopyLanes& dl) {
+                                          int& nm, uint32_t& tn, uint32_t tstr, uint32_t m0b,
+                                          const CopyLanes& dl) {
   static_assert(D == 128 || D == 64, "three-tile blocks exist for HD 128 and 64");
 #if defined(__HIP_DEVICE_COMPILE__)
   float a0, b0, a1, b1, th0, th1, r0, r1;
-  uint32_t st, mflag, lc, lm, cr, cc, v0, v1;
+  uint32_t st, lc, lm, wt, v0, v1;
   uint64_t c0, c1, any;
   const float ninf = kNegInf;
   const uint32_t one2 = 0x3F803F80u;  // bf16 pair (1, 1): v_dot2 sums a packed pair
@@ -933,6 +932,43 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
         }
     }
   };
+  // Hand-scheduled blocks: the walkers' region changes and the key-bound
+  // cuts happen at tiles known ahead, so the blocks keep two counters
+  // instead of testing every tile.  cut_in: the tiles from the bound
+  // walker's tile v on before the first one a key bound cuts -- in a shard
+  // visit the one its keys end in (lim < 32), in the current tiles the first
+  // whose first key passes the workgroup's smallest row position - 31 (from
+  // there on every tile), and no later than the walk's end (every tile
+  // past it is cut).  tn: the tiles before some walker enters its next
+  // region; at 0 the walkers that finished theirs enter the next.
+  auto cut_in = [&](const Walker& w, int v) RA_INLINE {
+    int n = 0;  // past the regions every tile is cut
+    if (w.k < p.P) {
+      n = max(w.lim, 0) / kBKV;
+    } else if (w.k == p.P) {
+      const int d = wg_min_pos - 31 - w.lim;
+      n = d < 0 ? 0 : d / kBKV + 1;
+    }
+    return min(n, T - v);
+  };
+  int nm = 0;                 // tiles before the next cut one (the blocks step it)
+  uint32_t tn = 0, tn0 = 0;   // tiles before a region change; tn0: its value when set
+  if constexpr (ASMBLK) {
+    nm = cut_in(wb_, 0);
+    tn = tn0 = (uint32_t)min(min(wb_.left, wk_.left), wv_.left);
+  }
+  auto region_change = [&](int v) RA_INLINE {  // after tile v: tn reached 0
+    wb_.left -= (int)tn0;
+    wk_.left -= (int)tn0;
+    wv_.left -= (int)tn0;
+    if (wb_.left == 0) {
+      enter(wb_, wb_.k + 1, 0, 0);
+      nm = cut_in(wb_, v + 1);
+    }
+    if (wk_.left == 0) enter(wk_, wk_.k + 1, 0, 0);
+    if (wv_.left == 0) enter(wv_, wv_.k + 1, 0, 1);
+    tn = tn0 = (uint32_t)min(min(wb_.left, wk_.left), wv_.left);
+  };
   // Tile v, in slot SL = v mod 4.
   auto body = [&](auto slot, int v) RA_INLINE {
     constexpr int SL = decltype(slot)::value;
@@ -954,45 +990,34 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       }
     }
     if constexpr (ASM256) {
-      // the block derives the key bound from these and the bound walker's
-      // lim (scalar, in the shadow of its QK^T MFMAs), then steps the three
-      // walkers: lim, the copy offsets and the tiles left in each region
-      const TileBound tb{wb_.k, p.P, wg_min_pos - 31, v, T};
+      // a cut tile's key bound comes from these and the bound walker's lim
+      // (on the mask's path); the block steps lim, the copy offsets and the
+      // counters nm and tn
+      const TileBound tb{wb_.k, p.P, v, T};
 
       // tile v's probabilities go to buffer v & 1; tile v-1's are read
       constexpr int PB = SL & 1;
       // this block's copies: K of tile v + 2 and V of tile v + 1
       const i32x4 dkr = desc_of(wk_), dvr = desc_of(wv_);
-      uint32_t tmin;
       tile_hd256<F32OUT, SL * TILE_B, ((SL + 3) % 4) * TILE_B, PB ^ 1, ((SL + 2) % 4) * TILE_B,
                  VBASE + ((SL + 1) % 4) * TILE_B, ((SL + 1) % 4) * TILE_B>(
           acc, pbuf[0], pbuf[1], qreg, kpre, ka, va, mlog, lsum2[SL & 1], lcomp2[SL & 1],
           lsum2[(SL & 1) ^ 1], lcomp2[(SL & 1) ^ 1], dq, sbnd, alpha, resc, c2, kTau<F32OUT>,
-          kPBound, tb, pos, dkr, dvr, wk_.off, wv_.off, wb_.lim, wb_.dlim, wb_.left, wk_.left,
-          wv_.left, tile_stride, tmin, m0b, dl);
-      // a walker that has finished its region enters the next
-      if (__builtin_expect(tmin == 0, 0)) {
-        if (wb_.left == 0) enter(wb_, wb_.k + 1, 0, 0);
-        if (wk_.left == 0) enter(wk_, wk_.k + 1, 0, 0);
-        if (wv_.left == 0) enter(wv_, wv_.k + 1, 0, 1);
-      }
+          kPBound, tb, pos, dkr, dvr, wk_.off, wv_.off, wb_.lim, wb_.dlim, nm, tn, tile_stride,
+          m0b, dl);
+      if (__builtin_expect(tn == 0, 0)) region_change(v);
     } else if constexpr (ASMPIPE) {
       // block v: scores of tile v, softmax of tile v-1, P.V of tile v-2
-      const TileBound tb{wb_.k, p.P, wg_min_pos - 31, v, T};
+      const TileBound tb{wb_.k, p.P, v, T};
       // this block's copies: K of tile v + 2 and V of tile v
       const i32x4 dkr = desc_of(wk_), dvr = desc_of(wv_);
-      uint32_t tmin;
       tile_pipe<D, SL * TILE_B, ((SL + 2) % 4) * TILE_B, SL & 1, ((SL + 2) % 4) * TILE_B,
                 VBASE + SL * TILE_B, ((SL + 1) % 4) * TILE_B>(
           acc, sc, pbuf[0], pbuf[1], qreg, kpre, ka, va, mlog, lsum2[SL & 1], lcomp2[SL & 1],
           lsum2[(SL & 1) ^ 1], lcomp2[(SL & 1) ^ 1], dq, sbnd, alpha, resc, c2, kTau<F32OUT>,
-          kPBound, tb, pos, dkr, dvr, wk_.off, wv_.off, wb_.lim, wb_.dlim, wb_.left, wk_.left,
-          wv_.left, tile_stride, tmin, m0b, dl);
-      if (__builtin_expect(tmin == 0, 0)) {
-        if (wb_.left == 0) enter(wb_, wb_.k + 1, 0, 0);
-        if (wk_.left == 0) enter(wk_, wk_.k + 1, 0, 0);
-        if (wv_.left == 0) enter(wv_, wv_.k + 1, 0, 1);
-      }
+          kPBound, tb, pos, dkr, dvr, wk_.off, wv_.off, wb_.lim, wb_.dlim, nm, tn, tile_stride,
+          m0b, dl);
+      if (__builtin_expect(tn == 0, 0)) region_change(v);
     } else {
       int lim[NRB];
       bool cut = bounds(wb_, lim);
