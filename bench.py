@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "fused ring attention TFLOP/s + % bf16 MFMA peak; ms/chunk at 32k ctx"
+WARMUP_S = 0.1                 # default warm-up: at least this long (and at least 5 steps)
 
 
 def alg_flops(w):
@@ -171,7 +172,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: at least 5, and as many "
+                         "more as fill 100 ms, so that the clock has settled on short steps)")
     ap.add_argument("--config", default="32k", help="workload name (default: 32k)")
     ap.add_argument("--head-dim", type=int, default=0, choices=(0, 64, 128, 256),
                     help="run the workload's shape at this head dim (0: the workload's own)")
@@ -269,9 +272,20 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
-    for _ in range(args.warmup):
+    # Warm-up.  The engine clock settles over the first ~10 ms of load, which
+    # a few steps of a short workload (a rank share: 0.4 ms) do not cover.
+    n_warm = args.warmup if args.warmup is not None else 5
+    for _ in range(n_warm):
         step()
     torch.cuda.synchronize()
+    if args.warmup is None:
+        t_w = time.perf_counter()
+        while time.perf_counter() - t_w < WARMUP_S:
+            for _ in range(5):
+                step()
+            n_warm += 5
+            torch.cuda.synchronize()
+    args.warmup = n_warm
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
