@@ -11,11 +11,13 @@ Tiles run in pairs (K and V slots t mod 4).  One block, in order:
      the end.  Every two k-steps one LDS-DMA copy of the next tiles is
      issued (8 per block: the wave's rows of one K tile and one V tile), so
      the vector memory pipe drains them in the MFMAs' shadow rather than
-     stalling the wave.  The tile's key bound and the walkers' step to the
-     next tile (offsets, bound, tiles left per region) are scalar ops in
-     the same shadow.
-  2. Only when the tile is cut by a key bound (a uniform flag): the scores
-     of keys at or past each row's bound become -inf.
+     stalling the wave.  The walkers' step to the next tile (copy offsets,
+     key bound, and the two counters the code around the block keeps:
+     tiles before the next cut one, tiles before a region change) is scalar
+     ops in the same shadow.
+  2. Only when the tile is cut by a key bound (the first counter has run
+     out): the tile's bound, then the scores of keys at or past each row's
+     bound become -inf.
   3. O^T += V^T P^T of tile v-1: 32 MFMAs.  After each MFMA an even share
      (by issue cost) of tile v's online softmax is issued.  ASM blocks (bf16
      output): one FMA + exp2 per score against the running max as it
@@ -216,8 +218,6 @@ def qk_part(extra=()):
     per step."""
     # KPRE was read by the block before (or before the loop): wait for it.
     out = ["s_nop 1", "s_waitcnt lgkmcnt(0)"] + dma_setup(0)
-    bound = [walk_ops()]
-    assert len(bound) <= NKS // 2, "one group of scalar ops per even k-step"
     extra = list(extra)
     per = -(-len(extra) // NKS) if extra else 0
     pending = []  # LDS reads in flight, in issue order
@@ -241,8 +241,8 @@ def qk_part(extra=()):
                 out += copy_step_ops()
             else:
                 out += dma_setup(k // 2 + 1)
-        elif k // 2 < len(bound):
-            out += bound[k // 2]
+        elif k == 0:  # the walkers' scalar step
+            out += walk_ops()
         out += extra[k * per:(k + 1) * per]
     return out
 

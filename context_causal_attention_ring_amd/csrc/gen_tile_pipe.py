@@ -183,11 +183,6 @@ def block(g, E):
     half = g.nm // 2
     gaps, per = base.assign(softmax_common(sr, pout), g.nm,
                             [g.qk_weight] * half + [1.0] * half)
-    # scalar groups (here the one of base.walk_ops), one after every
-    # stride-th step of the block's 2 nks steps
-    bound = [base.walk_ops()]
-    stride = 2 * g.nks // len(bound)
-    assert stride * len(bound) == 2 * g.nks
     out = ["s_nop 1", "s_waitcnt lgkmcnt(0)"] + dma_setup(g, 0)
     pending = []  # LDS reads in flight, in issue order
 
@@ -198,7 +193,7 @@ def block(g, E):
         out.append(f"s_waitcnt lgkmcnt({len(pending) - 1 - i})")
         pending = pending[i + 1:]
 
-    m = step = 0
+    m = 0
     for k in range(g.nks):
         if k >= 2:  # this step's K operand (read two steps ahead) must be in
             wait_for(("k", k))
@@ -218,9 +213,8 @@ def block(g, E):
         if k % 2 == 1:  # one copy of the next tiles per two k-steps
             out += dma_issue(g, k // 2)
             out += base.copy_step_ops() if k == g.nks - 1 else dma_setup(g, k // 2 + 1)
-        if step % stride == 0:
-            out += bound[step // stride]
-        step += 1
+        if k == 0:  # the walkers' scalar step, in the first k-step's shadow
+            out += base.walk_ops()
     for t in range(g.nt):
         ks, db = divmod(t, g.ndb)
         wait_for(("v", t, 1))
@@ -236,10 +230,7 @@ def block(g, E):
                     pending += [("v", t + 2, h) for h in (0, 1)]
             out += gaps[m]
             m += 1
-        if step % stride == 0:
-            out += bound[step // stride]
-        step += 1
-    assert m == g.nm and step == 2 * g.nks
+    assert m == g.nm
     tail = [] if even else ["s_waitcnt vmcnt(0)", "s_barrier"] + base.kpre_reads()
     # Common path: no lane's tile sum passed its bound and tile u is not cut.
     out += ["s_cmp_lg_u64 %[any], 0", "s_cbranch_scc1 8f", "10:"] + base.mask_test("7f")
