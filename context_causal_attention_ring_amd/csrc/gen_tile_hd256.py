@@ -285,6 +285,47 @@ def sig_ops(buf):
 DOT_WAIT = 4
 
 
+SCC_READERS = ("s_cselect", "s_cbranch_scc", "s_cmov", "s_addc", "s_subb")
+SCC_WRITERS = ("s_cmp", "s_add_", "s_sub_", "s_and_", "s_or_", "s_xor_", "s_min_", "s_max_",
+               "s_lshl", "s_lshr", "s_ashr", "s_bfe", "s_not", "s_abs", "s_andn2", "s_orn2",
+               "s_nand", "s_nor", "s_xnor", "s_bcnt", "s_absdiff", "s_addc", "s_subb")
+
+
+def check_scc(lines):
+    """Raise unless every instruction that reads SCC finds, as the nearest
+    SCC writer before it (a label ends the search: a branch target starts
+    its own sequence), a compare: no scalar op placed between a compare and
+    its selects (the copies' M0 setup, the walkers' step) may clobber SCC."""
+    last = None
+    for ln in lines:
+        op = ln.split(None, 1)[0] if ln.strip() else ""
+        if op.endswith(":"):
+            last = None
+            continue
+        if op.startswith(SCC_READERS) and last is not None and not last.startswith("s_cmp"):
+            raise AssertionError(f"{ln!r} reads SCC last written by {last!r}")
+        if op.startswith(SCC_WRITERS):
+            last = ln
+
+
+def scc_atomic(ops):
+    """Merge each SALU compare with the ops that read its SCC into one op
+    (lines joined by newlines), so that spreading the ops over MFMA gaps
+    never puts a gap's scalar ops between them; emit with split_ops."""
+    out = []
+    for kind, text in ops:
+        if out and text.startswith(SCC_READERS) and out[-1][1].split("\n")[0].startswith("s_cmp"):
+            out[-1] = (out[-1][0], out[-1][1] + "\n" + text)
+        else:
+            out.append((kind, text))
+    return out
+
+
+def split_ops(texts):
+    """The lines of a gap's ops (undoing scc_atomic's joins)."""
+    return [ln for text in texts for ln in text.split("\n")]
+
+
 def check_dot_hazards(lines):
     """Raise if an instruction other than v_dot2 reads a VGPR a v_dot2
     wrote fewer than DOT_WAIT wait states before (s_nop n counts n + 1;
@@ -308,15 +349,16 @@ def check_dot_hazards(lines):
             pending = [(r, w) for r, w in pending if r != dst.strip()] + [(dst.strip(), 0)]
 
 
-def pack_f32(rb, j, direct):
+def pack_f32(rb, j, direct, src=s):
     """fp32 output: split the probabilities of keys 2j, 2j + 1 of row block
     rb into hi = the bf16 truncation (exact: the upper half of the fp32
     word) and lo = bf16(p - hi), so that hi + lo holds p to about 2^-16
     relative and the P.V MFMAs on both carry no bf16 rounding of the
     weights.  direct: write the hi and lo operands at once (their buffer is
     no longer read); else leave hi packed in the odd score register and lo
-    in the even one for a later move.  a0 and b0 are scratch."""
-    i0, i1 = s(rb, 2 * j), s(rb, 2 * j + 1)
+    in the even one for a later move (src: the score registers).  a0 and b0
+    are scratch."""
+    i0, i1 = src(rb, 2 * j), src(rb, 2 * j + 1)
     hi, lo = (pbreg(0, rb, j), pbreg(1, rb, j)) if direct else (i1, i0)
     return [("valu", f"v_and_b32 %[a0], %[hmask], {i0}"),
             ("valu", f"v_and_b32 %[b0], %[hmask], {i1}"),
@@ -704,6 +746,7 @@ def render():
             out.append(f"// P.V block of variant {name}_P{pin}: about {per:.1f} full-rate VALU issue"
                        " slots of softmax work per MFMA.")
             check_dot_hazards(body)
+            check_scc(body)
             out += macro(f"RA_TILE_HD256_{name}_P{pin}", body)
     q = [f'[q{rb}_{k}] "{{{qop(rb, k)}}}"(q[{rb}][{k}])' for rb in range(NRB) for k in range(NKS)]
     out += operand_list("RA_TILE_HD256_Q_OPERANDS", q)

@@ -250,6 +250,99 @@ def block(g, E):
     return out, per
 
 
+def block_f32(g, E):
+    """Block u with u mod 2 = E at geometry g, fp32 output: the exact-max
+    softmax of tile u-1 (running-max vote, rescale factors; in place on its
+    scores, there is no slow path) and O^T += V^T (P_hi + P_lo)^T of tile
+    u-2, four MFMAs per step (hi and lo of each row block).  As in the
+    HD = 256 fp32 block the probabilities are single-buffered: the step-0
+    hi/lo operands of tile u-1 are packed once the MFMAs reading tile u-2's
+    are done, the step-1 ones into the score registers (free once the
+    softmax has read them) and moved into place after the last MFMA."""
+    sw, sr = E, 1 - E
+    even = E == 0
+    src = sreg(sr)
+    nqk = NRB * g.nks
+    nm = nqk + 2 * NRB * g.nt
+    soft = base.softmax_ops(0, pack=False, src=src)
+    assert soft[0] == ("nop", "s_nop 4")  # the scores are a block old
+    soft = soft[1:]
+    late = [op for rb in range(NRB) for j in range(4, 8)
+            for op in base.pack_f32(rb, j, False, src)]
+    direct = [op for rb in range(NRB) for j in range(4)
+              for op in base.pack_f32(rb, j, True, src)]
+    # the last reader of the step-0 operands is P.V MFMA 4 ndb - 1; they may
+    # be overwritten from the gap four MFMAs after it
+    ks0_free = nqk + 2 * NRB * g.ndb - 1 + 4
+    w = [g.qk_weight] * nqk + [1.0] * (nm - nqk)
+    ca = sum(base.COST[k] for k, _ in soft + late)
+    cd = sum(base.COST[k] for k, _ in direct)
+    g1 = max(ks0_free + 1, round(nm * ca / (ca + cd)))
+    # the vote's compare-and-select chains stay whole: the S^T half's gaps
+    # are followed by the copies' and walkers' scalar ops, which write SCC
+    ga, per = base.assign(base.scc_atomic(soft + late), g1, w[:g1])
+    gd, _ = base.assign(direct, nm - g1, w[g1:])
+    gaps = [base.split_ops(gap) for gap in ga + gd]
+    out = ["s_nop 1", "s_waitcnt lgkmcnt(0)"] + dma_setup(g, 0)
+    pending = []
+
+    def wait_for(tag):
+        nonlocal pending
+        i = pending.index(tag)
+        out.append(f"s_waitcnt lgkmcnt({len(pending) - 1 - i})")
+        pending = pending[i + 1:]
+
+    m = 0
+    for k in range(g.nks):
+        if k >= 2:
+            wait_for(("k", k))
+        for rb in range(NRB):
+            c = "0" if k == 0 else stile(sw, rb)
+            out.append(f"v_mfma_f32_32x32x16_bf16 {stile(sw, rb)}, {kop(k)}, {qop(g, rb, k)}, "
+                       f"{c}")
+            if rb == 0:
+                if k + 2 < g.nks:
+                    out.append(kread(k + 2))
+                    pending.append(("k", k + 2))
+                else:
+                    out += vreads(g, k + 2 - g.nks)
+                    pending += [("v", k + 2 - g.nks, h) for h in (0, 1)]
+            out += gaps[m]
+            m += 1
+        if k % 2 == 1:
+            out += dma_issue(g, k // 2)
+            out += base.copy_step_ops() if k == g.nks - 1 else dma_setup(g, k // 2 + 1)
+        if k == 0:
+            out += base.walk_ops()
+    for t in range(g.nt):
+        ks, db = divmod(t, g.ndb)
+        wait_for(("v", t, 1))
+        for u in range(2 * NRB):
+            buf, rb = divmod(u, NRB)
+            out.append(f"v_mfma_f32_32x32x16_bf16 %[acc{rb}{db}], {base.grp(vgroup(g, t))}, "
+                       f"{base.pbop(buf, rb, ks)}, %[acc{rb}{db}]")
+            if u == 0:
+                if even and t == KPRE_STEP:
+                    out += base.kpre_reads()
+                    pending += [("kp", 0), ("kp", 1)]
+                if t + 2 < g.nt:
+                    out += vreads(g, t + 2)
+                    pending += [("v", t + 2, h) for h in (0, 1)]
+            out += gaps[m]
+            m += 1
+    assert m == nm
+    # the step-1 operands: the last MFMAs read them while they run
+    out += ["s_nop 15", "s_nop 15"]
+    for rb in range(NRB):
+        for j in range(4, 8):
+            out.append(f"v_mov_b32 {base.pbreg(0, rb, j)}, {src(rb, 2 * j + 1)}")
+            out.append(f"v_mov_b32 {base.pbreg(1, rb, j)}, {src(rb, 2 * j)}")
+    tail = [] if even else ["s_waitcnt vmcnt(0)", "s_barrier"] + base.kpre_reads()
+    out += base.mask_test("7f") + ["11:"] + tail + ["s_branch 9f"]
+    out += ["7:"] + base.mask_body(sreg(sw)) + ["s_branch 11b", "9:"]
+    return out, per
+
+
 def offset_operands(g):
     """The block's LDS offsets (immediates, from the slot offsets KOFF, VOFF,
     MK, MV of the asm statement's scope) and the copy lane offsets: K
@@ -267,18 +360,24 @@ def offset_operands(g):
 
 def render(g):
     out = [f"// Generated by gen_tile_pipe.py -- edit the generator, not this file.",
-           f"// One step of the HD = {g.hd} tile loop (bf16 output): S^T = K Q^T of tile u,",
+           f"// One step of the HD = {g.hd} tile loop: S^T = K Q^T of tile u,",
            "// the online softmax of tile u-1 and O^T += V^T P^T of tile u-2, the",
-           f"// softmax spread over all {g.nm} MFMAs.  Variant E<e> is block u with",
-           "// u mod 2 = e: it writes score buffer e, reads score buffer 1 - e,",
-           "// reads probability buffer e and writes buffer 1 - e.  Operands are",
-           "// bound by the asm statement in ring_attn_fused.hip."]
-    for E in (0, 1):
-        body, per = block(g, E)
-        out.append(f"// Block E{E}: about {per:.1f} full-rate VALU issue slots of softmax work"
-                   " per MFMA.")
-        base.check_dot_hazards(body)
-        out += base.macro(f"{g.name}_E{E}", body)
+           "// softmax spread over all the block's MFMAs.  Variant E<e> is block u",
+           "// with u mod 2 = e: it writes score buffer e, reads score buffer 1 - e,",
+           "// reads probability buffer e and writes buffer 1 - e.  Variant F32_E<e>",
+           "// (fp32 output) takes the exact-max softmax and hi + lo probabilities",
+           "// (P.V MFMAs for both), single-buffered in the two probability buffers",
+           "// (hi, lo).  Operands are bound by the asm statement in",
+           "// ring_attn_fused.hip."]
+    for f32 in (False, True):
+        for E in (0, 1):
+            body, per = block_f32(g, E) if f32 else block(g, E)
+            name = f"F32_E{E}" if f32 else f"E{E}"
+            out.append(f"// Block {name}: about {per:.1f} full-rate VALU issue slots of softmax"
+                       " work per MFMA.")
+            base.check_dot_hazards(body)
+            base.check_scc(body)
+            out += base.macro(f"{g.name}_{name}", body)
     q = [f'[q{rb}_{k}] "{{{qop(g, rb, k)}}}"(q[{rb}][{k}])' for rb in range(NRB)
          for k in range(g.nks)]
     out += base.operand_list(f"{g.name}_Q_OPERANDS", q)
@@ -298,6 +397,7 @@ def render(g):
                 for ks in range(NPS)]
         out += base.operand_list(f"{g.name}_PB_IN{buf}", [f'"{{{r}}}"({c})' for r, c in regs])
         out += base.operand_list(f"{g.name}_PB_OUT{buf}", [f'"=&{{{r}}}"({c})' for r, c in regs])
+        out += base.operand_list(f"{g.name}_PB_RW{buf}", [f'"+{{{r}}}"({c})' for r, c in regs])
     clob = [f'"v{r}"' for r in list(range(T0, T0 + 4 * NRB)) + list(range(RING0, RING0 + 12))]
     out += base.operand_list(f"{g.name}_CLOBBERS", clob)
     return "\n".join(out) + "\n"

@@ -325,15 +325,18 @@ __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], bf16x8 (&p0)[2][
 #endif
 }
 
-// One step of the HD = 128 or HD = 64 tile loop, bf16 output (generated by
+// One step of the HD = 128 or HD = 64 tile loop (generated by
 // gen_tile_pipe.py: tile_hd128.inc, tile_hd64.inc; this binds their
 // operands).  Block u computes S^T = K Q^T of tile u (K slot at KOFF, first
 // two operands in kpre) into score buffer sc[E], E = u mod 2; runs the
-// online softmax of tile u-1 on sc[1 - E] (its raw scores stay: the
-// exponentials go to temporaries) into probability buffer 1 - E, with the
-// slow path and the significant-tile correction of the HD = 256 block; and
-// accumulates O^T += V^T P^T of tile u-2 (V slot at VOFF, probability
-// buffer E).  The softmax is spread over all the block's MFMAs.  When tile
+// online softmax of tile u-1 on sc[1 - E]; and accumulates O^T += V^T P^T
+// of tile u-2 (V slot at VOFF).  bf16 output: the softmax of the HD = 256
+// block (raw scores kept: the exponentials go to temporaries, so the slow
+// path needs no second S^T; the significant-tile correction) into
+// probability buffer 1 - E, while P.V reads buffer E.  fp32 output (F32):
+// the exact-max softmax in place and hi + lo probabilities, single-buffered
+// in p0 (hi) and p1 (lo) as in the HD = 256 fp32 block, four P.V MFMAs per
+// step.  The softmax is spread over all the block's MFMAs.  When tile
 // u is cut by a key bound its scores are masked at the end of the block,
 // for the next one.  Copies: the wave's rows of K tile u + 2 (to MK) and V
 // tile u (to MV), D / 64 instructions each; copy b of wave w moves the 1024
@@ -361,7 +364,17 @@ __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], bf16x8 (&p0)[2][
                : RA_TILE_HD##HD##_Q_OPERANDS, RA_TILE_HD##HD##_##PIN, RA_TILE_INPUT_OPERANDS,   \
                  RA_TILE_HD##HD##_OFFSET_OPERANDS, [one2] "s"(one2)                             \
                : RA_TILE_HD##HD##_CLOBBERS, "memory", "scc", "m0")
-template <int D, uint32_t KOFF, uint32_t VOFF, int E, uint32_t MK, uint32_t MV, uint32_t KPO>
+// fp32 output: hi and lo probabilities both read and rewritten, no dq / bound
+#define RA_TILE_PIPE_F32_ASM(HD, E, SOUT, SRW)                                                 \
+  asm volatile(RA_TILE_HD##HD##_F32_E##E                                                        \
+               : RA_TILE_STATE_OPERANDS, RA_TILE_HD##HD##_ACC_OPERANDS,                         \
+                 RA_TILE_HD##HD##_KPRE_OPERANDS, RA_TILE_HD##HD##_PB_RW0,                       \
+                 RA_TILE_HD##HD##_PB_RW1, RA_TILE_HD##HD##_##SOUT, RA_TILE_HD##HD##_##SRW        \
+               : RA_TILE_HD##HD##_Q_OPERANDS, RA_TILE_INPUT_OPERANDS,                           \
+                 RA_TILE_HD##HD##_OFFSET_OPERANDS, [hmask] "s"(hmask), [psel] "s"(psel)         \
+               : RA_TILE_HD##HD##_CLOBBERS, "memory", "scc", "m0")
+template <int D, bool F32, uint32_t KOFF, uint32_t VOFF, int E, uint32_t MK, uint32_t MV,
+          uint32_t KPO>
 __device__ __forceinline__ void tile_pipe(f32x16 (&acc)[2][D / 32], f32x16 (&sc)[2][2],
                                           bf16x8 (&p0)[2][2], bf16x8 (&p1)[2][2],
                                           const bf16x8 (&q)[2][D / 16], bf16x8 (&kpre)[2],
@@ -382,7 +395,17 @@ __device__ __forceinline__ void tile_pipe(f32x16 (&acc)[2][D / 32], f32x16 (&sc)
   uint64_t c0, c1, any;
   const float ninf = kNegInf;
   const uint32_t one2 = 0x3F803F80u;  // bf16 pair (1, 1): v_dot2 sums a packed pair
-  if constexpr (D == 128 && E == 0) {
+  const uint32_t hmask = 0xFFFF0000u;  // the bf16 truncation of an fp32 word
+  const uint32_t psel = 0x07060302u;   // v_perm: the upper halves of two words
+  if constexpr (F32 && D == 128 && E == 0) {
+    RA_TILE_PIPE_F32_ASM(128, 0, S_OUT0, S_RW1);
+  } else if constexpr (F32 && D == 128) {
+    RA_TILE_PIPE_F32_ASM(128, 1, S_OUT1, S_RW0);
+  } else if constexpr (F32 && E == 0) {
+    RA_TILE_PIPE_F32_ASM(64, 0, S_OUT0, S_RW1);
+  } else if constexpr (F32) {
+    RA_TILE_PIPE_F32_ASM(64, 1, S_OUT1, S_RW0);
+  } else if constexpr (D == 128 && E == 0) {
     RA_TILE_PIPE_ASM(128, 0, S_OUT0, S_RW1, PB_OUT1, PB_IN0);
   } else if constexpr (D == 128) {
     RA_TILE_PIPE_ASM(128, 1, S_OUT1, S_RW0, PB_OUT0, PB_IN1);
@@ -394,6 +417,7 @@ __device__ __forceinline__ void tile_pipe(f32x16 (&acc)[2][D / 32], f32x16 (&sc)
 #endif
 }
 #undef RA_TILE_PIPE_ASM
+#undef RA_TILE_PIPE_F32_ASM
 #undef RA_TILE_STATE_OPERANDS
 #undef RA_TILE_LQ_OPERANDS
 #undef RA_TILE_INPUT_OPERANDS
@@ -411,11 +435,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   constexpr uint32_t TILE_B = TILE * 2;   // bytes of one K or V tile
   constexpr int DPW = kBKV * CPR / (64 * kWaves);  // DMA instructions per wave per tile
   static_assert(DPW >= 1 && DPW * 64 * kWaves == kBKV * CPR, "tile must split over the waves");
-  // hand-scheduled tile bodies: HD = 256 (both output types), the
-  // three-tile blocks at HD = 128 and 64 (bf16 output; fp32 output there
-  // runs the compiler-scheduled loop)
+  // hand-scheduled tile bodies: HD = 256 (one tile per block) and the
+  // three-tile blocks at HD = 128 and 64, both output types
   constexpr bool ASM256 = D == 256 && NRB == 2 && NKB == 1;
-  constexpr bool ASMPIPE = (D == 128 || D == 64) && !F32OUT && NRB == 2 && NKB == 1;
+  constexpr bool ASMPIPE = (D == 128 || D == 64) && NRB == 2 && NKB == 1;
   constexpr bool ASMBLK = ASM256 || ASMPIPE;
   // LDS: K slots 0..3 then V slots 0..3 (tile t in slot t mod 4).  Slot
   // offsets are compile-time constants because the tile loop is unrolled
@@ -1011,8 +1034,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
       const TileBound tb{wb_.k, p.P, v, T};
       // this block's copies: K of tile v + 2 and V of tile v
       const i32x4 dkr = desc_of(wk_), dvr = desc_of(wv_);
-      tile_pipe<D, SL * TILE_B, ((SL + 2) % 4) * TILE_B, SL & 1, ((SL + 2) % 4) * TILE_B,
-                VBASE + SL * TILE_B, ((SL + 1) % 4) * TILE_B>(
+      tile_pipe<D, F32OUT, SL * TILE_B, ((SL + 2) % 4) * TILE_B, SL & 1,
+                ((SL + 2) % 4) * TILE_B, VBASE + SL * TILE_B, ((SL + 1) % 4) * TILE_B>(
           acc, sc, pbuf[0], pbuf[1], qreg, kpre, ka, va, mlog, lsum2[SL & 1], lcomp2[SL & 1],
           lsum2[(SL & 1) ^ 1], lcomp2[(SL & 1) ^ 1], dq, sbnd, alpha, resc, c2, kTau<F32OUT>,
           kPBound, tb, pos, dkr, dvr, wk_.off, wv_.off, wb_.lim, wb_.dlim, nm, tn, tile_stride,
