@@ -3,7 +3,16 @@ row: head dims, GQA groups, shard counts, stripe units, first shards, cache
 lengths (none, short, unaligned), head/tail pieces at arbitrary chunk
 positions, pad rows, pad current tokens, split counts and both output
 dtypes, drawn together so that combinations the hand-written cases do not
-name are covered too."""
+name are covered too.  RINGATTN_RANDOM_CASES=N runs N configurations of the
+same draw instead of the default 24 (a wider sweep).
+
+A second draw takes long walks: caches of up to 40000 tokens in up to 64
+shards, up to 1400 chunk rows (several row tiles per KV head), splits up to
+16.  Those are checked on sampled rows (the ends of each piece, the real/pad
+edge and seeded random rows); RINGATTN_RANDOM_LARGE_CASES=N runs N of them
+instead of the default 6."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -11,30 +20,33 @@ import torch
 import context_causal_attention_ring_amd as ra
 import oracle
 import workloads
-from helpers import Case
+from helpers import Case, sample_rows
 from test_gpu_parity import (SENTINEL, TOL_BF16, TOL_F32, check_pads_untouched, compare,
                              run_split)
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 24
+N_CASES = int(os.environ.get("RINGATTN_RANDOM_CASES", "24"))
+N_LARGE = int(os.environ.get("RINGATTN_RANDOM_LARGE_CASES", "6"))
 
 
-def draw(i):
-    """Configuration i, a pure function of i (numpy's seeded generator)."""
-    g = np.random.default_rng(1000 + i)
+def draw(i, large=False):
+    """Configuration i, a pure function of i (numpy's seeded generator);
+    large: the long-walk draw."""
+    g = np.random.default_rng((5000 if large else 1000) + i)
     hd = int(g.choice([64, 128, 256]))
-    nkv = int(g.choice([1, 2, 3, 4]))
-    group = int(g.choice([1, 2, 3, 4, 8, 16]))
-    while nkv * group > 16:
+    nkv = int(g.choice([1, 2] if large else [1, 2, 3, 4]))
+    group = int(g.choice([1, 4, 8, 16] if large else [1, 2, 3, 4, 8, 16]))
+    while nkv * group > (32 if large else 16):
         group //= 2
-    P = int(g.integers(1, 10))
-    interleave = int(g.choice([1, 1, 1, 2, 7, 16]))
-    cache_len = 0 if g.random() < 0.2 else int(g.integers(1, 2500))
-    head_rows = int(g.integers(0, 120))
-    tail_rows = int(g.integers(0 if head_rows else 1, 120))
-    head_pos = int(g.integers(0, 200))
-    tail_pos = head_pos + head_rows + int(g.integers(0, 200))
+    P = int(g.choice([1, 2, 3, 8, 13, 64])) if large else int(g.integers(1, 10))
+    interleave = int(g.choice([1, 1, 4, 16, 64] if large else [1, 1, 1, 2, 7, 16]))
+    max_cache, max_rows, max_gap = (40000, 700, 2000) if large else (2500, 120, 200)
+    cache_len = 0 if g.random() < (0.1 if large else 0.2) else int(g.integers(1, max_cache))
+    head_rows = int(g.integers(0, max_rows))
+    tail_rows = int(g.integers(0 if head_rows else 1, max_rows))
+    head_pos = int(g.integers(0, max_gap))
+    tail_pos = head_pos + head_rows + int(g.integers(0, max_gap))
     q_rows = head_rows + tail_rows
     # pads only at the end of the rows: a partly real tail needs a full head
     real_rows = int(g.integers(0, q_rows + 1)) if g.random() < 0.5 else q_rows
@@ -48,12 +60,12 @@ def draw(i):
     cur_len = max(last + 1, 1) + int(g.integers(0, 40))
     cur_real = max(last + 1, 0) + int(g.integers(0, cur_len - max(last + 1, 0) + 1))
     cap = max(oracle.shard_lengths(cache_len, P, interleave) + [1])
-    w = workloads.custom(f"rand{i}", seed=2000 + i, nq=nkv * group, nkv=nkv, hd=hd,
+    w = workloads.custom(f"{'large' if large else 'rand'}{i}", seed=(6000 if large else 2000) + i, nq=nkv * group, nkv=nkv, hd=hd,
                          cache_len=cache_len, P=P, head_rows=head_rows, tail_rows=tail_rows,
                          real_rows=real_rows, shard_cap=cap, interleave=interleave,
                          head_pos=head_pos, tail_pos=tail_pos, cur_len=cur_len,
                          cur_real=cur_real)
-    splits = int(g.choice([1, 1, 1, 2, 3, 5]))
+    splits = int(g.choice([1, 2, 4, 7, 16] if large else [1, 1, 1, 2, 3, 5]))
     fp32 = bool(g.random() < 0.3)
     ring_start = int(g.integers(0, P))
     return w, splits, fp32, ring_start
@@ -73,6 +85,20 @@ def test_random_configuration_matches_oracle(i):
     check_pads_untouched(case, out, lse)
 
 
+@pytest.mark.parametrize("i", range(N_LARGE))
+def test_random_long_walk_matches_oracle(i):
+    w, splits, fp32, ring_start = draw(i, large=True)
+    print(f"[gpu] long-walk config {i}: NQ={w.nq} NKV={w.nkv} HD={w.hd} L={w.cache_len} "
+          f"P={w.P} I={w.interleave} start={ring_start} head={w.head_rows}@{w.head_pos} "
+          f"tail={w.tail_rows}@{w.tail_start} real={w.real_rows} cur={w.n_cur}/{w.n_cur_real} "
+          f"splits={splits} fp32={fp32}", flush=True)
+    case = Case(w).to_device()
+    out, lse = run_split(case, splits, out_fp32=fp32, ring_start=ring_start)
+    if w.real_rows:
+        compare(case, out, lse, sample_rows(w, 48, seed=i), TOL_F32 if fp32 else TOL_BF16)
+    check_pads_untouched(case, out, lse)
+
+
 def test_random_configurations_are_varied():
     """The draw covers what it claims (a check of the generator, on the CPU
     side of the same file)."""
@@ -83,3 +109,6 @@ def test_random_configurations_are_varied():
     assert any(w.real_rows < w.q_rows for w, *_ in ws)
     assert any(w.interleave > 1 for w, *_ in ws) and any(r > 0 for *_, r in ws)
     assert any(w.n_cur_real < w.n_cur for w, *_ in ws)
+    large = [draw(i, large=True) for i in range(N_LARGE)]
+    assert any(w.cache_len > 10000 for w, *_ in large) and any(s > 1 for _, s, _, _ in large)
+    assert any(w.real_rows * (w.nq // w.nkv) > 256 for w, *_ in large)
