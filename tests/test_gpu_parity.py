@@ -435,7 +435,7 @@ def test_rank_shares_reassemble_the_chunk():
 
 # ---------------------------------------------------------------- two-launch comparator
 
-def run_partial(case, regions, out_fp32=True):
+def run_partial(case, regions, out_fp32=True, ring_start=0):
     w, d = case.w, case.d
     C, NQ, HD = w.q_rows, w.nq, w.hd
     out = torch.full((C, NQ, HD), SENTINEL, device="cuda",
@@ -446,7 +446,8 @@ def run_partial(case, regions, out_fp32=True):
                         head_pos=w.head_pos, tail_pos=w.tail_start)
     print(f"[gpu] ring_attn_partial {w.name} regions={regions} C={C} L={w.cache_len}", flush=True)
     ra.ring_attn_partial(d["q"], d["k_cache"], d["v_cache"], d["k_cur"], d["v_cur"], w.cache_len,
-                         w.P, ra.StripeLayout(w.interleave, 0), regions, out, lse, dims)
+                         w.P, ra.StripeLayout(w.interleave, ring_start), regions, out, lse,
+                         dims)
     torch.cuda.synchronize()
     return out, lse, dims
 

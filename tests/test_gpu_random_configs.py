@@ -17,7 +17,14 @@ write of a random number of the chunk's tokens inside the attention launch
 (split or not): bit for bit what the write followed by the attention
 gives, the cache against the oracle's write, the attention against the
 oracle; RINGATTN_RANDOM_WRITE_CASES=N runs N of them instead of the
-default 8."""
+default 8.
+
+A fourth set runs the two-launch comparator on configurations of the first
+draw: the cache-only and current-only launches against the oracle's
+one-region attention, their LSE merge against the merge's definition on
+the same partials, and with fp32 partials the merged result against the
+full attention; RINGATTN_RANDOM_PARTIAL_CASES=N runs N of them instead of
+the default 8."""
 import os
 
 import numpy as np
@@ -28,14 +35,15 @@ import context_causal_attention_ring_amd as ra
 import oracle
 import workloads
 from helpers import Case, bits, sample_rows
-from test_gpu_parity import (SENTINEL, TOL_BF16, TOL_F32, check_pads_untouched, compare,
-                             run_split)
+from test_gpu_parity import (SENTINEL, TOL_BF16, TOL_F32, TOL_LSE, check_pads_untouched,
+                             compare, peaky_bf16_tol, run_partial, run_split)
 
 pytestmark = pytest.mark.gpu
 
 N_CASES = int(os.environ.get("RINGATTN_RANDOM_CASES", "24"))
 N_LARGE = int(os.environ.get("RINGATTN_RANDOM_LARGE_CASES", "6"))
 N_WRITE = int(os.environ.get("RINGATTN_RANDOM_WRITE_CASES", "8"))
+N_PARTIAL = int(os.environ.get("RINGATTN_RANDOM_PARTIAL_CASES", "8"))
 
 
 def draw(i, large=False):
@@ -69,7 +77,8 @@ def draw(i, large=False):
     cur_real = max(last + 1, 0) + int(g.integers(0, cur_len - max(last + 1, 0) + 1))
     cap = max(oracle.shard_lengths(cache_len, P, interleave) + [1])
     name, seed = (f"large{i}", 6000 + i) if large else (f"rand{i}", 2000 + i)
-    w = workloads.custom(name, seed=seed, nq=nkv * group, nkv=nkv, hd=hd, cache_len=cache_len, P=P, head_rows=head_rows, tail_rows=tail_rows,
+    w = workloads.custom(name, seed=seed, nq=nkv * group, nkv=nkv, hd=hd, cache_len=cache_len,
+                         P=P, head_rows=head_rows, tail_rows=tail_rows,
                          real_rows=real_rows, shard_cap=cap, interleave=interleave,
                          head_pos=head_pos, tail_pos=tail_pos, cur_len=cur_len,
                          cur_real=cur_real)
@@ -169,6 +178,59 @@ def test_random_fused_write_matches_write_then_attention(i):
     if w.real_rows:
         compare(case, out, lse, list(range(w.real_rows)), TOL_F32 if fp32 else TOL_BF16)
     check_pads_untouched(case, out, lse)
+
+
+@pytest.mark.parametrize("i", range(N_PARTIAL))
+def test_random_partials_and_merge(i):
+    w, _, parts_fp32, ring_start = draw(6000 + i)
+    out_fp32 = bool(np.random.default_rng(11000 + i).random() < 0.5)
+    print(f"[gpu] partial config {i}: NQ={w.nq} NKV={w.nkv} HD={w.hd} L={w.cache_len} P={w.P} "
+          f"I={w.interleave} start={ring_start} head={w.head_rows}@{w.head_pos} "
+          f"tail={w.tail_rows}@{w.tail_start} real={w.real_rows} cur={w.n_cur}/{w.n_cur_real} "
+          f"parts_fp32={parts_fp32} out_fp32={out_fp32}", flush=True)
+    case = Case(w).to_device()
+    o1, l1, _ = run_partial(case, ra.RA_REGION_CACHE, parts_fp32, ring_start)
+    o2, l2, _ = run_partial(case, ra.RA_REGION_CURRENT, parts_fp32, ring_start)
+    out = torch.full((w.q_rows, w.nq, w.hd), SENTINEL, device="cuda",
+                     dtype=torch.float32 if out_fp32 else torch.bfloat16)
+    lse = torch.full((w.nq, w.q_rows), SENTINEL, device="cuda", dtype=torch.float32)
+    ra.merge_attn_states(o1, l1, o2, l2, out, lse, ra.make_dims(
+        case.d["q"], case.d["k_cur"], w.shard_cap, real_rows=w.real_rows,
+        head_rows=w.head_rows, out_fp32=out_fp32))
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu()
+    check_pads_untouched(case, out, lse)
+    if not w.real_rows:
+        return
+    rows = list(range(w.real_rows))
+    t = case.t
+    args = (t["q"].float().numpy(), t["k_cache_tok"].float().numpy(),
+            t["v_cache_tok"].float().numpy(), t["k_cur"].float().numpy(),
+            t["v_cur"].float().numpy(), rows, w.scale)
+    tol = TOL_F32 if parts_fp32 else TOL_BF16
+    parts = []
+    for o, l, only in ((o1, l1, dict(current=False)), (o2, l2, dict(cache=False))):
+        r, rl = oracle.attention_rows(*args, positions=w.positions, **only)
+        o, l = o.cpu().double().numpy()[rows], l.cpu().double().numpy()[:, rows]
+        fin = np.isfinite(rl)
+        print(f"    partial {only} max|d out|={np.abs(o - r).max():.3e} (<= {tol})", flush=True)
+        assert np.abs(o - r).max() <= tol
+        assert (np.isneginf(l) == ~fin).all()
+        if fin.any():
+            assert np.abs(l[fin] - rl[fin]).max() <= TOL_LSE
+        parts += [o, l]
+    # the merge kernel against the merge's definition on these very partials:
+    # what is left is the output's own rounding (reading of the bf16 bar for
+    # outputs of 2 and more, as for the peaky inputs)
+    om, lm = oracle.two_pass_merge(*parts)
+    d = np.abs(out.double().numpy()[rows] - om)
+    bar = TOL_F32 if out_fp32 else peaky_bf16_tol(om)
+    print(f"    merge of the partials max|d out|={d.max():.3e} max|d|/bar={np.max(d / bar):.3f}",
+          flush=True)
+    assert (d <= bar).all()
+    assert np.abs(lse.double().numpy()[:, rows] - lm).max() <= TOL_LSE
+    if parts_fp32:  # and the whole against the oracle's full attention
+        compare(case, out, lse, rows, TOL_F32 if out_fp32 else TOL_BF16)
 
 
 def test_random_configurations_are_varied():
