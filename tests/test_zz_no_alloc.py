@@ -2,7 +2,10 @@
 caller workspace: the same kernels on the same inputs, so the results must
 be bit-identical; two calls in a row, the second smaller than the first (the
 library's workspace keeps the first call's partials, which must not leak
-into the second), and the second also against the oracle."""
+into the second), and the second also against the oracle; then a run of
+seeded random configurations, one call after another on the same
+workspace, each bit-identical to the caller-workspace call and within the
+bar of the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -10,18 +13,20 @@ import torch
 import context_causal_attention_ring_amd as ra
 import workloads
 from helpers import Case
-from test_gpu_parity import FULL_CASES, SENTINEL, TOL_F32, check_pads_untouched, compare
+from test_gpu_parity import (FULL_CASES, SENTINEL, TOL_BF16, TOL_F32, check_pads_untouched,
+                             compare)
+from test_gpu_random_configs import draw
 
 pytestmark = pytest.mark.gpu
 
 
-def both(case, splits, out_fp32):
+def both(case, splits, out_fp32, ring_start=0):
     """(noalloc out, lse), (workspace out, lse) for one case."""
     w, d = case.w, case.d
     dims = ra.make_dims(d["q"], d["k_cur"], w.shard_cap, real_rows=w.real_rows,
                         head_rows=w.head_rows, scale=w.scale, out_fp32=out_fp32,
                         head_pos=w.head_pos, tail_pos=w.tail_start)
-    layout = ra.StripeLayout(w.interleave, 0)
+    layout = ra.StripeLayout(w.interleave, ring_start)
     dt = torch.float32 if out_fp32 else torch.bfloat16
     res = []
     for noalloc in (True, False):
@@ -55,3 +60,21 @@ def test_noalloc_split_matches_workspace_split_twice():
     assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
     compare(small, o1, l1, list(range(small.w.real_rows)), TOL_F32)
     check_pads_untouched(small, o1, l1)
+
+
+def test_noalloc_split_random_sequence():
+    """Twelve seeded random configurations (splits 2 to 16), one after
+    another: each call finds the previous call's partials in the workspace."""
+    for i in range(12):
+        w, _, fp32, ring_start = draw(8000 + i)
+        splits = int(np.random.default_rng(12000 + i).choice([2, 3, 5, 16]))
+        print(f"[gpu] noalloc random {i}: NQ={w.nq} NKV={w.nkv} HD={w.hd} L={w.cache_len} "
+              f"P={w.P} I={w.interleave} start={ring_start} real={w.real_rows} "
+              f"splits={splits} fp32={fp32}", flush=True)
+        case = Case(w).to_device()
+        (o1, l1), (o2, l2) = both(case, splits, fp32, ring_start)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+        assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+        if w.real_rows:
+            compare(case, o1, l1, list(range(w.real_rows)), TOL_F32 if fp32 else TOL_BF16)
+        check_pads_untouched(case, o1, l1)
