@@ -369,8 +369,8 @@ def pack_f32(rb, j, direct, src=s):
 
 
 def mask_part(src=s):
-    """Keys at or past the row's bound -> -inf, only when the flag is set
-    (src: the score registers, (rb, i) -> name).
+    """Keys at or past the row's bound -> -inf, only on a cut tile (the cut
+    counter nm has run below 0; src: the score registers, (rb, i) -> name).
     The bound of row block rb is lc (a visit's keys left, lm = 0) or
     pos_rb + lc (current tiles, lm = 1: lc = 1 - first key's position).
     Lane half h holds keys 8 (i / 4) + 4 h + i % 4 of the tile; with lim =

@@ -35,7 +35,10 @@
 //    adds and build a descriptor only on entering the next region.
 //    Rows are stored with a 16-byte-chunk XOR swizzle chosen per operand so
 //    that K reads (32 rows, one chunk) and transposed V reads
-//    (ds_read_b64_tr_b16, 4 rows x 4 chunks) are both bank-conflict free.
+//    (ds_read_b64_tr_b16, 4 rows x 4 chunks) are both bank-conflict free at
+//    HD = 256 and 128.  At HD = 64 a row has 8 chunks and the K reads meet
+//    some conflicts; they wait behind the MFMAs (a conflict-free pattern
+//    for that case timed no faster).
 //  * Fetches go through buffer descriptors whose size is the valid length
 //    of the visited region: rows past a shard's length (or past the real
 //    chunk rows) come back as zeros without touching memory -- the
@@ -187,9 +190,9 @@ __device__ __forceinline__ float wave_max_pair(float x) {
 
 // One 32-key tile at HD = 256 as a single instruction block (generated:
 // tile_hd256.inc; this binds its operands).  In order: S^T = K Q^T of tile
-// v from the K slot at KOFF, its first two operands already in kpre; if
-// mflag, scores of keys at or past each row's bound (lim = bound - 4 h)
-// become -inf; then O^T += V^T P^T of tile v-1 (V slot at VOFF, bf16
+// v from the K slot at KOFF, its first two operands already in kpre; if a
+// key bound cuts the tile (the counter nm below ran out), scores of keys at
+// or past each row's bound become -inf; then O^T += V^T P^T of tile v-1 (V slot at VOFF, bf16
 // probabilities pin) with tile v's online softmax in the MFMAs' shadow.  The
 // even tile of a pair (PIN = 1) reads the odd tile's kpre from the K slot at
 // KPO during its P.V; the odd tile (PIN = 0) ends with the pair's wait for
