@@ -20,7 +20,11 @@
  *   - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is
  *     the default stream).  They do not synchronise the host, allocate, or
  *     copy host to device, and keep no pointer after returning; buffers must
- *     stay alive until the stream has run the work.
+ *     stay alive until the stream has run the work.  A call puts only kernel
+ *     launches on the stream (no memset, no copy), so it may be captured into
+ *     a HIP graph, which reads the buffers at each replay.  Apart from
+ *     ring_attn_prefill_split_noalloc, calls share no device state, and
+ *     calls on different streams may run concurrently.
  *   - Every argument is validated on the host before any HIP call.  On error
  *     nothing is launched, a non-zero ra_status_t is returned and
  *     ra_last_error() describes it.  Launch failures return RA_ERR_HIP.
