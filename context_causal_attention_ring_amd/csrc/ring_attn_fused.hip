@@ -1165,8 +1165,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   if (p.write_tokens > 0) {
     const int64_t t0 = (int64_t)logical * p.write_per_wg;
     const int64_t t1 = min((int64_t)p.write_tokens, t0 + p.write_per_wg);
-    for (int64_t idx = t0 * p.write_chunks + threadIdx.x; idx < t1 * p.write_chunks;
-         idx += blockDim.x) {
+    // the thread's index from the wave id (an SGPR) and the lane id, as in
+    // the epilogue: keeping threadIdx.x in a VGPR across the walk would
+    // spill it
+    const int tid_w = wave * 64 + lane_e;
+    for (int64_t idx = t0 * p.write_chunks + tid_w; idx < t1 * p.write_chunks;
+         idx += kWaves * 64) {
       const int64_t t = idx / p.write_chunks;
       const int c = (int)(idx - t * p.write_chunks);
       const int64_t pos = p.write_pos0 + t;

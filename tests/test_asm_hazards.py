@@ -162,6 +162,31 @@ def test_compiler_code_never_uses_m0(extra):
         assert not bad, f"{name}: compiler code uses M0: {bad[:4]}"
 
 
+def scratch_use(asm):
+    """(kernel, private segment bytes, VGPR spills) of every fused kernel."""
+    out = []
+    for name, body in re.findall(r"\.amdhsa_kernel (\S*fused_kernel\S*)(.*?)\.end_amdhsa_kernel",
+                                 asm, re.S):
+        seg = int(re.search(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", body).group(1))
+        out.append((name, seg))
+    spills = [int(x) for x in re.findall(r"\.vgpr_spill_count:\s+(\d+)", asm)]
+    return out, spills
+
+
+@pytest.mark.skipif(not HAS_HIPCC, reason="needs hipcc to assemble the kernel")
+@pytest.mark.parametrize("extra", [(), ("-DRA_SYNC_EVERY_TILE",)], ids=["product", "checking"])
+def test_fused_kernels_use_no_scratch(extra):
+    """Every register of the fused kernels is spoken for during the walk, so
+    a value the compiler keeps live across it spills to scratch memory; none
+    may (values needed after the walk are derived again there)."""
+    with tempfile.TemporaryDirectory() as tmp:
+        asm = open(build.assemble(out=os.path.join(tmp, "fused.s"), extra=extra)).read()
+    segs, spills = scratch_use(asm)
+    assert len(segs) == 6
+    assert all(seg == 0 for _, seg in segs), segs
+    assert spills and all(n == 0 for n in spills), spills
+
+
 def test_m0_check_has_teeth():
     """The M0 check flags explicit and implicit users, and passes plain code."""
     assert m0_users(["s_mov_b32 m0, s4", "s_sendmsg sendmsg(MSG_INTERRUPT)",
