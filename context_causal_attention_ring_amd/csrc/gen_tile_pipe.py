@@ -46,6 +46,7 @@ so the last tile's P.V comes out of the final block.
 Usage: python gen_tile_pipe.py            (rewrites both .inc files)
        python gen_tile_pipe.py --check    (exit 1 if one is stale)
 """
+import contextlib
 import os
 import sys
 
@@ -55,13 +56,23 @@ import gen_tile_hd256 as base  # noqa: E402  (softmax, mask, walker and hazard h
 
 NPS = 2            # 16-key steps of P.V per 32-key tile
 NRB = base.NRB     # 32-row blocks per wave
+# The register map of the geometry being written (see Geometry and regmap):
 Q0 = 44            # Q^T operands (pinned): row block rb, k-step k -> v[Q0 + 4 NKS rb + 4 k : +3]
 S0 = (108, 140)    # score buffers (pinned): buffer b, row block rb, key slot i -> v[S0[b] + 16 rb + i]
 T0 = 204           # exponentials (clobbered): row block rb, key slot i -> v[T0 + 4 rb + i % 4]
 PB = base.PB       # bf16 probabilities (pinned), two buffers, as at HD = 256
-KPRE = base.KPRE   # K operands of k-steps 0 and 1 (pinned), read ahead
+KPRE = base.KPRE   # K operands of k-steps 0 and 1 (pinned), read ahead; None: read in the block
 RING0 = base.RING0  # operand ring (clobbered)
 KPRE_STEP = 2      # P.V step of an even block after which the next tile's KPRE is read
+# HD = 128: the HD = 256 map (one wave per SIMD, 512 registers).  HD = 64:
+# two workgroups per CU, so a wave has 256 registers, 64 of them the
+# accumulator's AGPRs: everything pinned or clobbered fits v[44:191], and
+# the first two K operands are read at the start of each block instead of
+# ahead (the other wave on the SIMD covers their latency).
+REGMAPS = {
+    128: dict(Q0=44, S0=(108, 140), T0=204, PB=base.PB, KPRE=base.KPRE, RING0=base.RING0),
+    64: dict(Q0=44, S0=(76, 108), T0=172, PB=(140, 156), KPRE=None, RING0=180),
+}
 # Softmax share of an MFMA gap in the S^T half relative to the P.V half: the
 # S^T half also carries the copies and the walkers' scalar step (HD = 128:
 # 0.7 measured 0.2-1.5 % faster than an even split on gfx950, 1.3 slower).
@@ -82,9 +93,32 @@ class Geometry:
         self.qk_weight = QK_WEIGHT[hd]
         self.name = f"RA_TILE_HD{hd}"
         self.out = os.path.join(HERE, f"tile_hd{hd}.inc")
+        self.regs = REGMAPS[hd]
+        r = self.regs
         assert self.nt == self.nks and 2 * self.ncopy == self.nks // 2
-        assert Q0 + 4 * self.nks * NRB <= S0[0] and S0[1] + 32 <= PB[0]
-        assert PB[1] + 16 <= T0 and T0 + 4 * NRB <= KPRE
+        assert r["Q0"] + 4 * self.nks * NRB <= r["S0"][0] and r["S0"][1] + 32 <= r["PB"][0]
+        assert r["PB"][1] + 16 <= r["T0"] and r["PB"][0] + 16 <= r["PB"][1]
+        top = r["T0"] + 4 * NRB
+        if r["KPRE"] is not None:
+            assert top <= r["KPRE"]
+            top = r["KPRE"] + 8
+        assert top <= r["RING0"] and r["RING0"] + 12 <= 256
+        self.top = r["RING0"] + 12  # VGPRs the blocks pin or clobber end here
+
+
+@contextlib.contextmanager
+def regmap(g):
+    """Geometry g's register map in force: the helpers of this module and
+    of gen_tile_hd256 read these constants when they are called."""
+    mine = {k: globals()[k] for k in g.regs}
+    theirs = (base.PB, base.RING0)
+    globals().update(g.regs)
+    base.PB, base.RING0 = g.regs["PB"], g.regs["RING0"]
+    try:
+        yield
+    finally:
+        globals().update(mine)
+        base.PB, base.RING0 = theirs
 
 
 def sreg(buf):
@@ -125,8 +159,25 @@ def kread(k):
 
 
 def kop(k):
-    """K operand of k-step k: the first two were read ahead into KPRE."""
-    return f"%[kp{k}]" if k < 2 else base.grp(kgroup(k))
+    """K operand of k-step k: the first two were read ahead into KPRE (when
+    the map has it)."""
+    return f"%[kp{k}]" if k < 2 and KPRE is not None else base.grp(kgroup(k))
+
+
+def block_start(g):
+    """The block's first instructions and the LDS reads they leave in
+    flight: without KPRE the first two K operands are read here."""
+    out = ["s_nop 1", "s_waitcnt lgkmcnt(0)"]
+    pending = []
+    if KPRE is None:
+        out += [kread(0), kread(1)]
+        pending = [("k", 0), ("k", 1)]
+    return out + dma_setup(g, 0), pending
+
+
+def kpre_reads():
+    """The next tile's KPRE reads (none without KPRE)."""
+    return base.kpre_reads() if KPRE is not None else []
 
 
 def vreads(g, t):
@@ -183,8 +234,7 @@ def block(g, E):
     half = g.nm // 2
     gaps, per = base.assign(softmax_common(sr, pout), g.nm,
                             [g.qk_weight] * half + [1.0] * half)
-    out = ["s_nop 1", "s_waitcnt lgkmcnt(0)"] + dma_setup(g, 0)
-    pending = []  # LDS reads in flight, in issue order
+    out, pending = block_start(g)  # pending: LDS reads in flight, in issue order
 
     def wait_for(tag):
         """Wait until the read tagged tag (and every one before it) is in."""
@@ -195,7 +245,7 @@ def block(g, E):
 
     m = 0
     for k in range(g.nks):
-        if k >= 2:  # this step's K operand (read two steps ahead) must be in
+        if k >= 2 or KPRE is None:  # this step's K operand must be in
             wait_for(("k", k))
         for rb in range(NRB):
             c = "0" if k == 0 else stile(sw, rb)
@@ -222,7 +272,7 @@ def block(g, E):
             out.append(f"v_mfma_f32_32x32x16_bf16 %[acc{rb}{db}], {base.grp(vgroup(g, t))}, "
                        f"{base.pbop(pin, rb, ks)}, %[acc{rb}{db}]")
             if rb == 0:
-                if even and t == KPRE_STEP:
+                if even and t == KPRE_STEP and KPRE is not None:
                     out += base.kpre_reads()
                     pending += [("kp", 0), ("kp", 1)]
                 if t + 2 < g.nt:
@@ -231,7 +281,7 @@ def block(g, E):
             out += gaps[m]
             m += 1
     assert m == g.nm
-    tail = [] if even else ["s_waitcnt vmcnt(0)", "s_barrier"] + base.kpre_reads()
+    tail = [] if even else ["s_waitcnt vmcnt(0)", "s_barrier"] + kpre_reads()
     # Common path: no lane's tile sum passed its bound and tile u is not cut.
     out += ["s_cmp_lg_u64 %[any], 0", "s_cbranch_scc1 8f", "10:"] + base.mask_test("7f")
     out += ["11:"] + tail + ["s_branch 9f"]
@@ -283,8 +333,7 @@ def block_f32(g, E):
     ga, per = base.assign(base.scc_atomic(soft + late), g1, w[:g1])
     gd, _ = base.assign(direct, nm - g1, w[g1:])
     gaps = [base.split_ops(gap) for gap in ga + gd]
-    out = ["s_nop 1", "s_waitcnt lgkmcnt(0)"] + dma_setup(g, 0)
-    pending = []
+    out, pending = block_start(g)
 
     def wait_for(tag):
         nonlocal pending
@@ -294,7 +343,7 @@ def block_f32(g, E):
 
     m = 0
     for k in range(g.nks):
-        if k >= 2:
+        if k >= 2 or KPRE is None:
             wait_for(("k", k))
         for rb in range(NRB):
             c = "0" if k == 0 else stile(sw, rb)
@@ -322,7 +371,7 @@ def block_f32(g, E):
             out.append(f"v_mfma_f32_32x32x16_bf16 %[acc{rb}{db}], {base.grp(vgroup(g, t))}, "
                        f"{base.pbop(buf, rb, ks)}, %[acc{rb}{db}]")
             if u == 0:
-                if even and t == KPRE_STEP:
+                if even and t == KPRE_STEP and KPRE is not None:
                     out += base.kpre_reads()
                     pending += [("kp", 0), ("kp", 1)]
                 if t + 2 < g.nt:
@@ -337,7 +386,7 @@ def block_f32(g, E):
         for j in range(4, 8):
             out.append(f"v_mov_b32 {base.pbreg(0, rb, j)}, {src(rb, 2 * j + 1)}")
             out.append(f"v_mov_b32 {base.pbreg(1, rb, j)}, {src(rb, 2 * j)}")
-    tail = [] if even else ["s_waitcnt vmcnt(0)", "s_barrier"] + base.kpre_reads()
+    tail = [] if even else ["s_waitcnt vmcnt(0)", "s_barrier"] + kpre_reads()
     out += base.mask_test("7f") + ["11:"] + tail + ["s_branch 9f"]
     out += ["7:"] + base.mask_body(sreg(sw)) + ["s_branch 11b", "9:"]
     return out, per
@@ -359,6 +408,11 @@ def offset_operands(g):
 
 
 def render(g):
+    with regmap(g):
+        return render_map(g)
+
+
+def render_map(g):
     out = [f"// Generated by gen_tile_pipe.py -- edit the generator, not this file.",
            f"// One step of the HD = {g.hd} tile loop: S^T = K Q^T of tile u,",
            "// the online softmax of tile u-1 and O^T += V^T P^T of tile u-2, the",
@@ -381,7 +435,10 @@ def render(g):
     q = [f'[q{rb}_{k}] "{{{qop(g, rb, k)}}}"(q[{rb}][{k}])' for rb in range(NRB)
          for k in range(g.nks)]
     out += base.operand_list(f"{g.name}_Q_OPERANDS", q)
-    kp = [f'[kp{k}] "+{{v[{KPRE + 4 * k}:{KPRE + 4 * k + 3}]}}"(kpre[{k}])' for k in range(2)]
+    if KPRE is not None:
+        kp = [f'[kp{k}] "+{{v[{KPRE + 4 * k}:{KPRE + 4 * k + 3}]}}"(kpre[{k}])' for k in range(2)]
+    else:  # no K operands read ahead: a placeholder the asm statement binds
+        kp = ['[kpd] "+s"(kpd)']
     out += base.operand_list(f"{g.name}_KPRE_OPERANDS", kp)
     acc = [f'[acc{rb}{db}] "+a"(acc[{rb}][{db}])' for rb in range(NRB) for db in range(g.ndb)]
     out += base.operand_list(f"{g.name}_ACC_OPERANDS", acc)

@@ -72,6 +72,11 @@ constexpr int kWaves = 4;           // waves per workgroup
 constexpr int kRowsPerWave = 64;    // (token, head) rows per wave (two 32-row MFMA blocks)
 constexpr int kRowsPerWG = kWaves * kRowsPerWave;
 constexpr int kBKV = 32;            // keys per KV tile
+// Workgroups of the fused kernel resident per CU: two at HD = 64 (32 KiB
+// of LDS and 256 registers per lane each), one otherwise.
+template <int D>
+constexpr int kWGsPerCU = D == 64 ? 2 : 1;
+constexpr int wgs_per_cu(int head_dim) { return head_dim == 64 ? 2 : 1; }
 
 hipError_t launch_fused(const FusedParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_kv_cache_write(const WriteParams& p, hipStream_t stream);

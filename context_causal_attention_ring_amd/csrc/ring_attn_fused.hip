@@ -354,9 +354,14 @@ __device__ __forceinline__ void tile_hd256(f32x16 (&acc)[2][8], bf16x8 (&p0)[2][
 //   va[d]  LDS address of this lane's transposed V read for d block d;
 //          step (ks, db) reads va[db] + VOFF + 32 D ks, and + 16 D for keys
 //          8..15
-// Q is pinned to v[44:44 + D / 2), the score buffers to v[108:171], the
+// HD = 128: Q is pinned to v[44:107], the score buffers to v[108:171], the
 // probability buffers to v[172:203] and kpre to v[236:243]; the
 // exponentials use v[204:211] and the operand ring v[244:255] (clobbered).
+// HD = 64 runs two workgroups per CU (a wave has 256 registers, 64 of them
+// the accumulator's): Q v[44:75], the score buffers v[76:139], the
+// probability buffers v[140:171], the exponentials v[172:179] and the ring
+// v[180:191]; there is no kpre: each block reads its first two K operands
+// itself, and the other wave on the SIMD covers their latency.
 #include "tile_hd128.inc"
 #include "tile_hd64.inc"
 #define RA_TILE_PIPE_ASM(HD, E, SOUT, SRW, POUT, PIN)                                          \
@@ -400,6 +405,7 @@ __device__ __forceinline__ void tile_pipe(f32x16 (&acc)[2][D / 32], f32x16 (&sc)
   const uint32_t one2 = 0x3F803F80u;  // bf16 pair (1, 1): v_dot2 sums a packed pair
   const uint32_t hmask = 0xFFFF0000u;  // the bf16 truncation of an fp32 word
   const uint32_t psel = 0x07060302u;   // v_perm: the upper halves of two words
+  [[maybe_unused]] uint32_t kpd = 0;    // HD = 64: stands in for kpre (nothing read ahead)
   if constexpr (F32 && D == 128 && E == 0) {
     RA_TILE_PIPE_F32_ASM(128, 0, S_OUT0, S_RW1);
   } else if constexpr (F32 && D == 128) {
@@ -426,7 +432,8 @@ __device__ __forceinline__ void tile_pipe(f32x16 (&acc)[2][D / 32], f32x16 (&sc)
 #undef RA_TILE_INPUT_OPERANDS
 
 template <int D, bool F32OUT>
-__global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedParams p) {
+__global__ __launch_bounds__(kWaves * 64, kWGsPerCU<D>) void ring_attn_fused_kernel(
+    FusedParams p) {
   constexpr int NRB = kRowsPerWave / 32;  // 32-row MFMA blocks per wave
   constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
   constexpr int NDB = D / 32;             // 32-wide d blocks of the output
@@ -934,7 +941,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ring_attn_fused_kernel(FusedPa
   // reads them for the tile after it).
   bf16x8 kpre[2];
 #if defined(__HIP_DEVICE_COMPILE__)
-  if constexpr (ASMBLK)
+  if constexpr (ASM256 || (ASMPIPE && D == 128))
     asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
                  : "={v[236:239]}"(kpre[0]), "={v[240:243]}"(kpre[1])
                  : "v"(ka[0]), "v"(ka[1])

@@ -458,17 +458,17 @@ int ra_split_suggest(const ra_dims_t* dims, int32_t num_cus, int32_t* splits) {
   if (d.real_rows < 0 || d.real_rows > d.q_rows)
     return fail(RA_ERR_INVALID_ARG, "real_rows must be in [0, q_rows=%d]; got %d", d.q_rows,
                 d.real_rows);
-  // One workgroup per CU at a time.  A launch of W workgroups takes
-  // ceil(W / CUs) waves; splitting multiplies W by S at a small cost per
-  // segment (its own Q load and partial output), so pick the S that best
-  // fills the last wave.
+  // One workgroup per CU at a time (two at HD = 64).  A launch of W
+  // workgroups takes ceil(W / slots) waves; splitting multiplies W by S at a
+  // small cost per segment (its own Q load and partial output), so pick the
+  // S that best fills the last wave.
   const int64_t group = d.num_q_heads / d.num_kv_heads;
   const int64_t wgs = ((int64_t)d.real_rows * group + ra::kRowsPerWG - 1) / ra::kRowsPerWG *
                       d.num_kv_heads;
   int32_t best = 1;
   double best_cost = 1e300;
   for (int32_t s = 1; s <= 16 && wgs > 0; ++s) {
-    const double waves = (double)(wgs * s) / num_cus;
+    const double waves = (double)(wgs * s) / ((int64_t)num_cus * ra::wgs_per_cu(d.head_dim));
     const double cost = std::ceil(waves) / waves * (1.0 + 0.02 * (s - 1));
     if (cost < best_cost - 1e-9) {
       best_cost = cost;

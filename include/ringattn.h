@@ -236,7 +236,7 @@ int ring_attn_prefill_split_noalloc(const void* q, const void* k_cache, const vo
 
 /* Host-only: a split count for these dims on a GPU with num_cus compute
  * units.  One workgroup (256 query rows of one KV head) runs per CU at a
- * time; the count is chosen so that the workgroups of all segments fill the
+ * time (two at HD = 64); the count is chosen so that the workgroups of all segments fill the
  * last wave best, charging each extra segment a small cost (1: no split).
  * Writes *splits; no GPU involved. */
 int ra_split_suggest(const ra_dims_t* dims, int32_t num_cus, int32_t* splits);

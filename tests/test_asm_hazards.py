@@ -187,6 +187,25 @@ def test_fused_kernels_use_no_scratch(extra):
     assert spills and all(n == 0 for n in spills), spills
 
 
+@pytest.mark.skipif(not HAS_HIPCC, reason="needs hipcc to assemble the kernel")
+def test_hd64_kernels_fit_two_workgroups_per_cu():
+    """At HD = 64 two workgroups share a CU: each wave may hold 256 of the
+    SIMD's 512 registers per lane (VGPRs and AGPRs together) and each
+    workgroup half the LDS."""
+    with tempfile.TemporaryDirectory() as tmp:
+        asm = open(build.assemble(out=os.path.join(tmp, "fused.s"), extra=())).read()
+    found = 0
+    for name, body in re.findall(r"\.amdhsa_kernel (\S*fused_kernel\S*)(.*?)\.end_amdhsa_kernel",
+                                 asm, re.S):
+        if "fused_kernelILi64E" not in name:
+            continue
+        found += 1
+        regs_ = int(re.search(r"\.amdhsa_next_free_vgpr\s+(\d+)", body).group(1))
+        lds = int(re.search(r"\.amdhsa_group_segment_fixed_size\s+(\d+)", body).group(1))
+        assert regs_ <= 256 and lds <= 80 * 1024, (name, regs_, lds)
+    assert found == 2
+
+
 def test_m0_check_has_teeth():
     """The M0 check flags explicit and implicit users, and passes plain code."""
     assert m0_users(["s_mov_b32 m0, s4", "s_sendmsg sendmsg(MSG_INTERRUPT)",
